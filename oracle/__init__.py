@@ -1,0 +1,262 @@
+"""CPU oracle for the INT8 W8A8 linear layer (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It wraps ``qlin_oracle.c`` (plain C,
+built with gcc) through ctypes on numpy arrays and shares nothing with the HIP
+library.  bf16 arrays are passed as ``uint16`` bit patterns.
+
+Each function follows the passage cited in ``qlin_oracle.c``:
+mini_trainer "quantized-training" guide (INT8 weights with per-row float
+magnitude, integer forward/backward products, stochastic requantization) and
+OneTrainer PR #1681 "Int8 conv rot" (block-Hadamard rotation of activations,
+per-row activation quantization).
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qlin_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F32 = 0
+BF16 = 1
+OK = 0
+EINVAL = 1
+EUNSUPPORTED = 2
+
+OP_FWD, OP_DX, OP_DW = 0, 1, 2
+
+# gcc flags: IEEE binary32 arithmetic with no contraction into FMA and no
+# fast-math, so every fl() in the definitions is one correctly rounded op.
+CFLAGS = ["-O2", "-std=gnu11", "-fPIC", "-shared", "-fopenmp",
+          "-ffp-contract=off", "-fno-fast-math", "-fno-finite-math-only"]
+
+
+def build(verbose=False):
+    """Compile qlin_oracle.c into liboracle.so (always recompiles)."""
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    global _lib
+    _lib = None
+
+
+_lib = None
+
+
+def lib():
+    """Load liboracle.so, building it first only if it does not exist."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        vp, i64, i32, f32, u64 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                  ctypes.c_float, ctypes.c_uint64)
+        L.orc_hadamard_scale.argtypes = [i32]
+        L.orc_hadamard_scale.restype = f32
+        L.orc_hadamard.argtypes = [vp, i32, i64, i64, i32, vp]
+        L.orc_quantize_rows.argtypes = [vp, i32, i64, i64, vp, i32, vp, vp]
+        L.orc_quantize_cols.argtypes = [vp, i32, i64, i64, vp, vp, vp, vp]
+        L.orc_gemm_s32.argtypes = [i32, vp, vp, i64, i64, i64, vp]
+        L.orc_gemm_s32_at.argtypes = [i32, vp, vp, i64, i64, i64, vp, vp, i64, vp]
+        L.orc_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
+        L.orc_bwd_dx.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+        L.orc_bwd_dw.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+        L.orc_op_at.argtypes = [i32, vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, i64, vp]
+        L.orc_philox4x32_10.argtypes = [vp, vp, vp]
+        L.orc_philox4x32_10.restype = None
+        L.orc_philox4x64_10.argtypes = [vp, vp, vp]
+        L.orc_philox4x64_10.restype = None
+        L.orc_sr_bits16.argtypes = [u64, u64, u64]
+        L.orc_sr_bits16.restype = ctypes.c_uint32
+        L.orc_sgd_requant.argtypes = [vp, vp, vp, i64, i64, f32, u64, u64, vp, vp]
+        for name in ("orc_hadamard", "orc_quantize_rows", "orc_quantize_cols",
+                     "orc_gemm_s32", "orc_gemm_s32_at", "orc_fwd", "orc_bwd_dx",
+                     "orc_bwd_dw", "orc_op_at", "orc_sgd_requant"):
+            getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _chk(st):
+    if st != OK:
+        raise OracleError(f"oracle status {st}")
+
+
+def _as_input(x):
+    """(contiguous array, dtype code) for an fp32 array or uint16 bf16 bits."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return x, BF16
+    if x.dtype != np.float32:
+        raise TypeError(f"oracle input must be float32 or uint16 (bf16 bits), got {x.dtype}")
+    return x, F32
+
+
+def _f32(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float32)
+
+
+def hadamard_scale(b):
+    return float(np.float32(lib().orc_hadamard_scale(int(b))))
+
+
+def hadamard(x, block):
+    """Block-Hadamard rotation of each row of x (fp32 or bf16 bits) -> fp32."""
+    x, dt = _as_input(x)
+    rows, cols = x.shape
+    y = np.empty((rows, cols), np.float32)
+    _chk(lib().orc_hadamard(_ptr(x), dt, rows, cols, int(block), _ptr(y)))
+    return y
+
+
+def quantize_rows(x, prescale=None, had_block=0):
+    """Per-row absmax INT8 quantization (optional rotation, then prescale)."""
+    x, dt = _as_input(x)
+    rows, cols = x.shape
+    p = _f32(prescale)
+    q = np.empty((rows, cols), np.int8)
+    s = np.empty(rows, np.float32)
+    _chk(lib().orc_quantize_rows(_ptr(x), dt, rows, cols, _ptr(p), int(had_block),
+                                 _ptr(q), _ptr(s)))
+    return q, s
+
+
+def quantize_cols(x, prescale=None, want_sum=False):
+    """Per-column absmax INT8 quantization of x * prescale[:, None]."""
+    x, dt = _as_input(x)
+    rows, cols = x.shape
+    p = _f32(prescale)
+    q = np.empty((rows, cols), np.int8)
+    s = np.empty(cols, np.float32)
+    cs = np.empty(cols, np.float32) if want_sum else None
+    _chk(lib().orc_quantize_cols(_ptr(x), dt, rows, cols, _ptr(p), _ptr(q), _ptr(s),
+                                 _ptr(cs)))
+    return (q, s, cs) if want_sum else (q, s)
+
+
+def _op_dims(op, M, N, K):
+    return {OP_FWD: (M, N), OP_DX: (M, K), OP_DW: (N, K)}[op]
+
+
+def gemm_s32(op, a, b, M, N, K):
+    """Raw int32 accumulators of product ``op`` (OP_FWD, OP_DX or OP_DW)."""
+    a = np.ascontiguousarray(a, np.int8)
+    b = np.ascontiguousarray(b, np.int8)
+    R, C = _op_dims(op, M, N, K)
+    c = np.empty((R, C), np.int32)
+    _chk(lib().orc_gemm_s32(op, _ptr(a), _ptr(b), M, N, K, _ptr(c)))
+    return c
+
+
+def gemm_s32_at(op, a, b, M, N, K, ii, jj):
+    a = np.ascontiguousarray(a, np.int8)
+    b = np.ascontiguousarray(b, np.int8)
+    ii = np.ascontiguousarray(ii, np.int64)
+    jj = np.ascontiguousarray(jj, np.int64)
+    out = np.empty(len(ii), np.int32)
+    _chk(lib().orc_gemm_s32_at(op, _ptr(a), _ptr(b), M, N, K, _ptr(ii), _ptr(jj),
+                               len(ii), _ptr(out)))
+    return out
+
+
+def fwd(qx, sx, qw, sw, bias=None):
+    qx = np.ascontiguousarray(qx, np.int8)
+    qw = np.ascontiguousarray(qw, np.int8)
+    M, K = qx.shape
+    N = qw.shape[0]
+    y = np.empty((M, N), np.float32)
+    _chk(lib().orc_fwd(_ptr(qx), _ptr(_f32(sx)), _ptr(qw), _ptr(_f32(sw)),
+                       _ptr(_f32(bias)), M, N, K, _ptr(y)))
+    return y
+
+
+def bwd_dx(qg1, sg1, qw):
+    qg1 = np.ascontiguousarray(qg1, np.int8)
+    qw = np.ascontiguousarray(qw, np.int8)
+    M, N = qg1.shape
+    K = qw.shape[1]
+    dx = np.empty((M, K), np.float32)
+    _chk(lib().orc_bwd_dx(_ptr(qg1), _ptr(_f32(sg1)), _ptr(qw), M, N, K, _ptr(dx)))
+    return dx
+
+
+def bwd_dw(qg2, sg2, qx):
+    qg2 = np.ascontiguousarray(qg2, np.int8)
+    qx = np.ascontiguousarray(qx, np.int8)
+    M, N = qg2.shape
+    K = qx.shape[1]
+    dw = np.empty((N, K), np.float32)
+    _chk(lib().orc_bwd_dw(_ptr(qg2), _ptr(_f32(sg2)), _ptr(qx), M, N, K, _ptr(dw)))
+    return dw
+
+
+def op_at(op, a, srow, b, scol, bias, M, N, K, ii, jj):
+    """Dequantized outputs of product ``op`` at positions (ii[t], jj[t])."""
+    a = np.ascontiguousarray(a, np.int8)
+    b = np.ascontiguousarray(b, np.int8)
+    ii = np.ascontiguousarray(ii, np.int64)
+    jj = np.ascontiguousarray(jj, np.int64)
+    out = np.empty(len(ii), np.float32)
+    _chk(lib().orc_op_at(op, _ptr(a), _ptr(_f32(srow)), _ptr(b), _ptr(_f32(scol)),
+                         _ptr(_f32(bias)), M, N, K, _ptr(ii), _ptr(jj), len(ii),
+                         _ptr(out)))
+    return out
+
+
+def philox4x32_10(ctr, key):
+    c = np.ascontiguousarray(ctr, np.uint32)
+    k = np.ascontiguousarray(key, np.uint32)
+    out = np.empty(4, np.uint32)
+    lib().orc_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def philox4x64_10(ctr, key):
+    c = np.ascontiguousarray(ctr, np.uint64)
+    k = np.ascontiguousarray(key, np.uint64)
+    out = np.empty(4, np.uint64)
+    lib().orc_philox4x64_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def sr_bits16(seed, step, i):
+    return int(lib().orc_sr_bits16(int(seed), int(step), int(i)))
+
+
+def sgd_requant(qw, sw, dw, lr, seed, step, bias=None, db=None):
+    """Returns updated (qw, sw, bias) copies; the inputs are left unchanged."""
+    qw = np.array(qw, np.int8, copy=True, order="C")
+    sw = np.array(sw, np.float32, copy=True)
+    dw = np.ascontiguousarray(dw, np.float32)
+    b = None if bias is None else np.array(bias, np.float32, copy=True)
+    N, K = qw.shape
+    _chk(lib().orc_sgd_requant(_ptr(qw), _ptr(sw), _ptr(dw), N, K, float(lr), int(seed),
+                               int(step), _ptr(b), _ptr(_f32(db))))
+    return qw, sw, b
+
+
+def prepare_weight(w, had_block=0):
+    """Weight preparation: rotate each row (optional), then per-row quantize.
+
+    Rejects all-zero rows (mini_trainer guide: initial zero directions are
+    rejected)."""
+    w = np.ascontiguousarray(w, np.float32)
+    if np.any(np.all(w == 0, axis=1)):
+        raise ValueError("weight has an all-zero row (zero direction)")
+    return quantize_rows(w, had_block=had_block)
