@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""Throughput of one training step of the INT8 W8A8 linear layer on one GPU.
+
+Workload: 12000 tokens, 5376 -> 7168, block-Hadamard rotation 128, bf16
+activations with 1% outlier channels, bf16 dY, seeded synthetic data (the
+headline shape of OneTrainer PR #1681's measurements).  A step is the whole
+path: rotate + quantize X, forward product, both dY quantizations, dX
+product, un-rotation of dX, dW product, and the SGD stochastic requant.
+Metric: int8 TOPS counting the three products (3 * 2 * M * N * K ops) over
+the wall time of the full step, and its fraction of the dense INT8 MFMA peak.
+
+Per-call durations come from HIP events recorded on the launch stream between
+the calls inside the timed steps; the dominant call is reported against its
+roofline.  The CPU baseline runs the oracle on a bounded token sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+M, K, N, HAD = 12000, 5376, 7168, 128
+LR = 1e-3
+SEED = 0
+PEAK_INT8_TOPS = 5000.0       # MI355X dense INT8 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+GEMM_OPS = 2.0 * M * N * K
+METRIC = "INT8 linear fwd+bwd TOPS at 12000x5376->7168; % of INT8 MFMA peak"
+
+# Algorithmic bytes per launch of the memory-bound calls (read once + write once).
+ALG_BYTES = {
+    "quantize_x": M * K * 2 + M * K + 4 * M,
+    "quantize_dy_rows": M * N * 2 + M * N + 4 * M + 4 * N,
+    "quantize_dy_cols": 2 * (M * N * 2) + M * N + 4 * N + 4 * M,
+    "unrotate_dx": 2 * M * K * 4,
+    "sgd_requant": N * K * (1 + 4 + 1) + 8 * N,
+}
+GEMMS = ("fwd", "bwd_dx", "bwd_dw")
+# Kernel symbol behind each call, as rocprofv3 names it.
+KERNEL_OF = {"fwd": "gemm_kernel<128, 128, false, false, 2>",
+             "bwd_dx": "gemm_kernel<128, 128, false, true, 1>",
+             "bwd_dw": "gemm_kernel<128, 128, true, true, 1>"}
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "w8a8_integer_linear_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(call, launches_key):
+    """Measured HBM bytes per launch from the committed counter summary, or None
+    when the summary is absent or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != source_digest():
+        return None
+    ent = rec.get("kernels", {}).get(launches_key)
+    return None if ent is None else ent.get("bytes_per_launch")
+
+
+def cpu_baseline(d, tokens):
+    """The oracle's full step on the first `tokens` rows (weight prep untimed)."""
+    import oracle
+    qw, sw = oracle.prepare_weight(d["w"], had_block=HAD)
+    x, dy = d["x"][:tokens], d["dy"][:tokens]
+    t0 = time.perf_counter()
+    qx, sx = oracle.quantize_rows(x, had_block=HAD)
+    oracle.fwd(qx, sx, qw, sw)
+    qg1, sg1 = oracle.quantize_rows(dy, prescale=sw)
+    qg2, sg2 = oracle.quantize_cols(dy, prescale=sx)
+    dx = oracle.bwd_dx(qg1, sg1, qw)
+    oracle.hadamard(dx, HAD)
+    dw = oracle.bwd_dw(qg2, sg2, qx)
+    oracle.sgd_requant(qw, sw, dw, LR, SEED, 0)
+    t = time.perf_counter() - t0
+    ops = 3 * 2.0 * tokens * N * K
+    return {"value": round(ops / t / 1e12, 6), "unit": "TOPS", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{tokens} of {M} tokens at full 5376->7168 width, all eight steps "
+                      f"(SGD requant over the whole weight), {t:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-tokens", type=int, default=32,
+                    help="token sample of the oracle CPU baseline (0 skips it)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer's data-"
+              "parallel sharding is not built here.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads
+    from w8a8_integer_linear_amd import LinearW8A8Training
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    print(f"[bench] generating inputs {M}x{K}->{N}", file=sys.stderr, flush=True)
+    d = workloads.linear(M, K, N, seed=SEED)
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    x, dy = dev(d["x"]), dev(d["dy"])
+    layer = LinearW8A8Training(dev(d["w"]), had_block=HAD, max_tokens=M)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    marks = []
+
+    def tick(label):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(stream)
+        marks.append((label, ev))
+
+    def step(i):
+        tick("start")
+        layer.forward(x)
+        layer.backward(dy)
+        layer.sgd_step(LR, SEED, i)
+
+    layer.timer = tick
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    marks.clear()
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_begin.elapsed_time(t_end) / args.steps
+
+    per = {}
+    for (_, a), (label, b) in zip(marks[:-1], marks[1:]):
+        if label == "start":
+            continue
+        per.setdefault(label, []).append(a.elapsed_time(b))
+    avg = {k: sum(v) / len(v) for k, v in per.items()}
+
+    breakdown = {}
+    for k, ms in avg.items():
+        if k in GEMMS:
+            breakdown[k] = {"ms": round(ms, 4), "tops": round(GEMM_OPS / (ms * 1e-3) / 1e12, 1),
+                            "frac_mfma": round(GEMM_OPS / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4)}
+        else:
+            gbs = ALG_BYTES[k] / (ms * 1e-3) / 1e9
+            breakdown[k] = {"ms": round(ms, 4), "gbs": round(gbs, 1),
+                            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    dominant = max(avg, key=avg.get)
+    if dominant in GEMMS:
+        ach = GEMM_OPS / (avg[dominant] * 1e-3) / 1e12
+        traffic = traffic_for(dominant, KERNEL_OF.get(dominant, dominant))
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_INT8_TOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_INT8_TOPS, 4), "traffic": traffic,
+                "kernel": dominant, "ms_per_launch": round(avg[dominant], 4)}
+    else:
+        ach = ALG_BYTES[dominant] / (avg[dominant] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4),
+                "traffic": traffic_for(dominant, dominant), "kernel": dominant,
+                "ms_per_launch": round(avg[dominant], 4)}
+
+    tops = 3 * GEMM_OPS / (ms_per_step * 1e-3) / 1e12
+    out = {
+        "metric": METRIC, "value": round(tops, 2), "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "INT8 W8A8 linear training step, 12000 tokens, 5376->7168, "
+                               "Hadamard block 128, bf16 X (1% x8 outlier channels), bf16 dY, "
+                               "SGD lr 1e-3 with Philox stochastic requant",
+                   "tokens": M, "in_features": K, "out_features": N, "had_block": HAD},
+        "pct_of_int8_peak": round(100 * tops / PEAK_INT8_TOPS, 2),
+        "roofline": roof,
+        "breakdown": breakdown,
+    }
+    if args.cpu_tokens > 0:
+        print(f"[bench] cpu baseline on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(d, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+/*
+ * qlin: INT8 W8A8 linear layer for quantized training on AMD MI355X (gfx950).
+ *
+ * The layer stores each weight matrix as INT8 codes with one float magnitude
+ * per output row and keeps no float master weight; it quantizes activations
+ * per row on every call, optionally after a block-Hadamard rotation along the
+ * contraction dimension; it runs the forward product and both backward
+ * products as int8 x int8 -> int32 matrix products on the saved INT8 input;
+ * and it updates the weight with an SGD step that stochastically requantizes
+ * each row.  Sources: the mini_trainer "quantized-training" guide (feature
+ * table; update paragraph; arithmetic paragraph on contractions above
+ * 131,071) and OneTrainer PR #1681 "Int8 conv rot" (summary; commit notes 1
+ * and 2).
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are device memory owned by the caller, row-major and
+ *    contiguous, 16-byte aligned.  The library allocates nothing and keeps no
+ *    mutable global state; calls on different streams are independent.
+ *  - 'stream' is a hipStream_t (NULL means the null stream).  Every call only
+ *    enqueues kernels on that stream and returns without synchronizing.
+ *  - Arguments are validated before anything is launched: on any error the
+ *    call returns a nonzero status and no output is touched.  Faults inside
+ *    kernels surface at the caller's next synchronization.
+ *  - Shapes: M (tokens) >= 0 is arbitrary; M == 0 is a no-op.  N (out
+ *    features) and K (in features) are multiples of 16.  A contraction longer
+ *    than QLIN_MAX_CONTRACTION is rejected with QLIN_EUNSUPPORTED.
+ *  - Arithmetic: IEEE binary32, round to nearest even, no fused multiply-add,
+ *    IEEE division.  Results are deterministic and do not depend on the
+ *    launch configuration, except col_sum of qlin_quantize_cols (fp32 sums
+ *    combined in arbitrary order).
+ */
+#ifndef QLIN_H
+#define QLIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define QLIN_OK 0
+#define QLIN_EINVAL 1       /* null pointer, bad shape, misalignment, bad block/dtype */
+#define QLIN_EUNSUPPORTED 2 /* contraction or row too long for this library */
+#define QLIN_EDEVICE 3      /* the HIP runtime reported an error at launch */
+
+/* Element types of floating inputs. */
+#define QLIN_F32 0
+#define QLIN_BF16 1
+
+/* Products, for qlin_gemm_s32. */
+#define QLIN_OP_FWD 0 /* acc[M,N] = qx[M,K]  . qw[N,K]^T */
+#define QLIN_OP_DX 1  /* acc[M,K] = qg1[M,N] . qw[N,K]   */
+#define QLIN_OP_DW 2  /* acc[N,K] = qg2[M,N]^T . qx[M,K] */
+
+/* Longest contraction for which an int32 sum of int8 x int8 products cannot
+ * overflow: 131071 * 128 * 128 < 2^31 (mini_trainer guide, arithmetic
+ * paragraph: longer contractions need an int64 combination of bounded int32
+ * partial products, which this library does not provide). */
+#define QLIN_MAX_CONTRACTION 131071
+/* Largest Hadamard block and longest row the row kernels accept. */
+#define QLIN_MAX_HAD_BLOCK 512
+#define QLIN_MAX_ROW 131072
+
+/* Human-readable name of a status code (static storage). */
+const char *qlin_status_string(int status);
+
+/* Version of the C ABI declared here. */
+int qlin_abi_version(void);
+
+/*
+ * Per-row dynamic INT8 quantization, optionally after a block-Hadamard
+ * rotation (OneTrainer PR #1681: the activations are rotated along the
+ * contraction dimension and quantized per row on every call; mini_trainer
+ * guide: INT8 direction with a float magnitude per output row).
+ *
+ *   x         [rows, cols] fp32 or bf16 (dtype QLIN_F32 / QLIN_BF16), input.
+ *   prescale  [cols] fp32 or NULL: multiplies each rotated element by the
+ *             scale of its column (used to fold the weight row scales into
+ *             dY before quantizing it for dX).
+ *   had_block 0 (no rotation) or a power of two in [2, 512] dividing cols:
+ *             each run of had_block elements is replaced by its normalized
+ *             Walsh-Hadamard transform (Sylvester order, scaled by
+ *             fl32(1/sqrt(had_block)), butterfly stages in ascending stride).
+ *   q         [rows, cols] int8 output, s [rows] fp32 output:
+ *             g = rotate(x) * prescale, a = max |g|, s = fl(a / 127) and
+ *             q = rne(fl(g / s)) in [-127, 127]; a row with a == 0 gets
+ *             s = 0 and q = 0.
+ * rows >= 0; cols in [16, QLIN_MAX_ROW], a multiple of 16.
+ */
+int qlin_quantize_rows(const void *x, int dtype, int64_t rows, int64_t cols,
+                       const float *prescale, int had_block, int8_t *q, float *s,
+                       void *stream);
+
+/*
+ * Per-column dynamic INT8 quantization of x * prescale[:, None], the operand
+ * of the weight-gradient product: scales sit on the output axis of that
+ * product, never on its contraction (token) axis.  q keeps the [rows, cols]
+ * layout of x.
+ *
+ *   x         [rows, cols] fp32 or bf16 input (dY, rows = tokens).
+ *   prescale  [rows] fp32 or NULL (the activation row scales s_x).
+ *   q         [rows, cols] int8 output; s [cols] fp32 output, defined as in
+ *             qlin_quantize_rows but per column.
+ *   col_sum   [cols] fp32 or NULL: sum over rows of the raw x (the bias
+ *             gradient), accumulated in fp32 in an unspecified order.
+ * rows >= 0; cols >= 16, a multiple of 16.  s (and col_sum) are also used as
+ * accumulators during the call and must not alias x, prescale or q.
+ */
+int qlin_quantize_cols(const void *x, int dtype, int64_t rows, int64_t cols,
+                       const float *prescale, int8_t *q, float *s, float *col_sum,
+                       void *stream);
+
+/*
+ * Block-Hadamard rotation of each row (the same transform as in
+ * qlin_quantize_rows).  The transform is symmetric and orthogonal, so the
+ * same call maps the rotated basis back (OneTrainer PR #1681: the weight
+ * stays in the rotated basis, (xR)(WR)^T = xW^T).
+ *   x [rows, cols] fp32 or bf16; y [rows, cols] fp32, may equal x when
+ *   dtype is QLIN_F32 (in place), must not otherwise overlap it.
+ *   block: power of two in [2, 512] dividing cols; cols a multiple of 16.
+ */
+int qlin_hadamard(const void *x, int dtype, int64_t rows, int64_t cols, int block,
+                  float *y, void *stream);
+
+/*
+ * Forward product with fused dequant (mini_trainer guide: integer forward
+ * product on INT8 weights; OneTrainer PR #1681: int8 x int8 -> int32
+ * product of quantized activations and weights).
+ *   qx [M,K] int8, sx [M]; qw [N,K] int8, sw [N]; bias [N] or NULL.
+ *   y [M,N] fp32: y = fl(fl(fl32(acc) * sx[m]) * sw[n]) (+ bias[n]) with
+ *   acc = sum_k qx[m,k] * qw[n,k] exact in int32.
+ * K <= QLIN_MAX_CONTRACTION.  M <= 16 takes a weight-streaming path.
+ */
+int qlin_fwd(const int8_t *qx, const float *sx, const int8_t *qw, const float *sw,
+             const float *bias, int64_t M, int64_t N, int64_t K, float *y, void *stream);
+
+/*
+ * Input-gradient product in the rotated basis (straight-through estimator
+ * across the activation quantizer).
+ *   qg1 [M,N] int8, sg1 [M]: dY * sw[None, :] quantized per row
+ *   (qlin_quantize_rows with prescale = sw); qw [N,K] int8.
+ *   dx [M,K] fp32: dx = fl(fl32(acc) * sg1[m]), acc = sum_n qg1[m,n] * qw[n,k].
+ * N <= QLIN_MAX_CONTRACTION.  Rotate dx back with qlin_hadamard when the
+ * layer uses a rotation.
+ */
+int qlin_bwd_dx(const int8_t *qg1, const float *sg1, const int8_t *qw, int64_t M,
+                int64_t N, int64_t K, float *dx, void *stream);
+
+/*
+ * Weight-gradient product on the saved INT8 input (mini_trainer guide:
+ * saved Linear inputs are stored in INT8 for the backward pass).
+ *   qg2 [M,N] int8, sg2 [N]: dY * sx[:, None] quantized per column
+ *   (qlin_quantize_cols with prescale = sx); qx [M,K] int8 from the forward.
+ *   dw [N,K] fp32: dw = fl(fl32(acc) * sg2[n]), acc = sum_m qg2[m,n] * qx[m,k].
+ * M <= QLIN_MAX_CONTRACTION.
+ */
+int qlin_bwd_dw(const int8_t *qg2, const float *sg2, const int8_t *qx, int64_t M,
+                int64_t N, int64_t K, float *dw, void *stream);
+
+/*
+ * SGD step with stochastic requantization of each weight row, in place
+ * (mini_trainer guide: updates stochastically requantize the represented
+ * weight and no float master weight is retained; OneTrainer PR #1681: the
+ * quantized weight is updated in its existing storage).
+ *   qw [N,K] int8 and sw [N] fp32, read and overwritten.
+ *   dw [N,K] fp32 weight gradient.
+ *   Per row n: w = fl(fl(sw[n] * q) - fl(lr * dw)); s' = fl(max|w| / 127)
+ *   (0 for an all-zero row); y = fl(w / s'); q' = floor(y) + (u < y -
+ *   floor(y)) clamped to [-127, 127], where u = r * 2^-16 and r is the 16-bit
+ *   half (i & 1) of word (i & 7) >> 1 of Philox4x32-10 (Salmon et al., SC'11)
+ *   at counter (lo(i>>3), hi(i>>3), lo(step), hi(step)) and key (lo(seed),
+ *   hi(seed)), i = n*K + k.  The result depends only on (inputs, lr, seed,
+ *   step), so a run resumed at the same step reproduces it exactly.
+ *   bias [N] and db [N] (both or neither): bias = fl(bias - fl(lr * db)).
+ * K in [16, QLIN_MAX_ROW], a multiple of 16.
+ */
+int qlin_sgd_requant(int8_t *qw, float *sw, const float *dw, int64_t N, int64_t K,
+                     float lr, uint64_t seed, uint64_t step, float *bias, const float *db,
+                     void *stream);
+
+/*
+ * Raw int32 accumulators of one of the three products (same kernels as the
+ * fused calls, no dequant), for exact verification.  op is QLIN_OP_FWD,
+ * QLIN_OP_DX or QLIN_OP_DW; a, b and the shape arguments mean what they mean
+ * in qlin_fwd / qlin_bwd_dx / qlin_bwd_dw; c is [M,N], [M,K] or [N,K].
+ */
+int qlin_gemm_s32(int op, const int8_t *a, const int8_t *b, int64_t M, int64_t N,
+                  int64_t K, int32_t *c, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLIN_H */

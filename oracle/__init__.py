@@ -59,6 +59,8 @@ def lib():
         L = ctypes.CDLL(_LIB)
         vp, i64, i32, f32, u64 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                   ctypes.c_float, ctypes.c_uint64)
+        L.orc_threads.argtypes = []
+        L.orc_threads.restype = i32
         L.orc_hadamard_scale.argtypes = [i32]
         L.orc_hadamard_scale.restype = f32
         L.orc_hadamard.argtypes = [vp, i32, i64, i64, i32, vp]
@@ -76,10 +78,11 @@ def lib():
         L.orc_philox4x64_10.restype = None
         L.orc_sr_bits16.argtypes = [u64, u64, u64]
         L.orc_sr_bits16.restype = ctypes.c_uint32
-        L.orc_sgd_requant.argtypes = [vp, vp, vp, i64, i64, f32, u64, u64, vp, vp]
+        L.orc_sgd_requant.argtypes = [vp, vp, vp, i64, i64, f32, u64, u64, vp, vp, vp]
+        L.orc_bwd_dw_rows.argtypes = [vp, vp, vp, i64, i64, i64, vp, i64, vp]
         for name in ("orc_hadamard", "orc_quantize_rows", "orc_quantize_cols",
                      "orc_gemm_s32", "orc_gemm_s32_at", "orc_fwd", "orc_bwd_dx",
-                     "orc_bwd_dw", "orc_op_at", "orc_sgd_requant"):
+                     "orc_bwd_dw", "orc_bwd_dw_rows", "orc_op_at", "orc_sgd_requant"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -110,6 +113,11 @@ def _as_input(x):
 
 def _f32(a):
     return None if a is None else np.ascontiguousarray(a, dtype=np.float32)
+
+
+def threads():
+    """Host threads the oracle's parallel loops use."""
+    return int(lib().orc_threads())
 
 
 def hadamard_scale(b):
@@ -206,6 +214,19 @@ def bwd_dw(qg2, sg2, qx):
     return dw
 
 
+def bwd_dw_rows(qg2, sg2, qx, rows):
+    """Rows ``rows`` of dW (each a full row of K outputs)."""
+    qg2 = np.ascontiguousarray(qg2, np.int8)
+    qx = np.ascontiguousarray(qx, np.int8)
+    rows = np.ascontiguousarray(rows, np.int64)
+    M, N = qg2.shape
+    K = qx.shape[1]
+    out = np.empty((len(rows), K), np.float32)
+    _chk(lib().orc_bwd_dw_rows(_ptr(qg2), _ptr(_f32(sg2)), _ptr(qx), M, N, K, _ptr(rows),
+                               len(rows), _ptr(out)))
+    return out
+
+
 def op_at(op, a, srow, b, scol, bias, M, N, K, ii, jj):
     """Dequantized outputs of product ``op`` at positions (ii[t], jj[t])."""
     a = np.ascontiguousarray(a, np.int8)
@@ -239,15 +260,18 @@ def sr_bits16(seed, step, i):
     return int(lib().orc_sr_bits16(int(seed), int(step), int(i)))
 
 
-def sgd_requant(qw, sw, dw, lr, seed, step, bias=None, db=None):
-    """Returns updated (qw, sw, bias) copies; the inputs are left unchanged."""
+def sgd_requant(qw, sw, dw, lr, seed, step, bias=None, db=None, row_ids=None):
+    """Returns updated (qw, sw, bias) copies; the inputs are left unchanged.
+
+    row_ids: global row index of each given row (keys the random stream)."""
     qw = np.array(qw, np.int8, copy=True, order="C")
     sw = np.array(sw, np.float32, copy=True)
     dw = np.ascontiguousarray(dw, np.float32)
     b = None if bias is None else np.array(bias, np.float32, copy=True)
     N, K = qw.shape
+    ids = None if row_ids is None else np.ascontiguousarray(row_ids, np.int64)
     _chk(lib().orc_sgd_requant(_ptr(qw), _ptr(sw), _ptr(dw), N, K, float(lr), int(seed),
-                               int(step), _ptr(b), _ptr(_f32(db))))
+                               int(step), _ptr(b), _ptr(_f32(db)), _ptr(ids)))
     return qw, sw, b
 
 

@@ -40,6 +40,7 @@
  * Philox4x64-10, and statistical properties of the stochastic rounding.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -55,6 +56,9 @@
  * 131071 * 128 * 128 < 2^31 (mini_trainer guide, arithmetic paragraph on
  * contractions above 131,071). */
 #define ORC_MAX_CONTRACTION 131071
+
+/* Threads the parallel loops use (OMP_NUM_THREADS or all cores). */
+int orc_threads(void) { return omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------- helpers */
 
@@ -343,6 +347,24 @@ int orc_bwd_dx(const int8_t *qg1, const float *sg1, const int8_t *qw, int64_t M,
     return ORC_OK;
 }
 
+/* One row of dW: out[k] = fl(fl32(sum_m qg2[m, n] * qx[m, k]) * sg2[n]) for all
+ * k, accumulated over m with the saved-input rows streamed in order. */
+static void dw_row(const int8_t *qg2, const float *sg2, const int8_t *qx, int64_t M,
+                   int64_t N, int64_t K, int64_t n, int64_t *acc, float *out)
+{
+    for (int64_t k = 0; k < K; k++)
+        acc[k] = 0;
+    for (int64_t m = 0; m < M; m++) {
+        int64_t g = qg2[m * N + n];
+        if (g == 0)
+            continue;
+        for (int64_t k = 0; k < K; k++)
+            acc[k] += g * (int64_t)qx[m * K + k];
+    }
+    for (int64_t k = 0; k < K; k++)
+        out[k] = dequant(2, acc[k], sg2, NULL, NULL, n, k);
+}
+
 /* dW: dw[N, K] from (qg2, sg2) (qg2 [M, N] with per-column scales) and the
  * saved qx [M, K]. */
 int orc_bwd_dw(const int8_t *qg2, const float *sg2, const int8_t *qx, int64_t M,
@@ -351,10 +373,32 @@ int orc_bwd_dw(const int8_t *qg2, const float *sg2, const int8_t *qx, int64_t M,
     int st = check_op(2, M, N, K);
     if (st != ORC_OK)
         return st;
-#pragma omp parallel for schedule(static)
-    for (int64_t n = 0; n < N; n++)
-        for (int64_t k = 0; k < K; k++)
-            dw[n * K + k] = dequant(2, dot_op(2, qg2, qx, M, N, K, n, k), sg2, NULL, NULL, n, k);
+#pragma omp parallel
+    {
+        int64_t *acc = (int64_t *)malloc((size_t)K * sizeof(int64_t));
+#pragma omp for schedule(dynamic)
+        for (int64_t n = 0; n < N; n++)
+            dw_row(qg2, sg2, qx, M, N, K, n, acc, dw + n * K);
+        free(acc);
+    }
+    return ORC_OK;
+}
+
+/* Selected rows of dW: out[t, :] = dw[rows[t], :]. */
+int orc_bwd_dw_rows(const int8_t *qg2, const float *sg2, const int8_t *qx, int64_t M,
+                    int64_t N, int64_t K, const int64_t *rows, int64_t count, float *out)
+{
+    int st = check_op(2, M, N, K);
+    if (st != ORC_OK)
+        return st;
+#pragma omp parallel
+    {
+        int64_t *acc = (int64_t *)malloc((size_t)K * sizeof(int64_t));
+#pragma omp for schedule(dynamic)
+        for (int64_t t = 0; t < count; t++)
+            dw_row(qg2, sg2, qx, M, N, K, rows[t], acc, out + t * K);
+        free(acc);
+    }
     return ORC_OK;
 }
 
@@ -440,9 +484,12 @@ uint32_t orc_sr_bits16(uint64_t seed, uint64_t step, uint64_t i)
 /* One plain SGD step on the represented weight, then stochastic requant of
  * each row (mini_trainer guide: updates stochastically requantize represented
  * weights, no floating master weight is kept).  In place on qw [N, K] and
- * sw [N]; bias -= lr * db when both are given. */
+ * sw [N]; bias -= lr * db when both are given.  row_ids (optional) gives the
+ * row index of each local row in the full weight matrix, which keys the
+ * random stream; without it local row n is row n. */
 int orc_sgd_requant(int8_t *qw, float *sw, const float *dw, int64_t N, int64_t K,
-                    float lr, uint64_t seed, uint64_t step, float *bias, const float *db)
+                    float lr, uint64_t seed, uint64_t step, float *bias, const float *db,
+                    const int64_t *row_ids)
 {
     if (N < 0 || K < 1)
         return ORC_EINVAL;
@@ -468,7 +515,8 @@ int orc_sgd_requant(int8_t *qw, float *sw, const float *dw, int64_t N, int64_t K
                     float y = w[j] / s_new;
                     float f = floorf(y);
                     float frac = y - f;
-                    float u = (float)orc_sr_bits16(seed, step, (uint64_t)(n * K + j)) *
+                    int64_t gn = row_ids ? row_ids[n] : n;
+                    float u = (float)orc_sr_bits16(seed, step, (uint64_t)(gn * K + j)) *
                               (1.0f / 65536.0f);
                     float v = f + (u < frac ? 1.0f : 0.0f);
                     if (v > 127.0f)

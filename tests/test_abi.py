@@ -1,0 +1,111 @@
+"""The C-ABI library: it loads, exports every entry point include/qlin.h
+declares, and rejects bad arguments before launching anything.
+
+The rejection tests pass fake (never dereferenced) device addresses and only
+run where no GPU is present, so that an accepted call could not touch memory."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlin.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlin_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from w8a8_integer_linear_amd import _native
+    if not os.path.exists(_native.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return _native.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_binding_covers_header():
+    from w8a8_integer_linear_amd import _native
+    assert sorted(_native.SIGNATURES) == _declared()
+
+
+def test_status_strings(L):
+    assert L.qlin_status_string(0) == b"ok"
+    assert L.qlin_status_string(1) == b"invalid argument"
+    assert L.qlin_status_string(2) == b"unsupported shape"
+    assert L.qlin_abi_version() == 1
+
+
+def _cpu_only():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("fake-pointer validation tests run only without a GPU")
+
+
+P = 0x10000   # a 16-byte aligned fake device address, never dereferenced
+Q = 0x20000
+R = 0x30000
+S = 0x40000
+ODD = 0x10008  # 8-byte aligned only
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((None, 0, 4, 16, None, 0, Q, R), 1),          # null x
+    ((P, 2, 4, 16, None, 0, Q, R), 1),             # bad dtype
+    ((P, 0, 4, 24, None, 0, Q, R), 1),             # cols not a multiple of 16
+    ((P, 0, 4, 0, None, 0, Q, R), 1),              # empty rows of zero length
+    ((P, 0, -1, 16, None, 0, Q, R), 1),            # negative rows
+    ((P, 0, 4, 48, None, 32, Q, R), 1),            # block does not divide cols
+    ((P, 0, 4, 96, None, 3, Q, R), 1),             # block not a power of two
+    ((P, 0, 4, 1024, None, 1024, Q, R), 1),        # block too large
+    ((ODD, 0, 4, 16, None, 0, Q, R), 1),           # misaligned x
+    ((P, 0, 4, 16, ODD, 0, Q, R), 1),              # misaligned prescale
+    ((P, 0, 4, 131072 + 16, None, 0, Q, R), 2),    # row too long
+    ((P, 0, 0, 16, None, 0, Q, R), 0),             # no rows: nothing to do
+])
+def test_quantize_rows_validation(L, args, expect):
+    _cpu_only()
+    assert L.qlin_quantize_rows(*args, None) == expect
+
+
+def test_product_validation(L):
+    _cpu_only()
+    # forward: K beyond the int32-exact contraction bound
+    assert L.qlin_fwd(P, Q, R, S, None, 4, 16, 131072, P, None) == 2
+    # dX: N (its contraction) beyond the bound
+    assert L.qlin_bwd_dx(P, Q, R, 4, 131072, 16, S, None) == 2
+    # dW: M (its contraction) beyond the bound
+    assert L.qlin_bwd_dw(P, Q, R, 131072, 16, 16, S, None) == 2
+    assert L.qlin_fwd(P, Q, R, S, None, 4, 24, 16, P, None) == 1     # N % 16
+    assert L.qlin_fwd(P, Q, R, S, None, 4, 16, 8, P, None) == 1      # K % 16
+    assert L.qlin_fwd(P, None, R, S, None, 4, 16, 16, P, None) == 1  # null sx
+    assert L.qlin_fwd(P, Q, R, S, None, -1, 16, 16, P, None) == 1    # negative M
+    assert L.qlin_fwd(P, Q, R, S, None, 0, 16, 16, P, None) == 0     # M = 0: no-op
+    assert L.qlin_bwd_dx(P, Q, R, 0, 16, 16, S, None) == 0
+    assert L.qlin_gemm_s32(7, P, Q, 4, 16, 16, R, None) == 1          # unknown product
+    assert L.qlin_gemm_s32(0, ODD, Q, 4, 16, 16, R, None) == 1        # misaligned
+
+
+def test_sgd_and_hadamard_validation(L):
+    _cpu_only()
+    assert L.qlin_sgd_requant(P, Q, R, 4, 16, 1e-3, 0, 0, S, None, None) == 1    # bias w/o db
+    assert L.qlin_sgd_requant(P, Q, R, 4, 24, 1e-3, 0, 0, None, None, None) == 1  # K % 16
+    assert L.qlin_sgd_requant(P, Q, R, 4, 16, float("nan"), 0, 0, None, None, None) == 1
+    assert L.qlin_sgd_requant(P, Q, R, 0, 16, 1e-3, 0, 0, None, None, None) == 0
+    assert L.qlin_hadamard(P, 0, 4, 128, 0, Q, None) == 1        # block 0 is not a rotation
+    assert L.qlin_hadamard(P, 0, 4, 96, 64, Q, None) == 1
+    assert L.qlin_hadamard(P, 1, 4, 128, 128, P, None) == 1      # bf16 -> fp32 cannot be in place
+    assert L.qlin_hadamard(P, 0, 0, 128, 128, P, None) == 0
+    assert L.qlin_quantize_cols(P, 0, 4, 16, None, Q, R, R, None) == 1   # s aliases col_sum
+    assert L.qlin_quantize_cols(P, 0, 4, 20, None, Q, R, None, None) == 1

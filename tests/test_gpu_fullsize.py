@@ -1,0 +1,110 @@
+"""Full-size parity of one training step of the headline layer (12000 tokens,
+5376 -> 7168, rotation block 128), run through the same layer object and
+launch configuration the benchmark times.
+
+The oracle recomputes every per-row quantity from the seeded inputs itself
+(weight prep, activation codes, both gradient quantizations) and compares
+them in full; the products are compared at sampled outputs it computes one by
+one (whole 128-blocks for the un-rotated dX, whole rows for dW and the
+stochastic requant).  Everything is bit-exact except the bias gradient."""
+import numpy as np
+import pytest
+
+import workloads
+from tests.gpu_util import announce, assert_bitwise, dev, host, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+def _step(T, d, M, K, N, had, lr, seed, step):
+    from w8a8_integer_linear_amd import LinearW8A8Training
+    announce("layer step", M, K, N, had)
+    layer = LinearW8A8Training(dev(d["w"]), bias=None if d["b"] is None else dev(d["b"]),
+                               had_block=had, max_tokens=M)
+    w0 = (host(layer.qw), host(layer.sw))
+    y = layer.forward(dev(d["x"]))
+    dx = layer.backward(dev(d["dy"]))
+    got = dict(qw=w0[0], sw=w0[1], qx=host(layer.qx), sx=host(layer.sx), y=host(y),
+               qg1=host(layer._qg1[:M]), sg1=host(layer._sg1[:M]), qg2=host(layer._qg2[:M]),
+               sg2=host(layer._sg2), dx=host(dx), dw=host(layer.dw))
+    if layer.db is not None:
+        got["db"] = host(layer.db)
+    layer.sgd_step(lr, seed, step)
+    T.cuda.synchronize()
+    got["qw1"], got["sw1"] = host(layer.qw), host(layer.sw)
+    if layer.bias is not None:
+        got["b1"] = host(layer.bias)
+    return got
+
+
+def _check_step(orc, d, got, M, K, N, had, lr, seed, step, n_samples, rng):
+    qw, sw = orc.prepare_weight(d["w"], had_block=had)
+    assert_bitwise(got["sw"], sw, "weight scales")
+    assert_bitwise(got["qw"], qw, "weight codes")
+    qx, sx = orc.quantize_rows(d["x"], had_block=had)
+    assert_bitwise(got["sx"], sx, "activation scales")
+    assert_bitwise(got["qx"], qx, "activation codes")
+    ii, jj = rng.integers(0, M, n_samples), rng.integers(0, N, n_samples)
+    y_ref = orc.op_at(orc.OP_FWD, qx, sx, qw, sw, d["b"], M, N, K, ii, jj)
+    assert_bitwise(got["y"][ii, jj], y_ref, "y samples")
+    qg1, sg1 = orc.quantize_rows(d["dy"], prescale=sw)
+    assert_bitwise(got["sg1"], sg1, "dY row scales")
+    assert_bitwise(got["qg1"], qg1, "dY row codes")
+    qg2, sg2, db = orc.quantize_cols(d["dy"], prescale=sx, want_sum=True)
+    assert_bitwise(got["sg2"], sg2, "dY column scales")
+    assert_bitwise(got["qg2"], qg2, "dY column codes")
+    # dX: whole blocks of the rotated-basis gradient, then the rotation back.
+    blk = had if had else 16
+    for m, b0 in zip(rng.integers(0, M, 6), rng.integers(0, K // blk, 6) * blk):
+        cols = np.arange(b0, b0 + blk)
+        dxr = orc.op_at(orc.OP_DX, qg1, sg1, qw, None, None, M, N, K, np.full(blk, m), cols)
+        ref = orc.hadamard(dxr[None, :], had)[0] if had else dxr
+        assert_bitwise(got["dx"][m, b0:b0 + blk], ref, f"dx row {m} block {b0}")
+    rows = np.sort(rng.choice(N, 4, replace=False))
+    dw_rows = orc.bwd_dw_rows(qg2, sg2, qx, rows)
+    assert_bitwise(got["dw"][rows], dw_rows, "dW rows")
+    if "db" in got:
+        xf = workloads.bf16_bits_to_f32(d["dy"]) if d["dy"].dtype == np.uint16 else d["dy"]
+        bound = 1e-5 * np.abs(xf.astype(np.float64)).sum(axis=0)
+        assert np.all(np.abs(got["db"].astype(np.float64) - db) <= bound)
+        # bias update b - lr * db, with db known to the column-sum tolerance
+        b_ref = d["b"].astype(np.float64) - np.float32(lr) * db.astype(np.float64)
+        tol = lr * bound + 2.0 ** -23 * np.abs(b_ref)
+        assert np.all(np.abs(got["b1"].astype(np.float64) - b_ref) <= tol)
+    q1, s1, _ = orc.sgd_requant(qw[rows], sw[rows], dw_rows, lr, seed, step, row_ids=rows)
+    assert_bitwise(got["sw1"][rows], s1, "updated scales")
+    assert_bitwise(got["qw1"][rows], q1, "updated codes")
+
+
+def test_tiny_train_step(orc):
+    """The tiny workload end to end (64 x 256 -> 128, bias, no rotation)."""
+    T = torch_cuda()
+    d = workloads.tiny()
+    got = _step(T, d, 64, 256, 128, 0, d["lr"], 0, 0)
+    _check_step(orc, d, got, 64, 256, 128, 0, d["lr"], 0, 0, 2000, np.random.default_rng(1))
+
+
+@pytest.mark.parametrize("M", [17, 2048])
+def test_forward_width_step(orc, M):
+    T = torch_cuda()
+    d = workloads.linear(M, 5376, 7168, seed=0)
+    got = _step(T, d, M, 5376, 7168, 128, 1e-3, 0, 3)
+    _check_step(orc, d, got, M, 5376, 7168, 128, 1e-3, 0, 3, 2048, np.random.default_rng(2))
+
+
+def test_headline_step(orc):
+    """12000 x 5376 -> 7168, rotation 128: the benchmarked training step."""
+    T = torch_cuda()
+    d = workloads.linear(12000, 5376, 7168, seed=0)
+    got = _step(T, d, 12000, 5376, 7168, 128, 1e-3, 0, 0)
+    _check_step(orc, d, got, 12000, 5376, 7168, 128, 1e-3, 0, 0, 2048, np.random.default_rng(3))
+
+
+def test_deterministic(orc):
+    """Two runs of the headline step give bitwise identical results."""
+    T = torch_cuda()
+    d = workloads.linear(2048, 5376, 7168, seed=5)
+    a = _step(T, d, 2048, 5376, 7168, 128, 1e-3, 9, 1)
+    b = _step(T, d, 2048, 5376, 7168, 128, 1e-3, 9, 1)
+    for k in a:
+        assert_bitwise(a[k], b[k], k)

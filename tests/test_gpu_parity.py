@@ -1,0 +1,270 @@
+"""GPU parity: every C-ABI call against the CPU oracle on identical seeded inputs.
+
+Integer outputs (codes, int32 accumulators, stochastically rounded weights)
+and the fp32 outputs are compared bit for bit: both sides follow the same
+operation order (IEEE binary32, no FMA contraction, round to nearest even),
+so the 1e-5 relative bound of the contract is met with zero difference.  The
+one exception is the column sum (bias gradient), whose fp32 order is
+unspecified: it is held to 1e-5 of the sum of magnitudes.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from tests.gpu_util import announce, assert_bitwise, dev, host, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def T():
+    return torch_cuda()
+
+
+@pytest.fixture(scope="module")
+def Q():
+    import w8a8_integer_linear_amd as q
+    return q
+
+
+def _x(rng, rows, cols, bf16, scale=1.0):
+    x = (rng.standard_normal((rows, cols), dtype=np.float32) * np.float32(scale)).astype(np.float32)
+    return workloads.f32_to_bf16_bits(x) if bf16 else x
+
+
+# --------------------------------------------------------------- quantizers
+
+ROW_CASES = [
+    # rows, cols, had, bf16, prescale
+    (64, 256, 0, False, False),        # tiny workload's activations
+    (17, 5376, 128, True, False),      # forward activations, rotated
+    (1, 16, 0, True, False),
+    (15, 48, 16, False, True),
+    (16, 7168, 0, True, True),         # dY * s_w for dX
+    (65, 2048, 512, False, False),     # largest block, one 256-thread pass
+    (3, 2064, 2, True, True),          # ragged second pass
+    (5, 14336, 128, False, False),     # MLP fc2 input width
+    (2, 20480, 256, True, False),      # 1024-thread path
+    (2, 131072, 64, False, True),      # longest row
+]
+
+
+@pytest.mark.parametrize("rows,cols,had,bf16,pre", ROW_CASES)
+def test_quantize_rows(T, Q, orc, rows, cols, had, bf16, pre):
+    rng = np.random.default_rng(rows * 131 + cols)
+    x = _x(rng, rows, cols, bf16)
+    p = rng.uniform(0.25, 4.0, cols).astype(np.float32) if pre else None
+    announce("quantize_rows", rows, cols, had, bf16, pre)
+    q, s = Q.qlin_quantize_rows(dev(x), prescale=None if p is None else dev(p), had_block=had)
+    T.cuda.synchronize()
+    qr, sr = orc.quantize_rows(x, prescale=p, had_block=had)
+    assert_bitwise(host(s), sr, "scales")
+    assert_bitwise(host(q), qr, "codes")
+
+
+def test_quantize_rows_edge_values(T, Q, orc):
+    """Zero rows, subnormal scales, huge values, exact ties."""
+    rows, cols = 6, 64
+    x = np.zeros((rows, cols), np.float32)
+    x[1, :] = np.float32(1e-40)                      # subnormal amax
+    x[1, 3] = np.float32(-3e-40)
+    x[2, :] = np.linspace(-3e38, 3e38, cols, dtype=np.float32)
+    x[3, :8] = np.array([127, 0.5, 1.5, 2.5, -0.5, -2.5, 126.5, -126.5], np.float32) * 2.0 ** -6
+    rng = np.random.default_rng(0)
+    x[4] = rng.standard_normal(cols).astype(np.float32)
+    x[5] = np.float32(7.0)
+    announce("quantize_rows edge values")
+    q, s = Q.qlin_quantize_rows(dev(x))
+    T.cuda.synchronize()
+    qr, sr = orc.quantize_rows(x)
+    assert_bitwise(host(s), sr, "scales")
+    assert_bitwise(host(q), qr, "codes")
+
+
+COL_CASES = [(64, 128, False, True), (17, 48, True, True), (1, 16, False, False),
+             (300, 7168, True, True), (12000, 272, True, True), (0, 32, True, True)]
+
+
+@pytest.mark.parametrize("rows,cols,bf16,pre", COL_CASES)
+def test_quantize_cols(T, Q, orc, rows, cols, bf16, pre):
+    rng = np.random.default_rng(rows + 7 * cols)
+    x = _x(rng, rows, cols, bf16, 0.01)
+    p = rng.uniform(1e-3, 1e-1, rows).astype(np.float32) if pre else None
+    announce("quantize_cols", rows, cols, bf16, pre)
+    q, s, cs = Q.qlin_quantize_cols(dev(x), prescale=None if p is None else dev(p), want_sum=True)
+    T.cuda.synchronize()
+    qr, sr, csr = orc.quantize_cols(x, prescale=p, want_sum=True)
+    assert_bitwise(host(s), sr, "scales")
+    assert_bitwise(host(q), qr, "codes")
+    xf = workloads.bf16_bits_to_f32(x) if bf16 else x
+    bound = 1e-5 * np.abs(xf.astype(np.float64)).sum(axis=0) + 1e-30
+    assert np.all(np.abs(host(cs).astype(np.float64) - csr) <= bound)
+
+
+@pytest.mark.parametrize("rows,cols,blk,bf16", [(3, 256, 128, False), (64, 5376, 128, False),
+                                                (5, 1024, 512, True), (7, 64, 2, False),
+                                                (9, 96, 32, True), (1, 16, 8, False)])
+def test_hadamard(T, Q, orc, rows, cols, blk, bf16):
+    rng = np.random.default_rng(blk + rows)
+    x = _x(rng, rows, cols, bf16)
+    announce("hadamard", rows, cols, blk, bf16)
+    xd = dev(x)
+    if bf16:
+        y = Q.qlin_hadamard(xd, blk)
+    else:
+        y = Q.qlin_hadamard(xd, blk, y=xd)          # in place
+    T.cuda.synchronize()
+    assert_bitwise(host(y), orc.hadamard(x, blk), "rotation")
+
+
+# ----------------------------------------------------------------- products
+
+PRODUCT_SHAPES = [
+    (64, 128, 256),      # tiny workload
+    (1, 16, 16), (15, 48, 32), (16, 64, 80), (17, 48, 32),   # around the row floor
+    (130, 272, 208),     # ragged tiles in every dimension
+    (257, 144, 5376),    # long contraction
+    (33, 4096, 64),      # many output columns
+]
+
+
+def _codes(rng, shape):
+    return rng.integers(-127, 128, size=shape).astype(np.int8)
+
+
+@pytest.mark.parametrize("M,N,K", PRODUCT_SHAPES)
+def test_gemm_s32(T, Q, orc, M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    qx, qw, qg = _codes(rng, (M, K)), _codes(rng, (N, K)), _codes(rng, (M, N))
+    for op, a, b in ((Q.QLIN_OP_FWD, qx, qw), (Q.QLIN_OP_DX, qg, qw), (Q.QLIN_OP_DW, qg, qx)):
+        announce("gemm_s32", op, M, N, K)
+        c = Q.qlin_gemm_s32(op, dev(a), dev(b), M, N, K)
+        T.cuda.synchronize()
+        assert_bitwise(host(c), orc.gemm_s32(op, a, b, M, N, K), f"acc op{op}")
+
+
+def test_gemm_s32_extremes(T, Q, orc):
+    """All +-127 codes at the longest contractions the test can afford."""
+    M, N, K = 32, 32, 16384
+    a = np.full((M, K), 127, np.int8)
+    b = np.full((N, K), -127, np.int8)
+    a[1] = -127
+    announce("gemm_s32 extremes")
+    c = Q.qlin_gemm_s32(Q.QLIN_OP_FWD, dev(a), dev(b), M, N, K)
+    T.cuda.synchronize()
+    assert_bitwise(host(c), orc.gemm_s32(0, a, b, M, N, K), "acc")
+
+
+@pytest.mark.parametrize("M,N,K", PRODUCT_SHAPES)
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_products_dequant(T, Q, orc, M, N, K, with_bias):
+    rng = np.random.default_rng(3 * M + N)
+    qx, qw, qg = _codes(rng, (M, K)), _codes(rng, (N, K)), _codes(rng, (M, N))
+    sx = rng.uniform(1e-3, 1e-1, M).astype(np.float32)
+    sw = rng.uniform(1e-4, 1e-2, N).astype(np.float32)
+    sg1 = rng.uniform(1e-6, 1e-4, M).astype(np.float32)
+    sg2 = rng.uniform(1e-6, 1e-4, N).astype(np.float32)
+    b = rng.standard_normal(N).astype(np.float32) * np.float32(0.01) if with_bias else None
+    announce("fwd", M, N, K, with_bias)
+    y = Q.qlin_fwd(dev(qx), dev(sx), dev(qw), dev(sw), None if b is None else dev(b))
+    T.cuda.synchronize()
+    assert_bitwise(host(y), orc.fwd(qx, sx, qw, sw, b), "y")
+    if with_bias:
+        return
+    announce("bwd_dx", M, N, K)
+    dx = Q.qlin_bwd_dx(dev(qg), dev(sg1), dev(qw))
+    T.cuda.synchronize()
+    assert_bitwise(host(dx), orc.bwd_dx(qg, sg1, qw), "dx")
+    announce("bwd_dw", M, N, K)
+    dw = Q.qlin_bwd_dw(dev(qg), dev(sg2), dev(qx))
+    T.cuda.synchronize()
+    assert_bitwise(host(dw), orc.bwd_dw(qg, sg2, qx), "dw")
+
+
+@pytest.mark.parametrize("M", [1, 4, 15, 16])
+def test_skinny_forward(T, Q, orc, M):
+    """M <= 16 takes the weight-streaming kernel (skinny workload: 4096 -> 4096)."""
+    d = workloads.skinny(M, K=4096, N=4096)
+    qw, sw = orc.prepare_weight(d["w"])
+    qx, sx = orc.quantize_rows(d["x"])
+    announce("skinny fwd", M)
+    y = Q.qlin_fwd(dev(qx), dev(sx), dev(qw), dev(sw))
+    c = Q.qlin_gemm_s32(Q.QLIN_OP_FWD, dev(qx), dev(qw), M, 4096, 4096)
+    T.cuda.synchronize()
+    assert_bitwise(host(c), orc.gemm_s32(0, qx, qw, M, 4096, 4096), "acc")
+    assert_bitwise(host(y), orc.fwd(qx, sx, qw, sw), "y")
+    bias = np.linspace(-1, 1, 4096, dtype=np.float32)
+    y2 = Q.qlin_fwd(dev(qx), dev(sx), dev(qw), dev(sw), dev(bias))
+    T.cuda.synchronize()
+    assert_bitwise(host(y2), orc.fwd(qx, sx, qw, sw, bias), "y+bias")
+
+
+def test_dw_empty_tokens(T, Q, orc):
+    N, K = 32, 48
+    announce("bwd_dw M=0")
+    dw = Q.qlin_bwd_dw(dev(np.zeros((0, N), np.int8)), dev(np.ones(N, np.float32)),
+                       dev(np.zeros((0, K), np.int8)))
+    T.cuda.synchronize()
+    assert np.all(host(dw) == 0)
+
+
+# ------------------------------------------------------------------ update
+
+SGD_CASES = [(128, 256, True), (64, 5376, False), (7, 16, True), (3, 20480, False),
+             (5, 14336, True)]
+
+
+@pytest.mark.parametrize("N,K,with_bias", SGD_CASES)
+def test_sgd_requant(T, Q, orc, N, K, with_bias):
+    rng = np.random.default_rng(N * K)
+    qw = _codes(rng, (N, K))
+    qw[:, 0] = 127
+    sw = rng.uniform(1e-4, 1e-2, N).astype(np.float32)
+    dw = rng.standard_normal((N, K)).astype(np.float32)
+    bias = rng.standard_normal(N).astype(np.float32) if with_bias else None
+    db = rng.standard_normal(N).astype(np.float32) if with_bias else None
+    for seed, step, lr in ((0, 0, 1e-3), (123456789012, 2 ** 33 + 5, 0.5), (1, 7, 0.0)):
+        announce("sgd_requant", N, K, seed, step, lr)
+        qd, sd, dd = dev(qw), dev(sw), dev(dw)
+        bd = None if bias is None else dev(bias)
+        Q.qlin_sgd_requant(qd, sd, dd, lr, seed, step, bias=bd,
+                           db=None if db is None else dev(db))
+        T.cuda.synchronize()
+        qr, sr, br = orc.sgd_requant(qw, sw, dw, lr, seed, step, bias=bias, db=db)
+        assert_bitwise(host(sd), sr, "scales")
+        assert_bitwise(host(qd), qr, "codes")
+        if bias is not None:
+            assert_bitwise(host(bd), br, "bias")
+
+
+def test_sgd_zero_rows(T, Q, orc):
+    N, K = 4, 64
+    qw = np.zeros((N, K), np.int8)
+    qw[1] = 5
+    sw = np.array([0.0, 0.5, 0.0, 1e-3], np.float32)
+    dw = np.zeros((N, K), np.float32)
+    dw[2, 3] = 1.0
+    announce("sgd_requant zero rows")
+    qd, sd = dev(qw), dev(sw)
+    Q.qlin_sgd_requant(qd, sd, dev(dw), 0.25, 0, 0)
+    T.cuda.synchronize()
+    qr, sr, _ = orc.sgd_requant(qw, sw, dw, 0.25, 0, 0)
+    assert_bitwise(host(sd), sr, "scales")
+    assert_bitwise(host(qd), qr, "codes")
+
+
+# --------------------------------------------------------- error behaviour
+
+def test_rejected_calls_leave_outputs_untouched(T, Q):
+    x = T.randn(4, 48, device="cuda")
+    q = T.full((4, 48), 5, dtype=T.int8, device="cuda")
+    s = T.full((4,), 3.0, device="cuda")
+    with pytest.raises(Q.QlinError):
+        Q.qlin_quantize_rows(x, had_block=32, q=q, s=s)     # 32 does not divide 48
+    qw = T.zeros((16, 131072), dtype=T.int8, device="cuda")
+    y = T.full((2, 16), 7.0, device="cuda")
+    with pytest.raises(Q.QlinError):
+        Q.qlin_fwd(T.zeros((2, 131072), dtype=T.int8, device="cuda"),
+                   T.ones(2, device="cuda"), qw, T.ones(16, device="cuda"), y=y)
+    T.cuda.synchronize()
+    assert bool((q == 5).all()) and bool((s == 3.0).all()) and bool((y == 7.0).all())

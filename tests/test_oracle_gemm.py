@@ -134,3 +134,15 @@ def test_rejects_long_contractions(orc):
     with pytest.raises(orc.OracleError):
         orc.bwd_dw(np.zeros((131072, 16), np.int8), np.zeros(16, np.float32),
                    np.zeros((131072, 16), np.int8))
+
+
+def test_dw_rows_and_brute_force(orc):
+    rng = np.random.default_rng(6)
+    M, N, K = 45, 32, 48
+    qg, qx = _codes(rng, (M, N)), _codes(rng, (M, K))
+    sg = rng.random(N).astype(np.float32)
+    full = orc.bwd_dw(qg, sg, qx)
+    acc = qg.astype(np.int64).T @ qx.astype(np.int64)
+    assert np.array_equal(full, (acc.astype(np.float32) * sg[:, None]).astype(np.float32))
+    rows = np.array([31, 0, 7, 7])
+    assert np.array_equal(orc.bwd_dw_rows(qg, sg, qx, rows), full[rows])

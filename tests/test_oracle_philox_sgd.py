@@ -156,3 +156,15 @@ def test_seed_and_step_select_the_stream(orc):
     d = orc.sgd_requant(q, s, dw, 1e-3, seed=2, step=5)[0]
     assert np.array_equal(a, b)
     assert not np.array_equal(a, c) and not np.array_equal(a, d)
+
+
+def test_row_ids_key_the_stream(orc):
+    """Updating selected rows with their global ids equals updating the full matrix."""
+    rng = np.random.default_rng(7)
+    q = rng.integers(-127, 128, size=(9, 64)).astype(np.int8)
+    s = rng.uniform(1e-3, 1e-2, 9).astype(np.float32)
+    dw = rng.standard_normal((9, 64)).astype(np.float32)
+    qf, sf, _ = orc.sgd_requant(q, s, dw, 1e-2, seed=4, step=2)
+    rows = np.array([8, 3, 5])
+    qs, ss, _ = orc.sgd_requant(q[rows], s[rows], dw[rows], 1e-2, seed=4, step=2, row_ids=rows)
+    assert np.array_equal(qs, qf[rows]) and np.array_equal(ss, sf[rows])

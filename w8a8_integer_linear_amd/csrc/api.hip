@@ -1,0 +1,216 @@
+// C-ABI entry points of libqlin: argument validation, then kernel launches on
+// the caller's stream.  Every check runs before the first launch, so a
+// rejected call leaves all outputs untouched; the validation itself makes no
+// HIP call.
+#include <math.h>
+
+#include "../../include/qlin.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+bool dtype_ok(int dt) { return dt == QLIN_F32 || dt == QLIN_BF16; }
+bool dim16(int64_t v) { return v >= 16 && v % 16 == 0; }
+bool hadamard_block_ok(int64_t cols, int b)
+{
+    return b >= 2 && b <= QLIN_MAX_HAD_BLOCK && pow2(b) && cols % b == 0;
+}
+
+// Both optional pointers 16-byte aligned when present.
+bool opt_aligned(const void *p) { return p == nullptr || aligned16(p); }
+
+// Largest token count a call accepts (grid dimensions and int32 tile indices).
+constexpr int64_t kMaxRows = (int64_t)1 << 30;
+
+int finish()
+{
+    return hipGetLastError() == hipSuccess ? QLIN_OK : QLIN_EDEVICE;
+}
+
+// fl32(1 / sqrt(b)), the rotation's normalisation.
+float hadamard_scale(int b) { return (float)(1.0 / sqrt((double)b)); }
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+} // namespace
+
+extern "C" {
+
+const char *qlin_status_string(int status)
+{
+    switch (status) {
+    case QLIN_OK: return "ok";
+    case QLIN_EINVAL: return "invalid argument";
+    case QLIN_EUNSUPPORTED: return "unsupported shape";
+    case QLIN_EDEVICE: return "device error";
+    default: return "unknown status";
+    }
+}
+
+int qlin_abi_version(void) { return kAbiVersion; }
+
+int qlin_quantize_rows(const void *x, int dtype, int64_t rows, int64_t cols,
+                       const float *prescale, int had_block, int8_t *q, float *s, void *stream)
+{
+    if (!x || !q || !s || !dtype_ok(dtype))
+        return QLIN_EINVAL;
+    if (!aligned16(x) || !aligned16(q) || !opt_aligned(prescale))
+        return QLIN_EINVAL;
+    if (rows < 0 || !dim16(cols))
+        return QLIN_EINVAL;
+    if (had_block != 0 && !hadamard_block_ok(cols, had_block))
+        return QLIN_EINVAL;
+    if (cols > QLIN_MAX_ROW || rows > kMaxRows)
+        return QLIN_EUNSUPPORTED;
+    if (rows == 0)
+        return QLIN_OK;
+    qlin::launch_quantize_rows(x, dtype == QLIN_BF16, rows, cols, prescale, had_block,
+                               had_block ? hadamard_scale(had_block) : 1.0f, q, s,
+                               as_stream(stream));
+    return finish();
+}
+
+int qlin_quantize_cols(const void *x, int dtype, int64_t rows, int64_t cols,
+                       const float *prescale, int8_t *q, float *s, float *col_sum, void *stream)
+{
+    if (!x || !q || !s || !dtype_ok(dtype))
+        return QLIN_EINVAL;
+    if (!aligned16(x) || !aligned16(q))
+        return QLIN_EINVAL;
+    if (rows < 0 || !dim16(cols))
+        return QLIN_EINVAL;
+    if (col_sum == s || (const void *)s == x || (const void *)col_sum == x)
+        return QLIN_EINVAL;
+    if (rows > 65535LL * 16)          // grid.y of the quantize pass stays below 65536
+        return QLIN_EUNSUPPORTED;
+    qlin::launch_quantize_cols(x, dtype == QLIN_BF16, rows, cols, prescale, q, s, col_sum,
+                               as_stream(stream));
+    return finish();
+}
+
+int qlin_hadamard(const void *x, int dtype, int64_t rows, int64_t cols, int block, float *y,
+                  void *stream)
+{
+    if (!x || !y || !dtype_ok(dtype))
+        return QLIN_EINVAL;
+    if (!aligned16(x) || !aligned16(y))
+        return QLIN_EINVAL;
+    if (rows < 0 || !dim16(cols) || !hadamard_block_ok(cols, block))
+        return QLIN_EINVAL;
+    if (dtype == QLIN_BF16 && rows > 0) {
+        // y may alias x only for an in-place fp32 call.
+        const char *xb = static_cast<const char *>(x), *yb = reinterpret_cast<const char *>(y);
+        const int64_t n = rows * cols;
+        if (yb < xb + 2 * n && xb < yb + 4 * n)
+            return QLIN_EINVAL;
+    }
+    if (rows > (int64_t)1 << 40 || (rows * cols) / 8 / 256 >= ((int64_t)1 << 31))
+        return QLIN_EUNSUPPORTED;
+    if (rows == 0)
+        return QLIN_OK;
+    qlin::launch_hadamard(x, dtype == QLIN_BF16, rows, cols, block, hadamard_scale(block), y,
+                          as_stream(stream));
+    return finish();
+}
+
+// Shared checks of the three products: shapes, then the contraction bound.
+static int check_product(int op, const void *a, const void *b, void *out, int64_t M, int64_t N,
+                         int64_t K)
+{
+    if (!a || !b || !out)
+        return QLIN_EINVAL;
+    if (!aligned16(a) || !aligned16(b) || !aligned16(out))
+        return QLIN_EINVAL;
+    if (M < 0 || !dim16(N) || !dim16(K))
+        return QLIN_EINVAL;
+    const int64_t contraction = op == QLIN_OP_FWD ? K : (op == QLIN_OP_DX ? N : M);
+    if (contraction > QLIN_MAX_CONTRACTION || M > kMaxRows || N > kMaxRows || K > kMaxRows)
+        return QLIN_EUNSUPPORTED;
+    return QLIN_OK;
+}
+
+int qlin_fwd(const int8_t *qx, const float *sx, const int8_t *qw, const float *sw,
+             const float *bias, int64_t M, int64_t N, int64_t K, float *y, void *stream)
+{
+    int st = check_product(QLIN_OP_FWD, qx, qw, y, M, N, K);
+    if (st != QLIN_OK)
+        return st;
+    if (!sx || !sw)
+        return QLIN_EINVAL;
+    if (M == 0)
+        return QLIN_OK;
+    qlin::ProductArgs p{QLIN_OP_FWD, qx, qw, M, N, K, sx, sw, bias, y, false};
+    qlin::launch_product(p, as_stream(stream));
+    return finish();
+}
+
+int qlin_bwd_dx(const int8_t *qg1, const float *sg1, const int8_t *qw, int64_t M, int64_t N,
+                int64_t K, float *dx, void *stream)
+{
+    int st = check_product(QLIN_OP_DX, qg1, qw, dx, M, N, K);
+    if (st != QLIN_OK)
+        return st;
+    if (!sg1)
+        return QLIN_EINVAL;
+    if (M == 0)
+        return QLIN_OK;
+    qlin::ProductArgs p{QLIN_OP_DX, qg1, qw, M, N, K, sg1, nullptr, nullptr, dx, false};
+    qlin::launch_product(p, as_stream(stream));
+    return finish();
+}
+
+int qlin_bwd_dw(const int8_t *qg2, const float *sg2, const int8_t *qx, int64_t M, int64_t N,
+                int64_t K, float *dw, void *stream)
+{
+    int st = check_product(QLIN_OP_DW, qg2, qx, dw, M, N, K);
+    if (st != QLIN_OK)
+        return st;
+    if (!sg2)
+        return QLIN_EINVAL;
+    // An empty token range still defines dW (all zero).
+    qlin::ProductArgs p{QLIN_OP_DW, qg2, qx, M, N, K, sg2, nullptr, nullptr, dw, false};
+    qlin::launch_product(p, as_stream(stream));
+    return finish();
+}
+
+int qlin_gemm_s32(int op, const int8_t *a, const int8_t *b, int64_t M, int64_t N, int64_t K,
+                  int32_t *c, void *stream)
+{
+    if (op != QLIN_OP_FWD && op != QLIN_OP_DX && op != QLIN_OP_DW)
+        return QLIN_EINVAL;
+    int st = check_product(op, a, b, c, M, N, K);
+    if (st != QLIN_OK)
+        return st;
+    if (M == 0 && op != QLIN_OP_DW)
+        return QLIN_OK;
+    qlin::ProductArgs p{op, a, b, M, N, K, nullptr, nullptr, nullptr, c, true};
+    qlin::launch_product(p, as_stream(stream));
+    return finish();
+}
+
+int qlin_sgd_requant(int8_t *qw, float *sw, const float *dw, int64_t N, int64_t K, float lr,
+                     uint64_t seed, uint64_t step, float *bias, const float *db, void *stream)
+{
+    if (!qw || !sw || !dw)
+        return QLIN_EINVAL;
+    if (!aligned16(qw) || !aligned16(dw))
+        return QLIN_EINVAL;
+    if ((bias == nullptr) != (db == nullptr))
+        return QLIN_EINVAL;
+    if (N < 0 || !dim16(K))
+        return QLIN_EINVAL;
+    if (!isfinite(lr))
+        return QLIN_EINVAL;
+    if (K > QLIN_MAX_ROW || N > kMaxRows)
+        return QLIN_EUNSUPPORTED;
+    if (N == 0)
+        return QLIN_OK;
+    qlin::launch_sgd_requant(qw, sw, dw, N, K, lr, seed, step, bias, db, as_stream(stream));
+    return finish();
+}
+
+} // extern "C"

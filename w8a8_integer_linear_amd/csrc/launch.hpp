@@ -1,0 +1,40 @@
+// Host-side launchers of the qlin kernels.  Arguments are validated by the
+// C-ABI layer (api.hip) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qlin {
+
+void launch_quantize_rows(const void *x, bool bf16, int64_t rows, int64_t cols,
+                          const float *prescale, int had, float cb, int8_t *q, float *s,
+                          hipStream_t st);
+
+void launch_quantize_cols(const void *x, bool bf16, int64_t rows, int64_t cols,
+                          const float *prescale, int8_t *q, float *s, float *col_sum,
+                          hipStream_t st);
+
+void launch_hadamard(const void *x, bool bf16, int64_t rows, int64_t cols, int blk, float cb,
+                     float *y, hipStream_t st);
+
+// Products.  op: 0 forward, 1 dX, 2 dW.  epi: 0 raw int32, 1 dequant.
+struct ProductArgs {
+    int op;
+    const int8_t *a;
+    const int8_t *b;
+    int64_t M, N, K;
+    const float *srow;  // sx, sg1 or sg2
+    const float *scol;  // sw (forward only)
+    const float *bias;  // forward only, may be null
+    void *out;          // float* or int32_t*
+    bool raw;           // int32 accumulators instead of dequantized floats
+};
+
+void launch_product(const ProductArgs &p, hipStream_t st);
+
+void launch_sgd_requant(int8_t *qw, float *sw, const float *dw, int64_t N, int64_t K, float lr,
+                        uint64_t seed, uint64_t step, float *bias, const float *db,
+                        hipStream_t st);
+
+} // namespace qlin

@@ -1,0 +1,330 @@
+// Row and column INT8 quantizers and the block-Hadamard rotation.
+//
+// Row quantization (OneTrainer PR #1681: activations rotated along the
+// contraction dimension and quantized per row on every call): one workgroup
+// per row, the row held in registers (eight consecutive elements per lane),
+// rotation done with in-lane and cross-lane butterflies, absmax reduced over
+// the workgroup, then codes written as packed bytes.  One HBM read of x and
+// one write of q.
+//
+// Column quantization (the weight-gradient operand; its scales sit on the
+// product's output axis): pass 1 reduces |x * prescale[r]| over row slabs and
+// merges slabs with an order-free integer atomicMax on the fp32 bits of the
+// non-negative maxima; a tiny kernel turns maxima into scales; pass 2
+// quantizes elementwise.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace qlin {
+
+// ------------------------------------------------------------ row quantizer
+
+template <bool BF16, int THREADS, int J>
+__global__ __launch_bounds__(THREADS) void quant_rows_kernel(
+    const void *__restrict__ x, int64_t cols, const float *__restrict__ prescale, int had,
+    float cb, int8_t *__restrict__ q, float *__restrict__ s)
+{
+    __shared__ float red[THREADS / kWave];
+    const int64_t row = blockIdx.x;
+    const int t = threadIdx.x;
+    const int64_t nch = cols / 8;
+    const int64_t base = row * cols;
+    float v[J][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < J; j++) {
+        const int64_t c = t + (int64_t)j * THREADS;
+        const bool ok = c < nch;
+        if (ok) {
+            load8<BF16>(x, base + c * 8, v[j]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                v[j][e] = 0.0f;
+        }
+        // Chunk index c is the same function of the lane in every pass, so
+        // lanes of one block stay together; a block is all valid or all
+        // padding because had divides cols.
+        if (had)
+            fwht8_lanes(v[j], had, cb);
+        if (prescale && ok) {
+            const float *p = prescale + c * 8;
+            f32x4 p0 = reinterpret_cast<const f32x4 *>(p)[0];
+            f32x4 p1 = reinterpret_cast<const f32x4 *>(p)[1];
+            v[j][0] = v[j][0] * p0[0]; v[j][1] = v[j][1] * p0[1];
+            v[j][2] = v[j][2] * p0[2]; v[j][3] = v[j][3] * p0[3];
+            v[j][4] = v[j][4] * p1[0]; v[j][5] = v[j][5] * p1[1];
+            v[j][6] = v[j][6] * p1[2]; v[j][7] = v[j][7] * p1[3];
+        }
+        if (ok) {
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                amax = fmaxf(amax, __builtin_fabsf(v[j][e]));
+        }
+    }
+    const float a = block_max<THREADS>(amax, red);
+    const float sc = a / 127.0f;
+    if (t == 0)
+        s[row] = sc;
+    const float inv = 1.0f / sc;
+    const bool zero = (a == 0.0f);
+    const bool subnormal = !zero && sc < 0x1p-126f;
+#pragma unroll
+    for (int j = 0; j < J; j++) {
+        const int64_t c = t + (int64_t)j * THREADS;
+        if (c >= nch)
+            continue;
+        float r[8];
+        if (zero) {
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                r[e] = 0.0f;
+        } else if (subnormal) {
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                r[e] = quant_code_exact(v[j][e], sc);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                r[e] = quant_code(v[j][e], sc, inv);
+        }
+        i32x2 out;
+        out[0] = (int)pack4(r[0], r[1], r[2], r[3]);
+        out[1] = (int)pack4(r[4], r[5], r[6], r[7]);
+        *reinterpret_cast<i32x2 *>(q + base + c * 8) = out;
+    }
+}
+
+template <bool BF16, int THREADS, int J>
+static void launch_rows_t(const void *x, int64_t rows, int64_t cols, const float *prescale,
+                          int had, float cb, int8_t *q, float *s, hipStream_t st)
+{
+    hipLaunchKernelGGL((quant_rows_kernel<BF16, THREADS, J>), dim3((unsigned)rows),
+                       dim3(THREADS), 0, st, x, cols, prescale, had, cb, q, s);
+}
+
+template <bool BF16>
+static void launch_rows_dt(const void *x, int64_t rows, int64_t cols, const float *prescale,
+                           int had, float cb, int8_t *q, float *s, hipStream_t st)
+{
+    // Registers per lane: 8 * J floats.  256 threads cover 2048 elements per
+    // pass; rows longer than 16384 switch to 1024 threads.
+    const int64_t nch = cols / 8;
+    const int64_t j256 = (nch + 255) / 256;
+    switch (j256) {
+    case 1: return launch_rows_t<BF16, 256, 1>(x, rows, cols, prescale, had, cb, q, s, st);
+    case 2: return launch_rows_t<BF16, 256, 2>(x, rows, cols, prescale, had, cb, q, s, st);
+    case 3: return launch_rows_t<BF16, 256, 3>(x, rows, cols, prescale, had, cb, q, s, st);
+    case 4: return launch_rows_t<BF16, 256, 4>(x, rows, cols, prescale, had, cb, q, s, st);
+    case 5: return launch_rows_t<BF16, 256, 5>(x, rows, cols, prescale, had, cb, q, s, st);
+    case 6: return launch_rows_t<BF16, 256, 6>(x, rows, cols, prescale, had, cb, q, s, st);
+    case 7: return launch_rows_t<BF16, 256, 7>(x, rows, cols, prescale, had, cb, q, s, st);
+    case 8: return launch_rows_t<BF16, 256, 8>(x, rows, cols, prescale, had, cb, q, s, st);
+    default: break;
+    }
+    const int64_t j1024 = (nch + 1023) / 1024;
+    if (j1024 <= 4)
+        return launch_rows_t<BF16, 1024, 4>(x, rows, cols, prescale, had, cb, q, s, st);
+    if (j1024 <= 8)
+        return launch_rows_t<BF16, 1024, 8>(x, rows, cols, prescale, had, cb, q, s, st);
+    return launch_rows_t<BF16, 1024, 16>(x, rows, cols, prescale, had, cb, q, s, st);
+}
+
+void launch_quantize_rows(const void *x, bool bf16, int64_t rows, int64_t cols,
+                          const float *prescale, int had, float cb, int8_t *q, float *s,
+                          hipStream_t st)
+{
+    if (bf16)
+        launch_rows_dt<true>(x, rows, cols, prescale, had, cb, q, s, st);
+    else
+        launch_rows_dt<false>(x, rows, cols, prescale, had, cb, q, s, st);
+}
+
+// --------------------------------------------------------- column quantizer
+
+// Zero the per-column accumulators (a fill kernel rather than a memset so the
+// sequence stays valid inside captured graphs).
+__global__ void zero_cols_kernel(float *__restrict__ s, float *__restrict__ col_sum, int64_t cols)
+{
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c < cols) {
+        s[c] = 0.0f;
+        if (col_sum)
+            col_sum[c] = 0.0f;
+    }
+}
+
+// Pass 1: each workgroup covers 512 columns (64 lanes x 8) and a slab of
+// kColSlab rows split over 4 row lanes.  Maxima of |x * p[r]| are merged into
+// s[] with atomicMax on the fp32 bit patterns (monotone for values >= 0);
+// column sums of the raw x with fp32 atomicAdd.
+constexpr int kColSlab = 256;
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void colmax_kernel(const void *__restrict__ x, int64_t rows,
+                                                     int64_t cols,
+                                                     const float *__restrict__ prescale,
+                                                     float *__restrict__ s,
+                                                     float *__restrict__ col_sum)
+{
+    __shared__ float red_max[4][512];
+    __shared__ float red_sum[4][512];
+    const int lc = threadIdx.x % 64;
+    const int lr = threadIdx.x / 64;
+    const int64_t c0 = (int64_t)blockIdx.x * 512 + lc * 8;
+    const int64_t r0 = (int64_t)blockIdx.y * kColSlab;
+    const int64_t r1 = r0 + kColSlab < rows ? r0 + kColSlab : rows;
+    float mx[8], sm[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        mx[e] = 0.0f;
+        sm[e] = 0.0f;
+    }
+    if (c0 < cols) {
+        for (int64_t r = r0 + lr; r < r1; r += 4) {
+            float v[8];
+            load8<BF16>(x, r * cols + c0, v);
+            const float p = prescale ? prescale[r] : 1.0f;
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                sm[e] = sm[e] + v[e];
+                float g = prescale ? v[e] * p : v[e];
+                mx[e] = fmaxf(mx[e], __builtin_fabsf(g));
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        red_max[lr][lc * 8 + e] = mx[e];
+        red_sum[lr][lc * 8 + e] = sm[e];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 512; i += 256) {
+        const int64_t c = (int64_t)blockIdx.x * 512 + i;
+        if (c >= cols)
+            continue;
+        float m = fmaxf(fmaxf(red_max[0][i], red_max[1][i]), fmaxf(red_max[2][i], red_max[3][i]));
+        atomicMax(reinterpret_cast<unsigned int *>(s) + c, __float_as_uint(m));
+        if (col_sum) {
+            float t = ((red_sum[0][i] + red_sum[1][i]) + red_sum[2][i]) + red_sum[3][i];
+            atomicAdd(col_sum + c, t);
+        }
+    }
+}
+
+// Column maxima -> scales, in place: s = fl(amax / 127).
+__global__ void col_scale_kernel(float *__restrict__ s, int64_t cols)
+{
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c < cols)
+        s[c] = s[c] / 127.0f;
+}
+
+// Pass 2: codes.  Each thread owns 8 columns (so 8 reciprocals) and walks
+// kColRows rows of them.
+constexpr int kColRows = 16;
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void colquant_kernel(const void *__restrict__ x, int64_t rows,
+                                                       int64_t cols,
+                                                       const float *__restrict__ prescale,
+                                                       const float *__restrict__ s,
+                                                       int8_t *__restrict__ q)
+{
+    const int64_t nch = cols / 8;
+    const int64_t ch = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (ch >= nch)
+        return;
+    const int64_t c0 = ch * 8;
+    float sc[8], inv[8];
+    bool exact = false;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        sc[e] = s[c0 + e];
+        inv[e] = 1.0f / sc[e];
+        exact |= sc[e] < 0x1p-126f;   // zero or subnormal scale: exact path
+    }
+    const int64_t r0 = (int64_t)blockIdx.y * kColRows;
+    const int64_t r1 = r0 + kColRows < rows ? r0 + kColRows : rows;
+    for (int64_t r = r0; r < r1; r++) {
+        float v[8], out[8];
+        load8<BF16>(x, r * cols + c0, v);
+        const float p = prescale ? prescale[r] : 1.0f;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            float g = prescale ? v[e] * p : v[e];
+            if (!exact)
+                out[e] = quant_code(g, sc[e], inv[e]);
+            else
+                out[e] = sc[e] == 0.0f ? 0.0f : quant_code_exact(g, sc[e]);
+        }
+        i32x2 w;
+        w[0] = (int)pack4(out[0], out[1], out[2], out[3]);
+        w[1] = (int)pack4(out[4], out[5], out[6], out[7]);
+        *reinterpret_cast<i32x2 *>(q + r * cols + c0) = w;
+    }
+}
+
+void launch_quantize_cols(const void *x, bool bf16, int64_t rows, int64_t cols,
+                          const float *prescale, int8_t *q, float *s, float *col_sum,
+                          hipStream_t st)
+{
+    const unsigned cblocks = (unsigned)((cols + 255) / 256);
+    hipLaunchKernelGGL(zero_cols_kernel, dim3(cblocks), dim3(256), 0, st, s, col_sum, cols);
+    if (rows > 0) {
+        dim3 g1((unsigned)((cols + 511) / 512), (unsigned)((rows + kColSlab - 1) / kColSlab));
+        if (bf16)
+            hipLaunchKernelGGL(colmax_kernel<true>, g1, dim3(256), 0, st, x, rows, cols, prescale,
+                               s, col_sum);
+        else
+            hipLaunchKernelGGL(colmax_kernel<false>, g1, dim3(256), 0, st, x, rows, cols,
+                               prescale, s, col_sum);
+    }
+    hipLaunchKernelGGL(col_scale_kernel, dim3(cblocks), dim3(256), 0, st, s, cols);
+    if (rows > 0) {
+        dim3 g2((unsigned)((cols / 8 + 255) / 256), (unsigned)((rows + kColRows - 1) / kColRows));
+        if (bf16)
+            hipLaunchKernelGGL(colquant_kernel<true>, g2, dim3(256), 0, st, x, rows, cols,
+                               prescale, s, q);
+        else
+            hipLaunchKernelGGL(colquant_kernel<false>, g2, dim3(256), 0, st, x, rows, cols,
+                               prescale, s, q);
+    }
+}
+
+// --------------------------------------------------------------- rotation
+
+// Flat over 8-element chunks: a wave covers 64 consecutive chunks, so every
+// block (at most 64 chunks, aligned) sits inside one wave.
+template <bool BF16>
+__global__ __launch_bounds__(256) void hadamard_kernel(const void *__restrict__ x, int64_t nch,
+                                                       int blk, float cb, float *__restrict__ y)
+{
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const bool ok = c < nch;
+    float v[8];
+    if (ok) {
+        load8<BF16>(x, c * 8, v);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            v[e] = 0.0f;
+    }
+    fwht8_lanes(v, blk, cb);
+    if (ok)
+        store8(y, c * 8, v);
+}
+
+void launch_hadamard(const void *x, bool bf16, int64_t rows, int64_t cols, int blk, float cb,
+                     float *y, hipStream_t st)
+{
+    const int64_t nch = rows * cols / 8;
+    const unsigned grid = (unsigned)((nch + 255) / 256);
+    if (bf16)
+        hipLaunchKernelGGL(hadamard_kernel<true>, dim3(grid), dim3(256), 0, st, x, nch, blk, cb, y);
+    else
+        hipLaunchKernelGGL(hadamard_kernel<false>, dim3(grid), dim3(256), 0, st, x, nch, blk, cb,
+                           y);
+}
+
+} // namespace qlin

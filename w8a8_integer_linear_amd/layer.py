@@ -1,0 +1,90 @@
+"""One INT8 W8A8 linear layer in quantized training, as a sequence of C-ABI calls.
+
+State (mini_trainer guide: INT8 direction with a float magnitude per output
+row, no float master weight; OneTrainer PR #1681: the weight lives in the
+rotated basis): qw [N,K] int8, sw [N] fp32, optional float bias, and the
+saved INT8 input (qx, sx) of the last forward.  Buffers for up to
+``max_tokens`` rows are allocated once, so the steps allocate nothing.
+
+Step order of one training step:
+  forward   qlin_quantize_rows(x, rotate)          -> qx, sx   (saved)
+            qlin_fwd(qx, sx, qw, sw, bias)         -> y
+  backward  qlin_quantize_rows(dY, prescale=sw)    -> qg1, sg1
+            qlin_quantize_cols(dY, prescale=sx)    -> qg2, sg2 (+ db)
+            qlin_bwd_dx(qg1, sg1, qw)              -> dx (rotated basis)
+            qlin_hadamard(dx, in place)            -> dx
+            qlin_bwd_dw(qg2, sg2, qx)              -> dw
+  update    qlin_sgd_requant(qw, sw, dw, lr, seed, step, bias, db)
+"""
+import torch
+
+from . import _native as nat
+
+
+class LinearW8A8Training:
+    def __init__(self, weight, bias=None, had_block=128, max_tokens=0):
+        """weight: [N, K] float GPU tensor in the original basis (rotated here)."""
+        self.timer = None    # optional callable(label) invoked after each call
+        N, K = weight.shape
+        self.N, self.K, self.had = N, K, int(had_block)
+        dev = weight.device
+        w = weight.to(torch.float32).contiguous()
+        self.qw, self.sw = nat.qlin_quantize_rows(w, had_block=self.had)
+        if bool((self.sw == 0).any()):
+            raise ValueError("weight has an all-zero row (zero direction)")
+        self.bias = None if bias is None else bias.to(torch.float32).contiguous().clone()
+        self.max_tokens = 0
+        self.dw = torch.empty((N, K), dtype=torch.float32, device=dev)
+        self.db = None if bias is None else torch.empty(N, dtype=torch.float32, device=dev)
+        self._alloc(max_tokens, dev)
+
+    def _alloc(self, M, dev):
+        if M <= self.max_tokens:
+            return
+        N, K = self.N, self.K
+        self.max_tokens = M
+        self._qx = torch.empty((M, K), dtype=torch.int8, device=dev)
+        self._sx = torch.empty(M, dtype=torch.float32, device=dev)
+        self._y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        self._qg1 = torch.empty((M, N), dtype=torch.int8, device=dev)
+        self._sg1 = torch.empty(M, dtype=torch.float32, device=dev)
+        self._qg2 = torch.empty((M, N), dtype=torch.int8, device=dev)
+        self._sg2 = torch.empty(N, dtype=torch.float32, device=dev)
+        self._dx = torch.empty((M, K), dtype=torch.float32, device=dev)
+
+    def forward(self, x):
+        M = x.shape[0]
+        self._alloc(M, x.device)
+        self.M = M
+        self.qx, self.sx = nat.qlin_quantize_rows(x, had_block=self.had, q=self._qx[:M],
+                                                  s=self._sx[:M])
+        self._tick("quantize_x")
+        y = nat.qlin_fwd(self.qx, self.sx, self.qw, self.sw, self.bias, y=self._y[:M])
+        self._tick("fwd")
+        return y
+
+    def backward(self, dy):
+        """Returns dx in the original basis; keeps dw (and db) for the update."""
+        M = self.M
+        qg1, sg1 = nat.qlin_quantize_rows(dy, prescale=self.sw, q=self._qg1[:M], s=self._sg1[:M])
+        self._tick("quantize_dy_rows")
+        r = nat.qlin_quantize_cols(dy, prescale=self.sx, q=self._qg2[:M], s=self._sg2,
+                                   col_sum=self.db)
+        qg2, sg2 = r[0], r[1]
+        self._tick("quantize_dy_cols")
+        dx = nat.qlin_bwd_dx(qg1, sg1, self.qw, dx=self._dx[:M])
+        self._tick("bwd_dx")
+        if self.had:
+            nat.qlin_hadamard(dx, self.had, y=dx)
+            self._tick("unrotate_dx")
+        nat.qlin_bwd_dw(qg2, sg2, self.qx, dw=self.dw)
+        self._tick("bwd_dw")
+        return dx
+
+    def sgd_step(self, lr, seed, step):
+        nat.qlin_sgd_requant(self.qw, self.sw, self.dw, lr, seed, step, bias=self.bias, db=self.db)
+        self._tick("sgd_requant")
+
+    def _tick(self, label):
+        if self.timer is not None:
+            self.timer(label)
