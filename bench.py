@@ -43,9 +43,9 @@ ALG_BYTES = {
 }
 GEMMS = ("fwd", "bwd_dx", "bwd_dw")
 # Kernel symbol behind each call, as rocprofv3 names it.
-KERNEL_OF = {"fwd": "gemm_kernel<128, 128, false, false, 2>",
-             "bwd_dx": "gemm_kernel<128, 128, false, true, 1>",
-             "bwd_dw": "gemm_kernel<128, 128, true, true, 1>"}
+KERNEL_OF = {"fwd": "gemm_kernel<256, 256, 2, 4, 128, false, false, 2>",
+             "bwd_dx": "gemm_kernel<256, 256, 2, 4, 128, false, true, 1>",
+             "bwd_dw": "gemm_kernel<256, 256, 2, 4, 128, true, true, 1>"}
 
 
 def source_digest():
@@ -98,7 +98,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-tokens", type=int, default=32,
+    ap.add_argument("--cpu-tokens", type=int, default=768,
                     help="token sample of the oracle CPU baseline (0 skips it)")
     args = ap.parse_args()
     if args.gpus != 1:

@@ -14,14 +14,17 @@
  *
  * Conventions for every entry point:
  *  - All array pointers are device memory owned by the caller, row-major and
- *    contiguous, 16-byte aligned.  The library allocates nothing and keeps no
- *    mutable global state; calls on different streams are independent.
+ *    contiguous, 16-byte aligned.  A pointer to an array with no element
+ *    (for example any [M, *] array when M == 0) may be NULL.  The library
+ *    allocates nothing and keeps no mutable global state; calls on different
+ *    streams are independent.
  *  - 'stream' is a hipStream_t (NULL means the null stream).  Every call only
  *    enqueues kernels on that stream and returns without synchronizing.
  *  - Arguments are validated before anything is launched: on any error the
  *    call returns a nonzero status and no output is touched.  Faults inside
  *    kernels surface at the caller's next synchronization.
- *  - Shapes: M (tokens) >= 0 is arbitrary; M == 0 is a no-op.  N (out
+ *  - Shapes: M (tokens) >= 0 is arbitrary; M == 0 is a no-op (except that
+ *    qlin_bwd_dw then writes an all-zero dW).  N (out
  *    features) and K (in features) are multiples of 16.  A contraction longer
  *    than QLIN_MAX_CONTRACTION is rejected with QLIN_EUNSUPPORTED.
  *  - Arithmetic: IEEE binary32, round to nearest even, no fused multiply-add,

@@ -20,8 +20,11 @@ bool hadamard_block_ok(int64_t cols, int b)
     return b >= 2 && b <= QLIN_MAX_HAD_BLOCK && pow2(b) && cols % b == 0;
 }
 
-// Both optional pointers 16-byte aligned when present.
+// Optional pointers: 16-byte aligned when present.
 bool opt_aligned(const void *p) { return p == nullptr || aligned16(p); }
+
+// An array argument: non-null and 16-byte aligned unless it holds no element.
+bool array_ok(const void *p, bool nonempty) { return nonempty ? (p && aligned16(p)) : opt_aligned(p); }
 
 // Largest token count a call accepts (grid dimensions and int32 tile indices).
 constexpr int64_t kMaxRows = (int64_t)1 << 30;
@@ -56,11 +59,10 @@ int qlin_abi_version(void) { return kAbiVersion; }
 int qlin_quantize_rows(const void *x, int dtype, int64_t rows, int64_t cols,
                        const float *prescale, int had_block, int8_t *q, float *s, void *stream)
 {
-    if (!x || !q || !s || !dtype_ok(dtype))
+    if (!dtype_ok(dtype) || rows < 0 || !dim16(cols))
         return QLIN_EINVAL;
-    if (!aligned16(x) || !aligned16(q) || !opt_aligned(prescale))
-        return QLIN_EINVAL;
-    if (rows < 0 || !dim16(cols))
+    if (!array_ok(x, rows > 0) || !array_ok(q, rows > 0) || (rows > 0 && !s) ||
+        !opt_aligned(prescale))
         return QLIN_EINVAL;
     if (had_block != 0 && !hadamard_block_ok(cols, had_block))
         return QLIN_EINVAL;
@@ -77,13 +79,11 @@ int qlin_quantize_rows(const void *x, int dtype, int64_t rows, int64_t cols,
 int qlin_quantize_cols(const void *x, int dtype, int64_t rows, int64_t cols,
                        const float *prescale, int8_t *q, float *s, float *col_sum, void *stream)
 {
-    if (!x || !q || !s || !dtype_ok(dtype))
+    if (!s || !dtype_ok(dtype) || rows < 0 || !dim16(cols))
         return QLIN_EINVAL;
-    if (!aligned16(x) || !aligned16(q))
+    if (!array_ok(x, rows > 0) || !array_ok(q, rows > 0) || !opt_aligned(prescale))
         return QLIN_EINVAL;
-    if (rows < 0 || !dim16(cols))
-        return QLIN_EINVAL;
-    if (col_sum == s || (const void *)s == x || (const void *)col_sum == x)
+    if (col_sum == s || (x && ((const void *)s == x || (const void *)col_sum == x)))
         return QLIN_EINVAL;
     if (rows > 65535LL * 16)          // grid.y of the quantize pass stays below 65536
         return QLIN_EUNSUPPORTED;
@@ -95,11 +95,9 @@ int qlin_quantize_cols(const void *x, int dtype, int64_t rows, int64_t cols,
 int qlin_hadamard(const void *x, int dtype, int64_t rows, int64_t cols, int block, float *y,
                   void *stream)
 {
-    if (!x || !y || !dtype_ok(dtype))
+    if (!dtype_ok(dtype) || rows < 0 || !dim16(cols) || !hadamard_block_ok(cols, block))
         return QLIN_EINVAL;
-    if (!aligned16(x) || !aligned16(y))
-        return QLIN_EINVAL;
-    if (rows < 0 || !dim16(cols) || !hadamard_block_ok(cols, block))
+    if (!array_ok(x, rows > 0) || !array_ok(y, rows > 0))
         return QLIN_EINVAL;
     if (dtype == QLIN_BF16 && rows > 0) {
         // y may alias x only for an in-place fp32 call.
@@ -117,15 +115,19 @@ int qlin_hadamard(const void *x, int dtype, int64_t rows, int64_t cols, int bloc
     return finish();
 }
 
-// Shared checks of the three products: shapes, then the contraction bound.
+// Shared checks of the three products: shapes, pointers, then the contraction
+// bound.  'a_rows' / 'b_rows' tell whether the operands hold any element and
+// 'out_rows' whether the output does.
 static int check_product(int op, const void *a, const void *b, void *out, int64_t M, int64_t N,
                          int64_t K)
 {
-    if (!a || !b || !out)
-        return QLIN_EINVAL;
-    if (!aligned16(a) || !aligned16(b) || !aligned16(out))
-        return QLIN_EINVAL;
     if (M < 0 || !dim16(N) || !dim16(K))
+        return QLIN_EINVAL;
+    const bool has_m = M > 0;
+    // forward and dX outputs have M rows; the dW output [N, K] exists for any M.
+    const bool out_nonempty = op == QLIN_OP_DW ? true : has_m;
+    const bool b_nonempty = op == QLIN_OP_DW ? has_m : true;
+    if (!array_ok(a, has_m) || !array_ok(b, b_nonempty && has_m) || !array_ok(out, out_nonempty))
         return QLIN_EINVAL;
     const int64_t contraction = op == QLIN_OP_FWD ? K : (op == QLIN_OP_DX ? N : M);
     if (contraction > QLIN_MAX_CONTRACTION || M > kMaxRows || N > kMaxRows || K > kMaxRows)
@@ -139,10 +141,10 @@ int qlin_fwd(const int8_t *qx, const float *sx, const int8_t *qw, const float *s
     int st = check_product(QLIN_OP_FWD, qx, qw, y, M, N, K);
     if (st != QLIN_OK)
         return st;
-    if (!sx || !sw)
-        return QLIN_EINVAL;
     if (M == 0)
         return QLIN_OK;
+    if (!sx || !sw)
+        return QLIN_EINVAL;
     qlin::ProductArgs p{QLIN_OP_FWD, qx, qw, M, N, K, sx, sw, bias, y, false};
     qlin::launch_product(p, as_stream(stream));
     return finish();
@@ -154,10 +156,10 @@ int qlin_bwd_dx(const int8_t *qg1, const float *sg1, const int8_t *qw, int64_t M
     int st = check_product(QLIN_OP_DX, qg1, qw, dx, M, N, K);
     if (st != QLIN_OK)
         return st;
-    if (!sg1)
-        return QLIN_EINVAL;
     if (M == 0)
         return QLIN_OK;
+    if (!sg1)
+        return QLIN_EINVAL;
     qlin::ProductArgs p{QLIN_OP_DX, qg1, qw, M, N, K, sg1, nullptr, nullptr, dx, false};
     qlin::launch_product(p, as_stream(stream));
     return finish();
@@ -195,13 +197,11 @@ int qlin_gemm_s32(int op, const int8_t *a, const int8_t *b, int64_t M, int64_t N
 int qlin_sgd_requant(int8_t *qw, float *sw, const float *dw, int64_t N, int64_t K, float lr,
                      uint64_t seed, uint64_t step, float *bias, const float *db, void *stream)
 {
-    if (!qw || !sw || !dw)
+    if (N < 0 || !dim16(K))
         return QLIN_EINVAL;
-    if (!aligned16(qw) || !aligned16(dw))
+    if (!array_ok(qw, N > 0) || !array_ok(dw, N > 0) || (N > 0 && !sw))
         return QLIN_EINVAL;
     if ((bias == nullptr) != (db == nullptr))
-        return QLIN_EINVAL;
-    if (N < 0 || !dim16(K))
         return QLIN_EINVAL;
     if (!isfinite(lr))
         return QLIN_EINVAL;

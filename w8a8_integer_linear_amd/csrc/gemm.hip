@@ -11,15 +11,22 @@
 //   forward  A = qx  [M,K] row, B = qw [N,K] row          C = y  [M,N]
 //   dX       A = qg1 [M,N] row, B = qw [N,K] km (t = n)   C = dx [M,K]
 //   dW       A = qg2 [M,N] km,  B = qx [M,K] km (t = m)   C = dw [N,K]
-// Both operands are staged in LDS with the contraction index contiguous, so
-// the MFMA fragment reads are the same 16-byte reads for every layout; a km
-// operand is loaded as 4 contraction rows x 8 bytes per lane and transposed in
-// registers with byte permutes before it is written to LDS.
+//
+// Tiles of BM x BN outputs and 64 contraction bytes per stage are copied
+// straight from global memory into LDS by 16-byte buffer loads, in the layout
+// they have in memory (XOR-swizzled at 16-byte granularity), through a ring of
+// up to four stages so that several stages of loads are in flight while one
+// is multiplied.  Fragments for v_mfma_i32_32x32x32_i8 are read with
+// ds_read_b128 from a row operand and with two ds_read_b64_tr_b8 from a km
+// operand: in each 16-lane group the transpose read hands lane i byte i & 7
+// of the row addressed by lane 2e + (i >> 3) as its byte e, so pointing lane
+// s at contraction row k0 + (s >> 1), column c0 + 8 (s & 1) gives lane i the
+// eight contraction values of column c0 + i: the same lane -> (column, k)
+// map as a row operand's 16-byte read.
 //
 // Exactness: int32 accumulation of int8 products is exact for contractions up
 // to 131,071 and does not depend on the order of k, so the placement of k
-// inside an MFMA fragment only has to agree between A and B (it does: both
-// are read with the same lane -> k map).
+// inside a fragment only has to agree between A and B, which it does.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -27,9 +34,8 @@ namespace qlin {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBK = 64;            // contraction bytes per pipeline stage
-constexpr int kLds = kBK + 16;     // LDS row stride in bytes (padding spreads banks)
+
+typedef int i32x2v __attribute__((ext_vector_type(2)));
 
 struct GemmParams {
     const int8_t *a;
@@ -43,107 +49,161 @@ struct GemmParams {
     int tiles_i, tiles_j;
 };
 
-// 4x4 byte transpose: x_r holds bytes (c0..c3) of row r, y_c gets bytes
-// (r0..r3) of column c.  v_perm_b32 byte selectors: 0-3 pick bytes of the
-// second source, 4-7 bytes of the first.
-__device__ __forceinline__ void transpose4x4(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3,
-                                             uint32_t *y)
+// ------------------------------------------------------------------ staging
+
+// Buffer resource over a whole operand: every lane offset used below is
+// either a valid byte offset (< 2^31 - 16 by the shape limits) or kOob, which
+// the buffer range check turns into a zero fill of the lane's 16 LDS bytes.
+constexpr uint32_t kOob = 0x7FFFFFF0u;
+constexpr int kRsrcWord3 = 0x00020000;   // raw 32-bit buffer format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const int8_t *base)
 {
-    const uint32_t t0 = __builtin_amdgcn_perm(x1, x0, 0x05010400u);
-    const uint32_t t1 = __builtin_amdgcn_perm(x3, x2, 0x05010400u);
-    const uint32_t t2 = __builtin_amdgcn_perm(x1, x0, 0x07030602u);
-    const uint32_t t3 = __builtin_amdgcn_perm(x3, x2, 0x07030602u);
-    y[0] = __builtin_amdgcn_perm(t1, t0, 0x05040100u);
-    y[1] = __builtin_amdgcn_perm(t1, t0, 0x07060302u);
-    y[2] = __builtin_amdgcn_perm(t3, t2, 0x05040100u);
-    y[3] = __builtin_amdgcn_perm(t3, t2, 0x07060302u);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(base), (short)0, (int)kOob,
+                                             kRsrcWord3);
 }
 
-// Global -> register -> LDS staging of one operand tile of ROWS output rows
-// by kBK contraction bytes.
-template <int ROWS, bool KM>
-struct Stage;
+typedef __attribute__((address_space(3))) int8_t lds_i8;
 
-template <int ROWS>
-struct Stage<ROWS, false> {
-    static constexpr int N = ROWS * (kBK / 16) / kThreads;   // 16-byte chunks per lane
-    i32x4 r[N];
+// One operand tile of ROWS output rows (or columns) by kBK (64 or 128)
+// contraction bytes,
+// copied straight from global memory into LDS by buffer loads (each wave
+// instruction fills 1 KiB: lane l writes bytes 16 l .. 16 l + 15).
+//
+// Row operand: LDS [ROWS][kBK]; the 16-byte chunk holding contraction bytes
+// 16 c .. of row r sits at position c ^ ((r >> 2) & 3) for kBK = 64 and
+// c ^ ((r >> 1) & 7) for kBK = 128, so the 16 rows read together by a
+// fragment load fall on 16 distinct bank groups.
+// Km operand: LDS [kBK][ROWS]; chunk c (columns 16 c ..) of contraction row k
+// sits at position c ^ (2 (k & 7)) (for ROWS >= 256), so the 8 rows read
+// together by a transpose load (and the neighbouring chunk read by the next
+// 16 lanes) fall on distinct bank groups.
+template <int ROWS, bool KM, int NT, int kBK>
+struct Operand {
+    static constexpr int kBytes = ROWS * kBK;
+    static constexpr int kLoads = kBytes / 16 / NT;      // 16-byte loads per lane per stage
+    static_assert(kBytes % (16 * NT) == 0, "tile does not split evenly over the threads");
+    static constexpr int kRowChunks = KM ? ROWS / 16 : kBK / 16;
 
-    __device__ __forceinline__ void load(const int8_t *base, int64_t ld, int i0, int lim,
-                                         int k0, int T)
+    __device__ static __forceinline__ int swz(int row)
     {
-#pragma unroll
-        for (int p = 0; p < N; p++) {
-            const int c = threadIdx.x + p * kThreads;
-            const int row = c / (kBK / 16);
-            const int kc = c % (kBK / 16);
-            const int gi = i0 + row;
-            const int gk = k0 + kc * 16;
-            if (gi < lim && gk < T)
-                r[p] = *reinterpret_cast<const i32x4 *>(base + (int64_t)gi * ld + gk);
-            else
-                r[p] = i32x4{0, 0, 0, 0};
-        }
+        if constexpr (!KM)
+            return kBK == 64 ? (row >> 2) & 3 : (row >> 1) & 7;
+        else if constexpr (ROWS >= 256)
+            return 2 * (row & 7);
+        else
+            return row & (ROWS / 16 - 1) & 7;
     }
 
-    __device__ __forceinline__ void store(int8_t *lds) const
+    // Enqueue the loads of stage k0 into 'dst' (this thread's share).
+    __device__ static __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, int64_t ld, int i0,
+                                                 int lim, int k0, int T, bool live, int8_t *dst)
     {
+        const int lane = __lane_id();
+        const int w = threadIdx.x / kWave;
 #pragma unroll
-        for (int p = 0; p < N; p++) {
-            const int c = threadIdx.x + p * kThreads;
-            const int row = c / (kBK / 16);
-            const int kc = c % (kBK / 16);
-            *reinterpret_cast<i32x4 *>(lds + row * kLds + kc * 16) = r[p];
-        }
-    }
-};
-
-template <int ROWS>
-struct Stage<ROWS, true> {
-    // Units of 4 contraction rows x 8 output bytes; lanes of a wave take 16
-    // consecutive contraction quads of 4 different column groups, which keeps
-    // the transposed LDS writes spread over banks.
-    static constexpr int N = (kBK / 4) * (ROWS / 8) / kThreads;
-    i32x2 r[N][4];
-
-    __device__ __forceinline__ void load(const int8_t *base, int64_t ld, int i0, int lim,
-                                         int k0, int T)
-    {
-#pragma unroll
-        for (int p = 0; p < N; p++) {
-            const int u = threadIdx.x + p * kThreads;
-            const int kq = u % (kBK / 4);
-            const int ic = u / (kBK / 4);
-            const int gi = i0 + ic * 8;
-#pragma unroll
-            for (int rr = 0; rr < 4; rr++) {
-                const int gk = k0 + kq * 4 + rr;
-                if (gi < lim && gk < T)
-                    r[p][rr] = *reinterpret_cast<const i32x2 *>(base + (int64_t)gk * ld + gi);
-                else
-                    r[p][rr] = i32x2{0, 0};
+        for (int p = 0; p < kLoads; p++) {
+            const int slot = (p * (NT / kWave) + w) * kWave + lane;   // 16-byte LDS slot
+            const int row = slot / kRowChunks;
+            const int c = (slot % kRowChunks) ^ swz(row);
+            int gi, gk;
+            int64_t off;
+            if constexpr (KM) {
+                gk = k0 + row;
+                gi = i0 + 16 * c;
+                off = (int64_t)gk * ld + gi;
+            } else {
+                gi = i0 + row;
+                gk = k0 + 16 * c;
+                off = (int64_t)gi * ld + gk;
             }
+            const uint32_t voff = (live && gi < lim && gk < T) ? (uint32_t)off : kOob;
+            lds_i8 *wave_dst = (lds_i8 *)dst + (p * (NT / kWave) + w) * (kWave * 16);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)wave_dst,
+                                                     16, voff, 0, 0, 0);
         }
     }
 
-    __device__ __forceinline__ void store(int8_t *lds) const
+    // Raw registers of one MFMA fragment while its LDS reads are in flight.
+    struct Raw {
+        i32x4 v;            // row operand: one 16-byte read
+        i32x2v lo, hi;      // km operand: two transpose reads
+    };
+
+    // Start loading the MFMA fragment of the 32 rows (columns) starting at
+    // 'r0' for contraction step kk (32 bytes): lane l gets row r0 + l % 32 and
+    // contraction bytes 16 (l / 32) .. +15 of the step.  Km fragments are read
+    // by inline asm so that the compiler does not order them behind the buffer
+    // loads still filling other stages; their registers are valid only after
+    // settle().
+    __device__ static __forceinline__ void frag(const int8_t *lds, int r0, int kk, Raw &f)
     {
-#pragma unroll
-        for (int p = 0; p < N; p++) {
-            const int u = threadIdx.x + p * kThreads;
-            const int kq = u % (kBK / 4);
-            const int ic = u / (kBK / 4);
-            uint32_t y[8];
-            transpose4x4((uint32_t)r[p][0][0], (uint32_t)r[p][1][0], (uint32_t)r[p][2][0],
-                         (uint32_t)r[p][3][0], y);
-            transpose4x4((uint32_t)r[p][0][1], (uint32_t)r[p][1][1], (uint32_t)r[p][2][1],
-                         (uint32_t)r[p][3][1], y + 4);
-#pragma unroll
-            for (int e = 0; e < 8; e++)
-                *reinterpret_cast<uint32_t *>(lds + (ic * 8 + e) * kLds + kq * 4) = y[e];
+        const int lane = __lane_id();
+        if constexpr (KM) {
+            const int s = lane % 16;
+            const int krow = kk * 32 + (lane / 32) * 16 + (s >> 1);
+            const int chunk = (r0 + ((lane % 32) / 16) * 16) / 16;
+            const uint32_t base = (uint32_t)(uintptr_t)(const lds_i8 *)lds;
+            const uint32_t a0 = base + krow * ROWS + 16 * (chunk ^ swz(krow)) + 8 * (s & 1);
+            const uint32_t a1 =
+                base + (krow + 8) * ROWS + 16 * (chunk ^ swz(krow + 8)) + 8 * (s & 1);
+            asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(f.lo) : "v"(a0));
+            asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(f.hi) : "v"(a1));
+        } else {
+            const int row = r0 + lane % 32;
+            const int c = kk * 2 + lane / 32;
+            f.v = *reinterpret_cast<const i32x4 *>(lds + row * kBK + 16 * (c ^ swz(row)));
         }
     }
+
+    // After an lgkmcnt(0) wait: ties the asm-loaded registers to the wait so no
+    // use (or copy) of them is scheduled before it.
+    __device__ static __forceinline__ void settle(Raw &f)
+    {
+        if constexpr (KM) {
+            asm volatile("" : "+v"(f.lo));
+            asm volatile("" : "+v"(f.hi));
+        }
+    }
+
+    __device__ static __forceinline__ i32x4 value(const Raw &f)
+    {
+        if constexpr (KM)
+            return i32x4{f.lo[0], f.lo[1], f.hi[0], f.hi[1]};
+        else
+            return f.v;
+    }
 };
+
+// Pipeline depth: as many stages as fit in 160 KiB of LDS, at most 4.
+template <int kStageBytes>
+constexpr int kStagesFor()
+{
+    return (160 * 1024 / kStageBytes) < 4 ? (160 * 1024 / kStageBytes) : 4;
+}
+
+__device__ __forceinline__ void wait_lgkmcnt0()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are pending.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier without a memory fence: a fence would also wait for the
+// loads of later stages still in flight.  LDS writes of a stage are complete
+// once the writing lane's own vmcnt wait has passed, which every lane does
+// before arriving here; the clobber keeps the compiler from moving LDS
+// accesses across the barrier.
+__device__ __forceinline__ void barrier_no_fence()
+{
+    asm volatile("s_barrier" ::: "memory");
+}
 
 enum { EPI_RAW = 0, EPI_ROWSCALE = 1, EPI_FWD = 2 };
 
@@ -168,22 +228,50 @@ __device__ __forceinline__ void tile_of(int pid, int tiles_i, int tiles_j, int &
     tj = in / gsize;
 }
 
-template <int BM, int BN, bool AKM, bool BKM, int EPI>
-__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmParams p)
+// ------------------------------------------------------------------- kernel
+
+template <int BM, int BN, int WM, int WN, int kBK, bool AKM, bool BKM, int EPI>
+__global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
 {
-    constexpr int FM = BM / 64;    // 32x32 blocks per wave along rows (2 x 2 waves)
-    constexpr int FN = BN / 64;
-    __shared__ __attribute__((aligned(16))) int8_t smem[2][(BM + BN) * kLds];
+    constexpr int NT = WM * WN * 64;
+    constexpr int FM = BM / WM / 32;   // 32x32 blocks per wave along rows
+    constexpr int FN = BN / WN / 32;
+    constexpr int NK = kBK / 32;       // MFMA contraction steps per stage
+    using OpA = Operand<BM, AKM, NT, kBK>;
+    using OpB = Operand<BN, BKM, NT, kBK>;
+    constexpr int kStage = OpA::kBytes + OpB::kBytes;
+    constexpr int kStages = kStagesFor<kStage>();
+    constexpr int kLoads = OpA::kLoads + OpB::kLoads;     // per lane per stage
+    __shared__ __attribute__((aligned(1024))) int8_t smem[kStages * kStage];
 
     int ti, tj;
     tile_of(blockIdx.x, p.tiles_i, p.tiles_j, ti, tj);
     const int i0 = ti * BM, j0 = tj * BN;
     const int lane = __lane_id();
     const int w = threadIdx.x / kWave;
-    const int wi = w / 2, wj = w % 2;
+    const int wi = w / WN, wj = w % WN;
 
-    Stage<BM, AKM> sa;
-    Stage<BN, BKM> sb;
+    // Row operands address rows from their tile start; km operands address
+    // columns from their tile start and contraction rows from each stage.
+    const int8_t *abase = AKM ? p.a + i0 : p.a + (int64_t)i0 * p.lda;
+    const int8_t *bbase = BKM ? p.b + j0 : p.b + (int64_t)j0 * p.ldb;
+    const int alim = p.R - i0, blim = p.S - j0;
+
+    const int KT = (p.T + kBK - 1) / kBK;
+    // Stage s of the contraction goes to buffer s % kStages.  Stages past the
+    // end are issued as all-out-of-range loads (zero fills of a buffer that is
+    // never read) so every iteration waits for the same number of loads.
+    auto issue = [&](int s) {
+        const bool live = s < KT;
+        const int k0 = live ? s * kBK : 0;
+        int8_t *dst = smem + (s % kStages) * kStage;
+        const int8_t *ak = AKM ? abase + (int64_t)k0 * p.lda : abase;
+        const int8_t *bk = BKM ? bbase + (int64_t)k0 * p.ldb : bbase;
+        OpA::issue(make_rsrc(ak), p.lda, 0, alim, AKM ? 0 : k0, AKM ? p.T - k0 : p.T, live, dst);
+        OpB::issue(make_rsrc(bk), p.ldb, 0, blim, BKM ? 0 : k0, BKM ? p.T - k0 : p.T, live,
+                   dst + OpA::kBytes);
+    };
+
     i32x16 acc[FM][FN];
 #pragma unroll
     for (int a = 0; a < FM; a++)
@@ -191,94 +279,149 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmParams p)
         for (int b = 0; b < FN; b++)
             acc[a][b] = i32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 
-    const int KT = (p.T + kBK - 1) / kBK;
-    sa.load(p.a, p.lda, i0, p.R, 0, p.T);
-    sb.load(p.b, p.ldb, j0, p.S, 0, p.T);
-    sa.store(smem[0]);
-    sb.store(smem[0] + BM * kLds);
-    __syncthreads();
-
-    for (int kt = 0; kt < KT; kt++) {
-        const bool more = kt + 1 < KT;
-        if (more) {
-            sa.load(p.a, p.lda, i0, p.R, (kt + 1) * kBK, p.T);
-            sb.load(p.b, p.ldb, j0, p.S, (kt + 1) * kBK, p.T);
-        }
-        const int8_t *la = smem[kt & 1];
-        const int8_t *lb = la + BM * kLds;
+    // Two fragment sets: the LDS reads of one are in flight while the MFMAs
+    // of the other run.  f0 holds contraction step 0 of a stage, f1 step 1.
+    typename OpA::Raw fa0[FM], fa1[FM];
+    typename OpB::Raw fb0[FN], fb1[FN];
+    auto load = [&](const int8_t *stage, int kk, typename OpA::Raw *fa, typename OpB::Raw *fb) {
+        const int8_t *lb = stage + OpA::kBytes;
 #pragma unroll
-        for (int kk = 0; kk < kBK / 32; kk++) {
-            i32x4 af[FM], bf[FN];
-            const int koff = kk * 32 + (lane / 32) * 16;
+        for (int a = 0; a < FM; a++)
+            OpA::frag(stage, wi * (BM / WM) + a * 32, kk, fa[a]);
 #pragma unroll
-            for (int a = 0; a < FM; a++)
-                af[a] = *reinterpret_cast<const i32x4 *>(
-                    la + (wi * (BM / 2) + a * 32 + lane % 32) * kLds + koff);
+        for (int b = 0; b < FN; b++)
+            OpB::frag(lb, wj * (BN / WN) + b * 32, kk, fb[b]);
+    };
+    auto settle = [&](typename OpA::Raw *fa, typename OpB::Raw *fb) {
+        wait_lgkmcnt0();
+#pragma unroll
+        for (int a = 0; a < FM; a++)
+            OpA::settle(fa[a]);
+#pragma unroll
+        for (int b = 0; b < FN; b++)
+            OpB::settle(fb[b]);
+    };
+    auto mma = [&](const typename OpA::Raw *fa, const typename OpB::Raw *fb) {
+        i32x4 av[FM], bv[FN];
+#pragma unroll
+        for (int a = 0; a < FM; a++)
+            av[a] = OpA::value(fa[a]);
+#pragma unroll
+        for (int b = 0; b < FN; b++)
+            bv[b] = OpB::value(fb[b]);
+#pragma unroll
+        for (int a = 0; a < FM; a++)
 #pragma unroll
             for (int b = 0; b < FN; b++)
-                bf[b] = *reinterpret_cast<const i32x4 *>(
-                    lb + (wj * (BN / 2) + b * 32 + lane % 32) * kLds + koff);
-#pragma unroll
-            for (int a = 0; a < FM; a++)
-#pragma unroll
-                for (int b = 0; b < FN; b++)
-                    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[a], bf[b], acc[a][b], 0,
-                                                                      0, 0);
-        }
-        if (more) {
-            sa.store(smem[(kt + 1) & 1]);
-            sb.store(smem[(kt + 1) & 1] + BM * kLds);
-        }
-        __syncthreads();
-    }
+                acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bv[b], av[a], acc[a][b], 0, 0, 0);
+    };
 
-    // Epilogue.  32x32 accumulator layout: lane l, register r holds column
-    // l % 32 and row 8 * (r / 4) + 4 * (l / 32) + r % 4 of the block.
+    // Stage s lives in buffer s % kStages and is issued at the top of stage
+    // s - kStages + 1, into the buffer that the barrier closing the previous
+    // stage has freed (every wave had read that stage into registers).  The
+    // fragment sets alternate: the reads of step kk + 1 are in flight while
+    // the MFMAs of step kk run; the first step of the next stage is read right
+    // after the barrier that ends this one.  sched_barrier(0) pins this order
+    // and sched_group_barrier spreads the stage's buffer loads over the MFMAs
+    // of the first step.
+    typename OpA::Raw fa[2][FM];
+    typename OpB::Raw fb[2][FN];
+#pragma unroll
+    for (int s = 0; s < kStages - 1; s++)
+        issue(s);
+    wait_vmcnt<(kStages - 2) * kLoads>();
+    barrier_no_fence();
+    load(smem, 0, fa[0], fb[0]);
+
+    for (int kt = 0; kt < KT; kt++) {
+        const int8_t *cur = smem + (kt % kStages) * kStage;
+#pragma unroll
+        for (int kk = 0; kk + 1 < NK; kk++) {
+            settle(fa[kk & 1], fb[kk & 1]);
+            load(cur, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+            if (kk == 0)
+                issue(kt + kStages - 1);
+            mma(fa[kk & 1], fb[kk & 1]);
+            if (kk == 0) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * (FM + FN), 0);
+#pragma unroll
+                for (int g = 0; g < kLoads; g++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, (FM * FN + kLoads - 1) / kLoads, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // Stage kt + 1 has landed once at most the loads of stages kt + 2 ..
+        // kt + kStages - 1 are outstanding.
+        wait_vmcnt<(kStages - 2) * kLoads>();
+        settle(fa[(NK - 1) & 1], fb[(NK - 1) & 1]);
+        barrier_no_fence();
+        if (kt + 1 < KT)
+            load(smem + ((kt + 1) % kStages) * kStage, 0, fa[0], fb[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(fa[(NK - 1) & 1], fb[(NK - 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vmcnt<0>();
+
+    // Epilogue.  The MFMA ran with B as its first operand, so each 32x32
+    // block holds C transposed: lane l has output row l % 32 and, in register
+    // 4 g + e, output column 8 g + 4 (l / 32) + e.  Every lane therefore
+    // writes 16-byte runs of four columns of its row.
 #pragma unroll
     for (int a = 0; a < FM; a++) {
+        const int i = i0 + wi * (BM / WM) + a * 32 + lane % 32;
+        if (i >= p.R)
+            continue;
+        float rs = 0.0f;
+        if constexpr (EPI != EPI_RAW)
+            rs = p.srow[i];
 #pragma unroll
         for (int b = 0; b < FN; b++) {
-            const int j = j0 + wj * (BN / 2) + b * 32 + lane % 32;
-            if (j >= p.S)
-                continue;
-            float cs = 0.0f, bj = 0.0f;
-            if constexpr (EPI == EPI_FWD) {
-                cs = p.scol[j];
-                if (p.bias)
-                    bj = p.bias[j];
-            }
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int i = i0 + wi * (BM / 2) + a * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
-                if (i >= p.R)
+            for (int g = 0; g < 4; g++) {
+                const int j = j0 + wj * (BN / WN) + b * 32 + 8 * g + 4 * (lane / 32);
+                if (j >= p.S)
                     continue;
                 const int64_t off = (int64_t)i * p.ldc + j;
-                const int v = acc[a][b][r];
+                const i32x16 &c = acc[a][b];
                 if constexpr (EPI == EPI_RAW) {
-                    static_cast<int32_t *>(p.out)[off] = v;
+                    *reinterpret_cast<i32x4 *>(static_cast<int32_t *>(p.out) + off) =
+                        i32x4{c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]};
                 } else {
-                    float f = (float)v * p.srow[i];
+                    f32x4 v;
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        v[e] = (float)c[4 * g + e] * rs;
                     if constexpr (EPI == EPI_FWD) {
-                        f = f * cs;
-                        if (p.bias)
-                            f = f + bj;
+                        const f32x4 cs = *reinterpret_cast<const f32x4 *>(p.scol + j);
+#pragma unroll
+                        for (int e = 0; e < 4; e++)
+                            v[e] = v[e] * cs[e];
+                        if (p.bias) {
+                            const f32x4 bj = *reinterpret_cast<const f32x4 *>(p.bias + j);
+#pragma unroll
+                            for (int e = 0; e < 4; e++)
+                                v[e] = v[e] + bj[e];
+                        }
                     }
-                    static_cast<float *>(p.out)[off] = f;
+                    *reinterpret_cast<f32x4 *>(static_cast<float *>(p.out) + off) = v;
                 }
             }
         }
     }
 }
 
-template <int BM, int BN, bool AKM, bool BKM, int EPI>
+template <int BM, int BN, int WM, int WN, int BK, bool AKM, bool BKM, int EPI>
 void run_gemm(const GemmParams &p0, hipStream_t st)
 {
     GemmParams p = p0;
     p.tiles_i = (p.R + BM - 1) / BM;
     p.tiles_j = (p.S + BN - 1) / BN;
     const unsigned grid = (unsigned)(p.tiles_i * p.tiles_j);
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, AKM, BKM, EPI>), dim3(grid), dim3(kThreads), 0, st,
-                       p);
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, AKM, BKM, EPI>), dim3(grid),
+                       dim3(WM * WN * 64), 0, st, p);
 }
 
 // Forward product for M <= 16 (decode-like shapes): the weight is streamed
@@ -348,6 +491,15 @@ __global__ __launch_bounds__(256) void skinny_fwd_kernel(const int8_t *__restric
     }
 }
 
+// Tile configuration of the three products: 256 x 256 outputs per
+// workgroup, 8 waves each owning 128 x 64, 128 contraction bytes per stage
+// (two stages in flight in 128 KiB of LDS).
+template <bool AKM, bool BKM, int EPI>
+void run_cfg(const GemmParams &p, hipStream_t st)
+{
+    run_gemm<256, 256, 2, 4, 128, AKM, BKM, EPI>(p, st);
+}
+
 } // namespace
 
 void launch_product(const ProductArgs &a, hipStream_t st)
@@ -374,25 +526,25 @@ void launch_product(const ProductArgs &a, hipStream_t st)
         p.b = a.b; p.ldb = a.K;
         p.R = (int)a.M; p.S = (int)a.N; p.T = (int)a.K; p.ldc = a.N;
         if (a.raw)
-            run_gemm<128, 128, false, false, EPI_RAW>(p, st);
+            run_cfg<false, false, EPI_RAW>(p, st);
         else
-            run_gemm<128, 128, false, false, EPI_FWD>(p, st);
+            run_cfg<false, false, EPI_FWD>(p, st);
     } else if (a.op == 1) {
         p.a = a.a; p.lda = a.N;
         p.b = a.b; p.ldb = a.K;
         p.R = (int)a.M; p.S = (int)a.K; p.T = (int)a.N; p.ldc = a.K;
         if (a.raw)
-            run_gemm<128, 128, false, true, EPI_RAW>(p, st);
+            run_cfg<false, true, EPI_RAW>(p, st);
         else
-            run_gemm<128, 128, false, true, EPI_ROWSCALE>(p, st);
+            run_cfg<false, true, EPI_ROWSCALE>(p, st);
     } else {
         p.a = a.a; p.lda = a.N;
         p.b = a.b; p.ldb = a.K;
         p.R = (int)a.N; p.S = (int)a.K; p.T = (int)a.M; p.ldc = a.K;
         if (a.raw)
-            run_gemm<128, 128, true, true, EPI_RAW>(p, st);
+            run_cfg<true, true, EPI_RAW>(p, st);
         else
-            run_gemm<128, 128, true, true, EPI_ROWSCALE>(p, st);
+            run_cfg<true, true, EPI_ROWSCALE>(p, st);
     }
 }
 
