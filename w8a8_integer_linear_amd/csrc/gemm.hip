@@ -175,11 +175,12 @@ struct Operand {
     }
 };
 
-// Pipeline depth: as many stages as fit in 160 KiB of LDS, at most 4.
-template <int kStageBytes>
+// Pipeline depth: as many stages as fit in this workgroup's share of the
+// 160 KiB of LDS (OCC workgroups per CU), at most 4.
+template <int kStageBytes, int OCC>
 constexpr int kStagesFor()
 {
-    return (160 * 1024 / kStageBytes) < 4 ? (160 * 1024 / kStageBytes) : 4;
+    return (160 * 1024 / OCC / kStageBytes) < 4 ? (160 * 1024 / OCC / kStageBytes) : 4;
 }
 
 __device__ __forceinline__ void wait_lgkmcnt0()
@@ -230,8 +231,8 @@ __device__ __forceinline__ void tile_of(int pid, int tiles_i, int tiles_j, int &
 
 // ------------------------------------------------------------------- kernel
 
-template <int BM, int BN, int WM, int WN, int kBK, bool AKM, bool BKM, int EPI>
-__global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
+template <int BM, int BN, int WM, int WN, int kBK, int OCC, bool AKM, bool BKM, int EPI>
+__global__ __launch_bounds__(WM *WN * 64, OCC) void gemm_kernel(GemmParams p)
 {
     constexpr int NT = WM * WN * 64;
     constexpr int FM = BM / WM / 32;   // 32x32 blocks per wave along rows
@@ -240,7 +241,8 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
     using OpA = Operand<BM, AKM, NT, kBK>;
     using OpB = Operand<BN, BKM, NT, kBK>;
     constexpr int kStage = OpA::kBytes + OpB::kBytes;
-    constexpr int kStages = kStagesFor<kStage>();
+    constexpr int kStages = kStagesFor<kStage, OCC>();
+    static_assert(kStages >= 2, "tile too large for the LDS share");
     constexpr int kLoads = OpA::kLoads + OpB::kLoads;     // per lane per stage
     __shared__ __attribute__((aligned(1024))) int8_t smem[kStages * kStage];
 
@@ -413,14 +415,14 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
     }
 }
 
-template <int BM, int BN, int WM, int WN, int BK, bool AKM, bool BKM, int EPI>
+template <int BM, int BN, int WM, int WN, int BK, int OCC, bool AKM, bool BKM, int EPI>
 void run_gemm(const GemmParams &p0, hipStream_t st)
 {
     GemmParams p = p0;
     p.tiles_i = (p.R + BM - 1) / BM;
     p.tiles_j = (p.S + BN - 1) / BN;
     const unsigned grid = (unsigned)(p.tiles_i * p.tiles_j);
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, AKM, BKM, EPI>), dim3(grid),
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, OCC, AKM, BKM, EPI>), dim3(grid),
                        dim3(WM * WN * 64), 0, st, p);
 }
 
@@ -497,7 +499,7 @@ __global__ __launch_bounds__(256) void skinny_fwd_kernel(const int8_t *__restric
 template <bool AKM, bool BKM, int EPI>
 void run_cfg(const GemmParams &p, hipStream_t st)
 {
-    run_gemm<256, 256, 2, 4, 128, AKM, BKM, EPI>(p, st);
+    run_gemm<256, 256, 2, 4, 128, 1, AKM, BKM, EPI>(p, st);
 }
 
 } // namespace

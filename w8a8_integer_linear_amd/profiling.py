@@ -1,0 +1,121 @@
+"""Turn rocprofv3 CSV output of bench.py runs into short text summaries.
+
+Usage (from the repository root, after the three profiler runs listed in
+the design doc have written their CSVs under OUT_DIR):
+
+    python -m w8a8_integer_linear_amd.profiling OUT_DIR
+
+Reads  OUT_DIR/kt/*kernel_stats.csv      (rocprofv3 --kernel-trace --stats)
+       OUT_DIR/fetch/*counter_collection.csv (rocprofv3 --pmc FETCH_SIZE)
+       OUT_DIR/write/*counter_collection.csv (rocprofv3 --pmc WRITE_SIZE)
+Writes profiles/kernels_headline_step.txt (per-kernel durations) and
+       profiles/pmc_traffic.json + profiles/pmc_traffic.txt (HBM bytes per
+       launch, scaled by the reading of the calibration copy of 512 MiB).
+"""
+import csv
+import glob
+import json
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PROFILES = os.path.join(ROOT, "profiles")
+COPY_BYTES = 512 << 20
+
+
+def _one(pattern):
+    hits = sorted(glob.glob(pattern))
+    if not hits:
+        raise FileNotFoundError(pattern)
+    return hits[0]
+
+
+def _short(name):
+    name = name.replace("qlin::(anonymous namespace)::", "").replace("qlin::", "")
+    return name.split("(")[0] if "gemm_kernel" not in name else name.split(")")[0] + ")"
+
+
+def kernel_stats(out_dir):
+    path = _one(os.path.join(out_dir, "kt", "*kernel_stats.csv"))
+    rows = list(csv.DictReader(open(path)))
+    res = []
+    for r in rows:
+        res.append({"kernel": _short(r["Name"]), "calls": int(r["Calls"]),
+                    "total_ns": float(r["TotalDurationNs"]),
+                    "avg_ns": float(r["AverageNs"]), "pct": float(r["Percentage"])})
+    return res
+
+
+def dispatches(out_dir, sub, name):
+    """{dispatch id: (short kernel name, counter value in KiB)}."""
+    path = _one(os.path.join(out_dir, sub, "*counter_collection.csv"))
+    out = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == name:
+            out[int(r["Dispatch_Id"])] = (_short(r["Kernel_Name"]), float(r["Counter_Value"]))
+    return out
+
+
+def main(out_dir, digest=None):
+    os.makedirs(PROFILES, exist_ok=True)
+    stats = kernel_stats(out_dir)
+    with open(os.path.join(PROFILES, "kernels_headline_step.txt"), "w") as f:
+        f.write("# rocprofv3 --kernel-trace --stats of the headline training step\n")
+        f.write("# (12000 tokens, 5376 -> 7168, Hadamard block 128).  Command:\n")
+        f.write("#   rocprofv3 --kernel-trace --stats -d OUT/kt -o kt --output-format csv -- "
+                "python bench.py --steps 5 --warmup 2 --cpu-tokens 0\n")
+        f.write(f"# {'kernel':<70} {'calls':>5} {'avg_us':>9} {'pct':>6}\n")
+        for s in sorted(stats, key=lambda r: -r["total_ns"]):
+            f.write(f"  {s['kernel'][:70]:<70} {s['calls']:>5} {s['avg_ns'] / 1e3:>9.2f} "
+                    f"{s['pct']:>6.2f}\n")
+    fetch = dispatches(out_dir, "fetch", "FETCH_SIZE")
+    write = dispatches(out_dir, "write", "WRITE_SIZE")
+    # The calibration copies are the 'copy' dispatches that wrote COPY_BYTES
+    # (both runs execute the same dispatch sequence, so ids line up).
+    target = COPY_BYTES / 1024
+    cal = [d for d, (n, v) in write.items()
+           if "copy" in n.lower() and abs(v - target) < 0.01 * target and d in fetch]
+    if not cal:
+        raise RuntimeError("calibration copy not found in the counter output")
+    f_fac = COPY_BYTES / (statistics.median(fetch[d][1] for d in cal) * 1024)
+    w_fac = COPY_BYTES / (statistics.median(write[d][1] for d in cal) * 1024)
+    per = {}
+    for d, (n, fv) in fetch.items():
+        if d in cal or d not in write or write[d][0] != n:
+            continue
+        per.setdefault(n, []).append((fv * 1024 * f_fac, write[d][1] * 1024 * w_fac))
+    kernels = {}
+    for n, vals in per.items():
+        fb = statistics.median(v[0] for v in vals)
+        wb = statistics.median(v[1] for v in vals)
+        kernels[n] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
+                      "bytes_per_launch": round(fb + wb), "launches": len(vals)}
+    if digest is None:
+        sys.path.insert(0, ROOT)
+        import bench
+        digest = bench.source_digest()
+    rec = {"source_digest": digest, "calibration_dispatches": cal, "fetch_scale": f_fac,
+           "write_scale": w_fac, "kernels": kernels,
+           "commands": ["rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o fetch --output-format csv -- "
+                        "python bench.py --steps 2 --warmup 1 --cpu-tokens 0 --copy-calibration",
+                        "rocprofv3 --pmc WRITE_SIZE -d OUT/write -o write --output-format csv -- "
+                        "python bench.py --steps 2 --warmup 1 --cpu-tokens 0 --copy-calibration"]}
+    with open(os.path.join(PROFILES, "pmc_traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    with open(os.path.join(PROFILES, "pmc_traffic.txt"), "w") as f:
+        f.write("# HBM bytes per launch from FETCH_SIZE / WRITE_SIZE, scaled so that a plain copy\n")
+        f.write(f"# of {COPY_BYTES >> 20} MiB reads and writes exactly that much "
+                f"(fetch x{f_fac:.3f}, write x{w_fac:.3f}).\n")
+        for c in rec["commands"]:
+            f.write(f"#   {c}\n")
+        f.write(f"# {'kernel':<70} {'fetch_MB':>9} {'write_MB':>9} {'total_MB':>9}\n")
+        for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["bytes_per_launch"]):
+            f.write(f"  {k[:70]:<70} {v['fetch_bytes'] / 1e6:>9.1f} {v['write_bytes'] / 1e6:>9.1f} "
+                    f"{v['bytes_per_launch'] / 1e6:>9.1f}\n")
+    print(open(os.path.join(PROFILES, "kernels_headline_step.txt")).read())
+    print(open(os.path.join(PROFILES, "pmc_traffic.txt")).read())
+
+
+if __name__ == "__main__":
+    main(sys.argv[1])
