@@ -140,16 +140,20 @@ int qlin_fwd(const int8_t *qx, const float *sx, const int8_t *qw, const float *s
              const float *bias, int64_t M, int64_t N, int64_t K, float *y, void *stream);
 
 /*
- * Input-gradient product in the rotated basis (straight-through estimator
- * across the activation quantizer).
+ * Input-gradient product (straight-through estimator across the activation
+ * quantizer), optionally rotated back to the original basis.
  *   qg1 [M,N] int8, sg1 [M]: dY * sw[None, :] quantized per row
- *   (qlin_quantize_rows with prescale = sw); qw [N,K] int8.
- *   dx [M,K] fp32: dx = fl(fl32(acc) * sg1[m]), acc = sum_n qg1[m,n] * qw[n,k].
- * N <= QLIN_MAX_CONTRACTION.  Rotate dx back with qlin_hadamard when the
- * layer uses a rotation.
+ *   (qlin_quantize_rows with prescale = sw); qw [N,K] int8 (rotated basis).
+ *   dx [M,K] fp32: dx_r = fl(fl32(acc) * sg1[m]), acc = sum_n qg1[m,n] * qw[n,k];
+ *   had_block = 0 stores dx_r; otherwise (a power of two in [2, 512]
+ *   dividing K) each row of dx_r is rotated in blocks of had_block exactly
+ *   as qlin_hadamard would (the rotation is its own inverse, OneTrainer PR
+ *   #1681 commit note 2), fused into the product's epilogue for blocks up to
+ *   128 and as a second kernel for larger blocks.
+ * N <= QLIN_MAX_CONTRACTION.
  */
 int qlin_bwd_dx(const int8_t *qg1, const float *sg1, const int8_t *qw, int64_t M,
-                int64_t N, int64_t K, float *dx, void *stream);
+                int64_t N, int64_t K, int had_block, float *dx, void *stream);
 
 /*
  * Weight-gradient product on the saved INT8 input (mini_trainer guide:

@@ -84,7 +84,7 @@ def test_product_validation(L):
     # forward: K beyond the int32-exact contraction bound
     assert L.qlin_fwd(P, Q, R, S, None, 4, 16, 131072, P, None) == 2
     # dX: N (its contraction) beyond the bound
-    assert L.qlin_bwd_dx(P, Q, R, 4, 131072, 16, S, None) == 2
+    assert L.qlin_bwd_dx(P, Q, R, 4, 131072, 16, 0, S, None) == 2
     # dW: M (its contraction) beyond the bound
     assert L.qlin_bwd_dw(P, Q, R, 131072, 16, 16, S, None) == 2
     assert L.qlin_fwd(P, Q, R, S, None, 4, 24, 16, P, None) == 1     # N % 16
@@ -92,7 +92,9 @@ def test_product_validation(L):
     assert L.qlin_fwd(P, None, R, S, None, 4, 16, 16, P, None) == 1  # null sx
     assert L.qlin_fwd(P, Q, R, S, None, -1, 16, 16, P, None) == 1    # negative M
     assert L.qlin_fwd(P, Q, R, S, None, 0, 16, 16, P, None) == 0     # M = 0: no-op
-    assert L.qlin_bwd_dx(P, Q, R, 0, 16, 16, S, None) == 0
+    assert L.qlin_bwd_dx(P, Q, R, 0, 16, 16, 0, S, None) == 0
+    assert L.qlin_bwd_dx(P, Q, R, 4, 16, 96, 64, S, None) == 1     # block does not divide K
+    assert L.qlin_bwd_dx(P, Q, R, 4, 16, 96, 3, S, None) == 1      # not a power of two
     assert L.qlin_gemm_s32(7, P, Q, 4, 16, 16, R, None) == 1          # unknown product
     assert L.qlin_gemm_s32(0, ODD, Q, 4, 16, 16, R, None) == 1        # misaligned
 

@@ -199,6 +199,21 @@ def test_skinny_forward(T, Q, orc, M):
     assert_bitwise(host(y2), orc.fwd(qx, sx, qw, sw, bias), "y+bias")
 
 
+@pytest.mark.parametrize("M,N,K,had", [(64, 128, 256, 128), (130, 272, 384, 128), (17, 48, 512, 64),
+                                       (33, 64, 256, 2), (40, 32, 64, 16), (5, 16, 1024, 256),
+                                       (3, 16, 512, 512), (257, 144, 5376, 128)])
+def test_bwd_dx_rotated_back(T, Q, orc, M, N, K, had):
+    """dX rotated back in the product's epilogue (blocks <= 128) or by a second
+    kernel (larger blocks) equals the oracle's dX followed by its rotation."""
+    rng = np.random.default_rng(M * 3 + had)
+    qg, qw = _codes(rng, (M, N)), _codes(rng, (N, K))
+    sg1 = rng.uniform(1e-6, 1e-4, M).astype(np.float32)
+    announce("bwd_dx rotated", M, N, K, had)
+    dx = Q.qlin_bwd_dx(dev(qg), dev(sg1), dev(qw), had_block=had)
+    T.cuda.synchronize()
+    assert_bitwise(host(dx), orc.hadamard(orc.bwd_dx(qg, sg1, qw), had), "dx")
+
+
 def test_dw_empty_tokens(T, Q, orc):
     N, K = 32, 48
     announce("bwd_dw M=0")

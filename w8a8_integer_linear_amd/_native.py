@@ -28,7 +28,7 @@ SIGNATURES = {
     "qlin_quantize_cols": ([_vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp], _i32),
     "qlin_hadamard": ([_vp, _i32, _i64, _i64, _i32, _vp, _vp], _i32),
     "qlin_fwd": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp], _i32),
-    "qlin_bwd_dx": ([_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp], _i32),
+    "qlin_bwd_dx": ([_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp], _i32),
     "qlin_bwd_dw": ([_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp], _i32),
     "qlin_sgd_requant": ([_vp, _vp, _vp, _i64, _i64, _f32, _u64, _u64, _vp, _vp, _vp], _i32),
     "qlin_gemm_s32": ([_i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp], _i32),
@@ -160,7 +160,7 @@ def qlin_fwd(qx, sx, qw, sw, bias=None, y=None, stream=None):
     return y
 
 
-def qlin_bwd_dx(qg1, sg1, qw, dx=None, stream=None):
+def qlin_bwd_dx(qg1, sg1, qw, had_block=0, dx=None, stream=None):
     M, N = qg1.shape
     K = qw.shape[1]
     _need(qg1, "qg1", torch.int8)
@@ -168,8 +168,8 @@ def qlin_bwd_dx(qg1, sg1, qw, dx=None, stream=None):
     _need(sg1, "sg1", torch.float32, (M,))
     dx = _empty((M, K), torch.float32, qg1) if dx is None else _need(dx, "dx", torch.float32,
                                                                      (M, K))
-    _check("qlin_bwd_dx", lib().qlin_bwd_dx(_ptr(qg1), _ptr(sg1), _ptr(qw), M, N, K, _ptr(dx),
-                                            _stream(stream)))
+    _check("qlin_bwd_dx", lib().qlin_bwd_dx(_ptr(qg1), _ptr(sg1), _ptr(qw), M, N, K,
+                                            int(had_block), _ptr(dx), _stream(stream)))
     return dx
 
 

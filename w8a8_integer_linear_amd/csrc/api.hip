@@ -151,17 +151,28 @@ int qlin_fwd(const int8_t *qx, const float *sx, const int8_t *qw, const float *s
 }
 
 int qlin_bwd_dx(const int8_t *qg1, const float *sg1, const int8_t *qw, int64_t M, int64_t N,
-                int64_t K, float *dx, void *stream)
+                int64_t K, int had_block, float *dx, void *stream)
 {
     int st = check_product(QLIN_OP_DX, qg1, qw, dx, M, N, K);
     if (st != QLIN_OK)
         return st;
+    if (had_block != 0 && !hadamard_block_ok(K, had_block))
+        return QLIN_EINVAL;
     if (M == 0)
         return QLIN_OK;
     if (!sg1)
         return QLIN_EINVAL;
     qlin::ProductArgs p{QLIN_OP_DX, qg1, qw, M, N, K, sg1, nullptr, nullptr, dx, false};
-    qlin::launch_product(p, as_stream(stream));
+    const hipStream_t s = as_stream(stream);
+    if (had_block >= 2 && had_block <= 128) {
+        p.had = had_block;
+        p.had_scale = hadamard_scale(had_block);
+        qlin::launch_product(p, s);
+    } else {
+        qlin::launch_product(p, s);
+        if (had_block)
+            qlin::launch_hadamard(dx, false, M, K, had_block, hadamard_scale(had_block), dx, s);
+    }
     return finish();
 }
 

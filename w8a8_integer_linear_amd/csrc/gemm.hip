@@ -47,6 +47,8 @@ struct GemmParams {
     const float *bias;
     void *out;
     int tiles_i, tiles_j;
+    int had;          // EPI_ROWSCALE_HAD: rotation block (2 .. 128, power of two)
+    float had_scale;  // fl32(1 / sqrt(had))
 };
 
 // ------------------------------------------------------------------ staging
@@ -206,7 +208,11 @@ __device__ __forceinline__ void barrier_no_fence()
     asm volatile("s_barrier" ::: "memory");
 }
 
-enum { EPI_RAW = 0, EPI_ROWSCALE = 1, EPI_FWD = 2 };
+// Epilogues: raw int32; dequant by the output row's scale; forward dequant by
+// row and column scales plus bias; row-scale dequant followed by the block
+// Hadamard rotation of each output row (blocks of up to 128 columns, which
+// needs a wave tile 128 columns wide).
+enum { EPI_RAW = 0, EPI_ROWSCALE = 1, EPI_FWD = 2, EPI_ROWSCALE_HAD = 3 };
 
 // Tile order: workgroups are dispatched round-robin over the 8 XCDs, so
 // consecutive ids are first regrouped per XCD (each XCD gets a contiguous
@@ -371,6 +377,103 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void gemm_kernel(GemmParams p)
     // block holds C transposed: lane l has output row l % 32 and, in register
     // 4 g + e, output column 8 g + 4 (l / 32) + e.  Every lane therefore
     // writes 16-byte runs of four columns of its row.
+    if constexpr (EPI == EPI_ROWSCALE_HAD) {
+        static_assert(FN == 4, "the rotating epilogue needs 128-column wave tiles");
+        // Within the wave's 128 columns, column c = 32 b + 8 g + 4 h + e with
+        // h = lane / 32: butterfly strides 1 and 2 pair registers e, stride 4
+        // pairs lane l with lane l ^ 32, strides 8 and 16 pair registers g and
+        // strides 32 and 64 pair blocks b.  Stages run in ascending stride,
+        // the lower element becoming lo + hi and the upper lo - hi, then every
+        // element is scaled once: the same operations, in the same order, as
+        // the separate rotation of the dequantized row.
+        const bool upper = lane >= 32;
+#pragma unroll
+        for (int a = 0; a < FM; a++) {
+            const int i = i0 + wi * (BM / WM) + a * 32 + lane % 32;
+            if (i >= p.R)
+                continue;   // lanes l and l ^ 32 share the row, so both skip
+            const float rs = p.srow[i];
+            float v[FN][16];
+#pragma unroll
+            for (int b = 0; b < FN; b++)
+#pragma unroll
+                for (int r = 0; r < 16; r++)
+                    v[b][r] = (float)acc[a][b][r] * rs;
+            auto pair = [](float &lo, float &hi) {
+                const float x = lo, y = hi;
+                lo = x + y;
+                hi = x - y;
+            };
+            if (p.had > 1)
+#pragma unroll
+                for (int b = 0; b < FN; b++)
+#pragma unroll
+                    for (int g = 0; g < 4; g++) {
+                        pair(v[b][4 * g], v[b][4 * g + 1]);
+                        pair(v[b][4 * g + 2], v[b][4 * g + 3]);
+                    }
+            if (p.had > 2)
+#pragma unroll
+                for (int b = 0; b < FN; b++)
+#pragma unroll
+                    for (int g = 0; g < 4; g++) {
+                        pair(v[b][4 * g], v[b][4 * g + 2]);
+                        pair(v[b][4 * g + 1], v[b][4 * g + 3]);
+                    }
+            if (p.had > 4)
+#pragma unroll
+                for (int b = 0; b < FN; b++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) {
+                        const float o = __shfl_xor(v[b][r], 32);
+                        v[b][r] = upper ? o - v[b][r] : v[b][r] + o;
+                    }
+            if (p.had > 8)
+#pragma unroll
+                for (int b = 0; b < FN; b++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        pair(v[b][e], v[b][4 + e]);
+                        pair(v[b][8 + e], v[b][12 + e]);
+                    }
+            if (p.had > 16)
+#pragma unroll
+                for (int b = 0; b < FN; b++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        pair(v[b][e], v[b][8 + e]);
+                        pair(v[b][4 + e], v[b][12 + e]);
+                    }
+            if (p.had > 32)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    pair(v[0][r], v[1][r]);
+                    pair(v[2][r], v[3][r]);
+                }
+            if (p.had > 64)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    pair(v[0][r], v[2][r]);
+                    pair(v[1][r], v[3][r]);
+                }
+#pragma unroll
+            for (int b = 0; b < FN; b++) {
+#pragma unroll
+                for (int g = 0; g < 4; g++) {
+                    const int j = j0 + wj * (BN / WN) + b * 32 + 8 * g + 4 * (lane / 32);
+                    if (j >= p.S)
+                        continue;
+                    f32x4 o;
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        o[e] = v[b][4 * g + e] * p.had_scale;
+                    *reinterpret_cast<f32x4 *>(static_cast<float *>(p.out) + (int64_t)i * p.ldc +
+                                               j) = o;
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int a = 0; a < FM; a++) {
         const int i = i0 + wi * (BM / WM) + a * 32 + lane % 32;
@@ -535,10 +638,16 @@ void launch_product(const ProductArgs &a, hipStream_t st)
         p.a = a.a; p.lda = a.N;
         p.b = a.b; p.ldb = a.K;
         p.R = (int)a.M; p.S = (int)a.K; p.T = (int)a.N; p.ldc = a.K;
-        if (a.raw)
+        if (a.raw) {
             run_cfg<false, true, EPI_RAW>(p, st);
-        else
+        } else if (a.had >= 2 && a.had <= 128) {
+            // dX with the un-rotation in the epilogue: 64 x 128 wave tiles.
+            p.had = a.had;
+            p.had_scale = a.had_scale;
+            run_gemm<256, 256, 4, 2, 128, 1, false, true, EPI_ROWSCALE_HAD>(p, st);
+        } else {
             run_cfg<false, true, EPI_ROWSCALE>(p, st);
+        }
     } else {
         p.a = a.a; p.lda = a.N;
         p.b = a.b; p.ldb = a.K;

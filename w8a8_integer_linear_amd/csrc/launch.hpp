@@ -29,6 +29,8 @@ struct ProductArgs {
     const float *bias;  // forward only, may be null
     void *out;          // float* or int32_t*
     bool raw;           // int32 accumulators instead of dequantized floats
+    int had = 0;        // dX only: rotate each output row in blocks of 'had' (<= 128)
+    float had_scale = 1.0f;
 };
 
 void launch_product(const ProductArgs &p, hipStream_t st);

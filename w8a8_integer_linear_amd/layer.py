@@ -11,8 +11,7 @@ Step order of one training step:
             qlin_fwd(qx, sx, qw, sw, bias)         -> y
   backward  qlin_quantize_rows(dY, prescale=sw)    -> qg1, sg1
             qlin_quantize_cols(dY, prescale=sx)    -> qg2, sg2 (+ db)
-            qlin_bwd_dx(qg1, sg1, qw)              -> dx (rotated basis)
-            qlin_hadamard(dx, in place)            -> dx
+            qlin_bwd_dx(qg1, sg1, qw, rotate back) -> dx
             qlin_bwd_dw(qg2, sg2, qx)              -> dw
   update    qlin_sgd_requant(qw, sw, dw, lr, seed, step, bias, db)
 """
@@ -72,11 +71,8 @@ class LinearW8A8Training:
                                    col_sum=self.db)
         qg2, sg2 = r[0], r[1]
         self._tick("quantize_dy_cols")
-        dx = nat.qlin_bwd_dx(qg1, sg1, self.qw, dx=self._dx[:M])
+        dx = nat.qlin_bwd_dx(qg1, sg1, self.qw, had_block=self.had, dx=self._dx[:M])
         self._tick("bwd_dx")
-        if self.had:
-            nat.qlin_hadamard(dx, self.had, y=dx)
-            self._tick("unrotate_dx")
         nat.qlin_bwd_dw(qg2, sg2, self.qx, dw=self.dw)
         self._tick("bwd_dw")
         return dx
