@@ -46,6 +46,10 @@ ROW_CASES = [
     (5, 14336, 128, False, False),     # MLP fc2 input width
     (2, 20480, 256, True, False),      # 1024-thread path
     (2, 131072, 64, False, True),      # longest row
+    (4500, 5376, 128, True, True),     # more rows than workgroups: rows grid-strided
+    (4200, 20480, 0, False, True),     # grid-strided 1024-thread path
+    (33, 1088, 64, True, True),        # fixed 64-block rotation, ragged pass
+    (9, 384, 128, False, True),        # one partial 256-thread pass, 3 blocks
 ]
 
 
@@ -103,7 +107,9 @@ def test_quantize_cols(T, Q, orc, rows, cols, bf16, pre):
 
 @pytest.mark.parametrize("rows,cols,blk,bf16", [(3, 256, 128, False), (64, 5376, 128, False),
                                                 (5, 1024, 512, True), (7, 64, 2, False),
-                                                (9, 96, 32, True), (1, 16, 8, False)])
+                                                (9, 96, 32, True), (1, 16, 8, False),
+                                                (4, 384, 64, True), (6, 160, 16, False),
+                                                (2, 48, 16, True), (5, 4096, 128, True)])
 def test_hadamard(T, Q, orc, rows, cols, blk, bf16):
     rng = np.random.default_rng(blk + rows)
     x = _x(rng, rows, cols, bf16)

@@ -4,7 +4,7 @@
 // HIP call.
 #include <math.h>
 
-#include "../../include/qlin.h"
+#include "qlin.h"
 #include "launch.hpp"
 
 namespace {

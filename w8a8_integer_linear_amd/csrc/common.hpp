@@ -16,24 +16,54 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// Eight consecutive elements of an fp32 or bf16 array as loaded from memory
+// (16 or 32 bytes), before widening.
+template <bool BF16> struct Raw8;
+template <> struct Raw8<true> {
+    i32x4 w;
+};
+template <> struct Raw8<false> {
+    f32x4 a, b;
+};
+
+// Raw load of the eight elements starting at element index 'idx' (a multiple
+// of 8).
+template <bool BF16>
+__device__ __forceinline__ Raw8<BF16> load_raw8(const void *base, int64_t idx)
+{
+    Raw8<BF16> r;
+    if constexpr (BF16) {
+        r.w = *reinterpret_cast<const i32x4 *>(static_cast<const uint16_t *>(base) + idx);
+    } else {
+        const f32x4 *p = reinterpret_cast<const f32x4 *>(static_cast<const float *>(base) + idx);
+        r.a = p[0];
+        r.b = p[1];
+    }
+    return r;
+}
+
+// Widen to fp32 (bf16 -> fp32 is exact).
+template <bool BF16>
+__device__ __forceinline__ void unpack8(const Raw8<BF16> &r, float v[8])
+{
+    if constexpr (BF16) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            v[2 * e] = bf16_lo((uint32_t)r.w[e]);
+            v[2 * e + 1] = bf16_hi((uint32_t)r.w[e]);
+        }
+    } else {
+        v[0] = r.a[0]; v[1] = r.a[1]; v[2] = r.a[2]; v[3] = r.a[3];
+        v[4] = r.b[0]; v[5] = r.b[1]; v[6] = r.b[2]; v[7] = r.b[3];
+    }
+}
+
 // Eight consecutive elements starting at element index 'idx' (a multiple of 8)
-// of an fp32 or bf16 array, widened to fp32 (bf16 -> fp32 is exact).
+// of an fp32 or bf16 array, widened to fp32.
 template <bool BF16>
 __device__ __forceinline__ void load8(const void *base, int64_t idx, float v[8])
 {
-    if constexpr (BF16) {
-        i32x4 w = *reinterpret_cast<const i32x4 *>(static_cast<const uint16_t *>(base) + idx);
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            v[2 * e] = bf16_lo((uint32_t)w[e]);
-            v[2 * e + 1] = bf16_hi((uint32_t)w[e]);
-        }
-    } else {
-        const f32x4 *p = reinterpret_cast<const f32x4 *>(static_cast<const float *>(base) + idx);
-        f32x4 a = p[0], b = p[1];
-        v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
-        v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
-    }
+    unpack8<BF16>(load_raw8<BF16>(base, idx), v);
 }
 
 __device__ __forceinline__ void store8(float *base, int64_t idx, const float v[8])
@@ -79,6 +109,135 @@ __device__ __forceinline__ void fwht8_lanes(float v[8], int blk, float cb)
         v[i] = v[i] * cb;
 }
 
+// Fixed-size rotation of blocks of BLK in {16, 32, 64, 128} elements, each
+// held by BLK / 8 consecutive lanes of a 16-lane row (eight consecutive
+// elements per lane).
+//
+// The cross-lane stages run on DPP lane permutes, which inside a row of 16
+// lanes reach partner lane ^ 1 and ^ 2 (quad permutes), ^ 7 (half-row mirror)
+// and ^ 8 (row rotation by 8) in one instruction, but not ^ 4.  So for
+// BLK >= 64 the lane with row position l holds chunk p = l ^ (3 * bit2(l)) of
+// its block (an involution on 0..15): the chunk at distance 4 then sits in
+// lane l ^ 7, the one at distance 8 in lane l ^ 8.  had_chunk() maps a chunk
+// index to the one its lane processes.
+//
+// Each stage pairs the lower chunk (bit k of p clear) with the upper one; the
+// oracle's lower result is lo + hi and the upper lo - hi.  A lane keeps its
+// values multiplied by a sign sigma (+1 or -1, the same for its eight values)
+// and computes w' = w + c * w_partner with c = +1 on the lower and -1 on the
+// upper lane: partner and own sigma agree (they differ only in bit k, not yet
+// processed), so the lower lane gets sigma (lo + hi) and the upper lane
+// sigma (hi - lo) = -sigma (lo - hi), i.e. sigma flips on upper lanes.  Each
+// value is one correctly rounded sum of +-lo and +-hi (the product by c is
+// exact), so with the sign undone (exactly, in the final scaling by
+// sigma * cb) the result is bit-identical to lo + hi and lo - hi.
+template <int BLK>
+__device__ __forceinline__ int64_t had_chunk(int64_t c)
+{
+    if constexpr (BLK >= 64)
+        return c ^ (((c >> 2) & 1) * 3);
+    else
+        return c;
+}
+
+// One stage for all eight values: v += c * v[partner lane], as v_fmac_f32
+// with its first source read through DPP.  Written as one asm block because
+// the compiler does not fold a DPP move into a multiply-accumulate.  The
+// s_nop covers the two wait states a DPP read needs after a VALU write of
+// the same register; inside the block each instruction writes only its own
+// register.
+#define QLIN_FWHT_DPP_STAGE(CTRL)                                                                \
+    asm("s_nop 1\n\t"                                                                           \
+        "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                     \
+        "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                     \
+        "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                     \
+        "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                     \
+        "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                     \
+        "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                     \
+        "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                     \
+        "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf"                           \
+        : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),    \
+          "+v"(v[7])                                                                             \
+        : "v"(c))
+
+template <int BLK, int K>
+__device__ __forceinline__ void fwht_lane_stage(float v[8], int p)
+{
+    static_assert(K < 4 && (8 << K) < BLK, "stage outside the block");
+    const float c = ((p >> K) & 1) ? -1.0f : 1.0f;
+    if constexpr (K == 0)
+        QLIN_FWHT_DPP_STAGE("quad_perm:[1,0,3,2]");
+    else if constexpr (K == 1)
+        QLIN_FWHT_DPP_STAGE("quad_perm:[2,3,0,1]");
+    else if constexpr (K == 2)
+        QLIN_FWHT_DPP_STAGE("row_half_mirror");
+    else
+        QLIN_FWHT_DPP_STAGE("row_ror:8");
+}
+
+template <int BLK>
+__device__ __forceinline__ void fwht8_fixed(float v[8], float cb)
+{
+    static_assert(BLK >= 16 && BLK <= 128 && (BLK & (BLK - 1)) == 0, "block size");
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            if ((i & h) == 0) {
+                const float lo = v[i], hi = v[i + h];
+                v[i] = lo + hi;
+                v[i + h] = lo - hi;
+            }
+        }
+    }
+    const int p = (int)had_chunk<BLK>(__lane_id() & 15) & (BLK / 8 - 1);
+    fwht_lane_stage<BLK, 0>(v, p);
+    if constexpr (BLK > 16)
+        fwht_lane_stage<BLK, 1>(v, p);
+    if constexpr (BLK > 32)
+        fwht_lane_stage<BLK, 2>(v, p);
+    if constexpr (BLK > 64)
+        fwht_lane_stage<BLK, 3>(v, p);
+    const float scale = (__builtin_popcount(p) & 1) ? -cb : cb;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        v[i] = v[i] * scale;
+}
+
+// Eight INT8 codes rne(fl(g / s)) packed into two dwords, for a scale s > 0
+// that is a normal number, with inv = fl(1 / s).  Fast path: t = fl(g * inv)
+// is within 2^-15 of fl(g / s) for |g| <= 127.01 s, so both round to the same
+// integer unless t lies within 2^-14 of a half-integer; if any of the eight
+// does, all eight take the exact quotient.  Rounding to an integer is done by
+// adding 1.5 * 2^23 (round to nearest even in the addition), which also leaves
+// the code as the low byte of the sum's bits.  The quotient is at most
+// 127 (1 + 2^-22) < 127.5 in magnitude, so no clamp is needed.
+__device__ __forceinline__ i32x2 quant8(const float g[8], float s, float inv)
+{
+    constexpr float kMagic = 0x1.8p23f;
+    float f[8];
+    float dmax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        const float t = g[e] * inv;
+        f[e] = t + kMagic;
+        dmax = fmaxf(dmax, __builtin_fabsf(t - (f[e] - kMagic)));
+    }
+    if (!(dmax < 0.5f - 0x1p-14f)) {
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            f[e] = __builtin_rintf(g[e] / s) + kMagic;
+    }
+    auto pack = [&](int o) {
+        const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(f[o + 1]), __float_as_uint(f[o]),
+                                                  0x0C0C0400u);
+        const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(f[o + 3]),
+                                                  __float_as_uint(f[o + 2]), 0x04000C0Cu);
+        return (int)(lo | hi);
+    };
+    return i32x2{pack(0), pack(4)};
+}
+
 __device__ __forceinline__ float wave_max(float v)
 {
 #pragma unroll
@@ -97,6 +256,15 @@ __device__ __forceinline__ float wave_sum(float v)
 
 // Max over the workgroup; every thread gets the result.  'red' holds one
 // float per wave.  Contains barriers: call from uniform control flow.
+//
+// The barriers wait only for the workgroup's LDS operations: __syncthreads()
+// would also wait for every outstanding global load of the wave, draining
+// loads issued ahead of time for the next piece of work.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <int THREADS>
 __device__ __forceinline__ float block_max(float v, float *red)
 {
@@ -105,12 +273,12 @@ __device__ __forceinline__ float block_max(float v, float *red)
     const int w = threadIdx.x / kWave;
     if (__lane_id() == 0)
         red[w] = v;
-    __syncthreads();
+    lds_barrier();
     float r = red[0];
 #pragma unroll
     for (int i = 1; i < NW; i++)
         r = fmaxf(r, red[i]);
-    __syncthreads();
+    lds_barrier();
     return r;
 }
 

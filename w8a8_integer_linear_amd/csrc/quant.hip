@@ -12,6 +12,8 @@
 // merges slabs with an order-free integer atomicMax on the fp32 bits of the
 // non-negative maxima; a tiny kernel turns maxima into scales; pass 2
 // quantizes elementwise.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -19,115 +21,187 @@ namespace qlin {
 
 // ------------------------------------------------------------ row quantizer
 
-template <bool BF16, int THREADS, int J>
-__global__ __launch_bounds__(THREADS) void quant_rows_kernel(
-    const void *__restrict__ x, int64_t cols, const float *__restrict__ prescale, int had,
-    float cb, int8_t *__restrict__ q, float *__restrict__ s)
+// Rotation of one 8-element chunk: HAD is the block size when it is known at
+// compile time (16 .. 128; 0: no rotation), -1 for a block size given at run
+// time.  With a fixed block the lane processes chunk had_chunk<HAD>(c) in
+// place of c.
+template <int HAD>
+__device__ __forceinline__ void rotate8(float v[8], int had, float cb)
 {
+    if constexpr (HAD > 0)
+        fwht8_fixed<HAD>(v, cb);
+    else if constexpr (HAD < 0)
+        fwht8_lanes(v, had, cb);
+}
+
+template <int HAD>
+__device__ __forceinline__ int64_t lane_chunk(int64_t c)
+{
+    if constexpr (HAD > 0)
+        return had_chunk<HAD>(c);
+    else
+        return c;
+}
+
+// Grid-stride over rows.  Each pass issues the loads of the workgroup's next
+// row before working on the current one, so HBM reads overlap the rotation,
+// reduction and quantization.  Loads are unconditional (indexes past the row
+// end are clamped to its last chunk and the values dropped) so that they all
+// issue back to back.  The per-column prescale of the thread's chunks is
+// loaded into registers once and reused for every row.
+template <bool BF16, int THREADS, int J, int HAD>
+__global__ __launch_bounds__(THREADS) void quant_rows_kernel(
+    const void *__restrict__ x, int64_t rows, int64_t cols, const float *__restrict__ prescale,
+    int had, float cb, int8_t *__restrict__ q, float *__restrict__ s)
+{
+    // 1024-thread workgroups have 128 registers per lane: no room for the
+    // prescale or the next row's data, which they load when they need it.
+    constexpr bool kKeepPrescale = THREADS <= 256;
+    constexpr bool kPrefetch = THREADS <= 256;
     __shared__ float red[THREADS / kWave];
-    const int64_t row = blockIdx.x;
     const int t = threadIdx.x;
     const int64_t nch = cols / 8;
-    const int64_t base = row * cols;
-    float v[J][8];
-    float amax = 0.0f;
+    // The chunk a lane processes in pass j; the permutation stays inside
+    // groups of 16 chunks, all valid or all past the end (cols is a multiple
+    // of 128 when HAD is 128, of 16 otherwise), and so does the clamp.
+    auto chunk = [&](int j) {
+        const int64_t c = lane_chunk<HAD>(t + (int64_t)j * THREADS);
+        return c < nch ? c : nch - 1;
+    };
+    float p[kKeepPrescale ? J : 1][8];
+    if (kKeepPrescale && prescale) {
 #pragma unroll
-    for (int j = 0; j < J; j++) {
-        const int64_t c = t + (int64_t)j * THREADS;
-        const bool ok = c < nch;
-        if (ok) {
-            load8<BF16>(x, base + c * 8, v[j]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; e++)
-                v[j][e] = 0.0f;
-        }
-        // Chunk index c is the same function of the lane in every pass, so
-        // lanes of one block stay together; a block is all valid or all
-        // padding because had divides cols.
-        if (had)
-            fwht8_lanes(v[j], had, cb);
-        if (prescale && ok) {
-            const float *p = prescale + c * 8;
-            f32x4 p0 = reinterpret_cast<const f32x4 *>(p)[0];
-            f32x4 p1 = reinterpret_cast<const f32x4 *>(p)[1];
-            v[j][0] = v[j][0] * p0[0]; v[j][1] = v[j][1] * p0[1];
-            v[j][2] = v[j][2] * p0[2]; v[j][3] = v[j][3] * p0[3];
-            v[j][4] = v[j][4] * p1[0]; v[j][5] = v[j][5] * p1[1];
-            v[j][6] = v[j][6] * p1[2]; v[j][7] = v[j][7] * p1[3];
-        }
-        if (ok) {
-#pragma unroll
-            for (int e = 0; e < 8; e++)
-                amax = fmaxf(amax, __builtin_fabsf(v[j][e]));
-        }
+        for (int j = 0; j < J; j++)
+            load8<false>(prescale, chunk(j) * 8, p[kKeepPrescale ? j : 0]);
     }
-    const float a = block_max<THREADS>(amax, red);
-    const float sc = a / 127.0f;
-    if (t == 0)
-        s[row] = sc;
-    const float inv = 1.0f / sc;
-    const bool zero = (a == 0.0f);
-    const bool subnormal = !zero && sc < 0x1p-126f;
+    Raw8<BF16> cur[J];
+    int64_t row = blockIdx.x;
 #pragma unroll
-    for (int j = 0; j < J; j++) {
-        const int64_t c = t + (int64_t)j * THREADS;
-        if (c >= nch)
-            continue;
-        float r[8];
-        if (zero) {
+    for (int j = 0; j < J; j++)
+        cur[j] = load_raw8<BF16>(x, row * cols + chunk(j) * 8);
+    for (; row < rows; row += gridDim.x) {
+        const int64_t base = row * cols;
+        const int64_t next = row + gridDim.x < rows ? row + gridDim.x : row;
+        Raw8<BF16> nxt[kPrefetch ? J : 1];
+        if constexpr (kPrefetch) {
 #pragma unroll
-            for (int e = 0; e < 8; e++)
-                r[e] = 0.0f;
-        } else if (subnormal) {
-#pragma unroll
-            for (int e = 0; e < 8; e++)
-                r[e] = quant_code_exact(v[j][e], sc);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; e++)
-                r[e] = quant_code(v[j][e], sc, inv);
+            for (int j = 0; j < J; j++)
+                nxt[j] = load_raw8<BF16>(x, next * cols + chunk(j) * 8);
         }
-        i32x2 out;
-        out[0] = (int)pack4(r[0], r[1], r[2], r[3]);
-        out[1] = (int)pack4(r[4], r[5], r[6], r[7]);
-        *reinterpret_cast<i32x2 *>(q + base + c * 8) = out;
+        float v[J][8];
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < J; j++) {
+            const bool ok = t + (int64_t)j * THREADS < nch;
+            unpack8<BF16>(cur[j], v[j]);
+            // Chunk index c is the same function of the lane in every pass, so
+            // lanes of one block stay together; a block is all valid or all
+            // clamped because had divides cols.
+            rotate8<HAD>(v[j], had, cb);
+            if (prescale) {
+                float pr[8];
+                if constexpr (kKeepPrescale) {
+#pragma unroll
+                    for (int e = 0; e < 8; e++)
+                        pr[e] = p[j][e];
+                } else {
+                    load8<false>(prescale, chunk(j) * 8, pr);
+                }
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    v[j][e] = v[j][e] * pr[e];
+            }
+            if (ok) {
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    amax = fmaxf(amax, __builtin_fabsf(v[j][e]));
+            }
+        }
+        const float a = block_max<THREADS>(amax, red);
+        const float sc = a / 127.0f;
+        if (t == 0)
+            s[row] = sc;
+        const float inv = 1.0f / sc;
+        const bool zero = (a == 0.0f);
+        const bool subnormal = !zero && sc < 0x1p-126f;
+#pragma unroll
+        for (int j = 0; j < J; j++) {
+            const int64_t c = lane_chunk<HAD>(t + (int64_t)j * THREADS);
+            i32x2 out;
+            if (zero) {
+                out = i32x2{0, 0};
+            } else if (subnormal) {
+                float r[8];
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    r[e] = quant_code_exact(v[j][e], sc);
+                out[0] = (int)pack4(r[0], r[1], r[2], r[3]);
+                out[1] = (int)pack4(r[4], r[5], r[6], r[7]);
+            } else {
+                out = quant8(v[j], sc, inv);
+            }
+            if (c < nch)
+                *reinterpret_cast<i32x2 *>(q + base + c * 8) = out;
+        }
+#pragma unroll
+        for (int j = 0; j < J; j++)
+            cur[j] = kPrefetch ? nxt[kPrefetch ? j : 0] : load_raw8<BF16>(x, next * cols + chunk(j) * 8);
     }
 }
 
-template <bool BF16, int THREADS, int J>
+// Workgroups per launch: enough to fill the GPU several times over; each
+// loops over rows.
+constexpr int64_t kRowGrid = 4096;
+
+template <bool BF16, int THREADS, int J, int HAD>
 static void launch_rows_t(const void *x, int64_t rows, int64_t cols, const float *prescale,
                           int had, float cb, int8_t *q, float *s, hipStream_t st)
 {
-    hipLaunchKernelGGL((quant_rows_kernel<BF16, THREADS, J>), dim3((unsigned)rows),
-                       dim3(THREADS), 0, st, x, cols, prescale, had, cb, q, s);
+    const unsigned grid = (unsigned)(rows < kRowGrid ? rows : kRowGrid);
+    hipLaunchKernelGGL((quant_rows_kernel<BF16, THREADS, J, HAD>), dim3(grid), dim3(THREADS), 0,
+                       st, x, rows, cols, prescale, had, cb, q, s);
+}
+
+template <bool BF16, int HAD>
+static void launch_rows_h(const void *x, int64_t rows, int64_t cols, const float *prescale,
+                          int had, float cb, int8_t *q, float *s, hipStream_t st)
+{
+    // Registers per lane: 8 * J floats (and as many for the prescale).  256
+    // threads cover 2048 elements per pass; rows longer than 16384 switch to
+    // 1024 threads.
+    const int64_t nch = cols / 8;
+    const int64_t j256 = (nch + 255) / 256;
+    switch (j256) {
+    case 1: return launch_rows_t<BF16, 256, 1, HAD>(x, rows, cols, prescale, had, cb, q, s, st);
+    case 2: return launch_rows_t<BF16, 256, 2, HAD>(x, rows, cols, prescale, had, cb, q, s, st);
+    case 3: return launch_rows_t<BF16, 256, 3, HAD>(x, rows, cols, prescale, had, cb, q, s, st);
+    case 4: return launch_rows_t<BF16, 256, 4, HAD>(x, rows, cols, prescale, had, cb, q, s, st);
+    case 5: return launch_rows_t<BF16, 256, 5, HAD>(x, rows, cols, prescale, had, cb, q, s, st);
+    case 6: return launch_rows_t<BF16, 256, 6, HAD>(x, rows, cols, prescale, had, cb, q, s, st);
+    case 7: return launch_rows_t<BF16, 256, 7, HAD>(x, rows, cols, prescale, had, cb, q, s, st);
+    case 8: return launch_rows_t<BF16, 256, 8, HAD>(x, rows, cols, prescale, had, cb, q, s, st);
+    default: break;
+    }
+    const int64_t j1024 = (nch + 1023) / 1024;
+    if (j1024 <= 4)
+        return launch_rows_t<BF16, 1024, 4, HAD>(x, rows, cols, prescale, had, cb, q, s, st);
+    if (j1024 <= 8)
+        return launch_rows_t<BF16, 1024, 8, HAD>(x, rows, cols, prescale, had, cb, q, s, st);
+    return launch_rows_t<BF16, 1024, 16, HAD>(x, rows, cols, prescale, had, cb, q, s, st);
 }
 
 template <bool BF16>
 static void launch_rows_dt(const void *x, int64_t rows, int64_t cols, const float *prescale,
                            int had, float cb, int8_t *q, float *s, hipStream_t st)
 {
-    // Registers per lane: 8 * J floats.  256 threads cover 2048 elements per
-    // pass; rows longer than 16384 switch to 1024 threads.
-    const int64_t nch = cols / 8;
-    const int64_t j256 = (nch + 255) / 256;
-    switch (j256) {
-    case 1: return launch_rows_t<BF16, 256, 1>(x, rows, cols, prescale, had, cb, q, s, st);
-    case 2: return launch_rows_t<BF16, 256, 2>(x, rows, cols, prescale, had, cb, q, s, st);
-    case 3: return launch_rows_t<BF16, 256, 3>(x, rows, cols, prescale, had, cb, q, s, st);
-    case 4: return launch_rows_t<BF16, 256, 4>(x, rows, cols, prescale, had, cb, q, s, st);
-    case 5: return launch_rows_t<BF16, 256, 5>(x, rows, cols, prescale, had, cb, q, s, st);
-    case 6: return launch_rows_t<BF16, 256, 6>(x, rows, cols, prescale, had, cb, q, s, st);
-    case 7: return launch_rows_t<BF16, 256, 7>(x, rows, cols, prescale, had, cb, q, s, st);
-    case 8: return launch_rows_t<BF16, 256, 8>(x, rows, cols, prescale, had, cb, q, s, st);
-    default: break;
-    }
-    const int64_t j1024 = (nch + 1023) / 1024;
-    if (j1024 <= 4)
-        return launch_rows_t<BF16, 1024, 4>(x, rows, cols, prescale, had, cb, q, s, st);
-    if (j1024 <= 8)
-        return launch_rows_t<BF16, 1024, 8>(x, rows, cols, prescale, had, cb, q, s, st);
-    return launch_rows_t<BF16, 1024, 16>(x, rows, cols, prescale, had, cb, q, s, st);
+    if (had == 0)
+        launch_rows_h<BF16, 0>(x, rows, cols, prescale, had, cb, q, s, st);
+    else if (had == 128)
+        launch_rows_h<BF16, 128>(x, rows, cols, prescale, had, cb, q, s, st);
+    else if (had == 64)
+        launch_rows_h<BF16, 64>(x, rows, cols, prescale, had, cb, q, s, st);
+    else
+        launch_rows_h<BF16, -1>(x, rows, cols, prescale, had, cb, q, s, st);
 }
 
 void launch_quantize_rows(const void *x, bool bf16, int64_t rows, int64_t cols,
@@ -296,11 +370,13 @@ void launch_quantize_cols(const void *x, bool bf16, int64_t rows, int64_t cols,
 
 // Flat over 8-element chunks: a wave covers 64 consecutive chunks, so every
 // block (at most 64 chunks, aligned) sits inside one wave.
-template <bool BF16>
+template <bool BF16, int HAD>
 __global__ __launch_bounds__(256) void hadamard_kernel(const void *__restrict__ x, int64_t nch,
                                                        int blk, float cb, float *__restrict__ y)
 {
-    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    // A fixed block size permutes chunks inside groups of 16, all valid or all
+    // past the end (nch is then a multiple of 16).
+    const int64_t c = lane_chunk<HAD>((int64_t)blockIdx.x * 256 + threadIdx.x);
     const bool ok = c < nch;
     float v[8];
     if (ok) {
@@ -310,7 +386,7 @@ __global__ __launch_bounds__(256) void hadamard_kernel(const void *__restrict__ 
         for (int e = 0; e < 8; e++)
             v[e] = 0.0f;
     }
-    fwht8_lanes(v, blk, cb);
+    rotate8<HAD>(v, blk, cb);
     if (ok)
         store8(y, c * 8, v);
 }
@@ -320,11 +396,23 @@ void launch_hadamard(const void *x, bool bf16, int64_t rows, int64_t cols, int b
 {
     const int64_t nch = rows * cols / 8;
     const unsigned grid = (unsigned)((nch + 255) / 256);
+    auto go = [&](auto bf, auto h) {
+        hipLaunchKernelGGL((hadamard_kernel<decltype(bf)::value, decltype(h)::value>), dim3(grid),
+                           dim3(256), 0, st, x, nch, blk, cb, y);
+    };
+    auto with_block = [&](auto bf) {
+        switch (blk) {
+        case 16: return go(bf, std::integral_constant<int, 16>());
+        case 32: return go(bf, std::integral_constant<int, 32>());
+        case 64: return go(bf, std::integral_constant<int, 64>());
+        case 128: return go(bf, std::integral_constant<int, 128>());
+        default: return go(bf, std::integral_constant<int, -1>());
+        }
+    };
     if (bf16)
-        hipLaunchKernelGGL(hadamard_kernel<true>, dim3(grid), dim3(256), 0, st, x, nch, blk, cb, y);
+        with_block(std::true_type());
     else
-        hipLaunchKernelGGL(hadamard_kernel<false>, dim3(grid), dim3(256), 0, st, x, nch, blk, cb,
-                           y);
+        with_block(std::false_type());
 }
 
 } // namespace qlin
