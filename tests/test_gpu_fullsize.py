@@ -1,6 +1,7 @@
 """Full-size parity of one training step of the headline layer (12000 tokens,
 5376 -> 7168, rotation block 128), run through the same layer object and
-launch configuration the benchmark times.
+launch configuration the benchmark times, and of the transformer MLP's two
+layers (8192 tokens, 4096 -> 14336 -> 4096) each on its own.
 
 The oracle recomputes every per-row quantity from the seeded inputs itself
 (weight prep, activation codes, both gradient quantizations) and compares
@@ -98,6 +99,20 @@ def test_headline_step(orc):
     d = workloads.linear(12000, 5376, 7168, seed=0)
     got = _step(T, d, 12000, 5376, 7168, 128, 1e-3, 0, 0)
     _check_step(orc, d, got, 12000, 5376, 7168, 128, 1e-3, 0, 0, 2048, np.random.default_rng(3))
+
+
+@pytest.mark.parametrize("which", [1, 2])
+def test_mlp_layer_step(orc, which):
+    """The transformer MLP's layers at their own shapes (8192 tokens; fc1
+    4096 -> 14336 with a bf16 input and fp32 gradient, fc2 14336 -> 4096 with
+    an fp32 GELU-output input and bf16 gradient), rotation 128 on both."""
+    T = torch_cuda()
+    d = workloads.mlp_layer(which)
+    N, K = d["w"].shape
+    M = d["x"].shape[0]
+    got = _step(T, d, M, K, N, 128, d["lr"], d["seed"], 0)
+    _check_step(orc, d, got, M, K, N, 128, d["lr"], d["seed"], 0, 2048,
+                np.random.default_rng(10 + which))
 
 
 def test_deterministic(orc):

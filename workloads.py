@@ -19,8 +19,15 @@ measurements, OneTrainer PR #1681 commit note 1: 5376 -> 7168 at 2048 and
   mlp     X bf16 [8192,4096] ~N(0,1), W1 [14336,4096], W2 [4096,14336]
           ~N(0,0.02), dY2 bf16 [8192,4096] ~N(0,0.01), rotation block 128 on
           both inputs, SGD lr 1e-3 with seeds 0 (fc1) and 1 (fc2).
+          Per-layer steps of the MLP draw, after those: H [8192,14336] ~N(0,1)
+          whose erf-GELU (float64, rounded to fp32) stands in for fc2's input,
+          and dY1 fp32 [8192,14336] ~N(0,0.01) for the gradient reaching fc1
+          through the GELU.  The GELU sits outside the INT8 path; these inputs
+          let each layer be checked on its own at the MLP's shapes.
 Draw order is fixed: X, outlier permutation, W, bias, dY.
 """
+import math
+
 import numpy as np
 
 HEADLINE = dict(M=12000, K=5376, N=7168, had_block=128)
@@ -82,3 +89,25 @@ def mlp(M=8192, d=4096, h=14336, seed=0):
     dy2 = _normal(rng, (M, d), 0.01)
     return dict(x=f32_to_bf16_bits(x), w1=w1, w2=w2, dy2=f32_to_bf16_bits(dy2),
                 lr=1e-3, had_block=128, seeds=(0, 1))
+
+
+def _gelu(h):
+    """Exact (erf) GELU, in float64, rounded once to fp32."""
+    from scipy.special import erf
+    h64 = h.astype(np.float64)
+    return (0.5 * h64 * (1.0 + erf(h64 / math.sqrt(2.0)))).astype(np.float32)
+
+
+def mlp_layer(which, M=8192, d=4096, h=14336, seed=0):
+    """Inputs for one layer of the MLP on its own: which = 1 (fc1, d -> h, bf16
+    input, fp32 gradient) or 2 (fc2, h -> d, fp32 GELU-output input, bf16
+    gradient)."""
+    base = mlp(M, d, h, seed)
+    rng = np.random.default_rng([seed, 5])
+    hid = _normal(rng, (M, h), 1.0)
+    if which == 1:
+        dy1 = _normal(rng, (M, h), 0.01)
+        return dict(x=base["x"], w=base["w1"], b=None, dy=dy1, lr=base["lr"], had_block=128,
+                    seed=base["seeds"][0])
+    return dict(x=_gelu(hid), w=base["w2"], b=None, dy=base["dy2"], lr=base["lr"],
+                had_block=128, seed=base["seeds"][1])
