@@ -105,7 +105,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-tokens", type=int, default=768,
+    ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="token sample of the oracle CPU baseline (0 skips it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before the steps, run a plain device copy of 512 MiB (three times) "

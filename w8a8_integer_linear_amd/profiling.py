@@ -8,9 +8,14 @@ the design doc have written their CSVs under OUT_DIR):
 Reads  OUT_DIR/kt/*kernel_stats.csv      (rocprofv3 --kernel-trace --stats)
        OUT_DIR/fetch/*counter_collection.csv (rocprofv3 --pmc FETCH_SIZE)
        OUT_DIR/write/*counter_collection.csv (rocprofv3 --pmc WRITE_SIZE)
-Writes profiles/kernels_headline_step.txt (per-kernel durations) and
+       OUT_DIR/busy/*counter_collection.csv (rocprofv3 --pmc SQ_BUSY_CYCLES
+                                    SQ_VALU_MFMA_BUSY_CYCLES), if present
+Writes profiles/kernels_headline_step.txt (per-kernel durations),
        profiles/pmc_traffic.json + profiles/pmc_traffic.txt (HBM bytes per
-       launch, scaled by the reading of the calibration copy of 512 MiB).
+       launch, scaled by the reading of the calibration copy of 512 MiB) and
+       profiles/mfma_busy_clock.txt (per kernel: the shader clock it ran at,
+       SQ busy cycles per shader engine over the dispatch's duration, and the
+       fraction of those cycles the SIMDs' matrix pipes were busy).
 """
 import csv
 import glob
@@ -55,6 +60,29 @@ def dispatches(out_dir, sub, name):
         if r["Counter_Name"] == name:
             out[int(r["Dispatch_Id"])] = (_short(r["Kernel_Name"]), float(r["Counter_Value"]))
     return out
+
+
+def busy_clock(out_dir):
+    """Per kernel: median effective shader clock (GHz) and MFMA-busy fraction."""
+    path = _one(os.path.join(out_dir, "busy", "*counter_collection.csv"))
+    info = list(csv.DictReader(open(_one(os.path.join(out_dir, "busy", "*agent_info.csv")))))
+    gpu = [r for r in info if r["Agent_Type"] == "GPU"][0]
+    n_se, n_simd = int(gpu["Array_Count"]), int(gpu["Simd_Count"])
+    per = {}
+    for r in csv.DictReader(open(path)):
+        d = per.setdefault(int(r["Dispatch_Id"]), {"name": _short(r["Kernel_Name"])})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        d["dur_s"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    by = {}
+    for d in per.values():
+        if d["dur_s"] <= 0 or "SQ_BUSY_CYCLES" not in d:
+            continue
+        cycles = d["SQ_BUSY_CYCLES"] / n_se
+        by.setdefault(d["name"], []).append(
+            (cycles / d["dur_s"] / 1e9, d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / n_simd / cycles,
+             d["dur_s"] * 1e6))
+    return {k: tuple(statistics.median(v[i] for v in vals) for i in range(3)) + (len(vals),)
+            for k, vals in by.items()}, n_se, n_simd
 
 
 def main(out_dir, digest=None):
@@ -115,6 +143,21 @@ def main(out_dir, digest=None):
                     f"{v['bytes_per_launch'] / 1e6:>9.1f}\n")
     print(open(os.path.join(PROFILES, "kernels_headline_step.txt")).read())
     print(open(os.path.join(PROFILES, "pmc_traffic.txt")).read())
+    if glob.glob(os.path.join(out_dir, "busy", "*counter_collection.csv")):
+        res, n_se, n_simd = busy_clock(out_dir)
+        with open(os.path.join(PROFILES, "mfma_busy_clock.txt"), "w") as f:
+            f.write("# Shader clock and matrix-pipe occupancy per kernel of the headline step.\n")
+            f.write("#   rocprofv3 --pmc SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES -d OUT/busy -o busy "
+                    "--output-format csv -- python bench.py --steps 2 --warmup 1 --cpu-tokens 0\n")
+            f.write(f"# clock = SQ_BUSY_CYCLES / {n_se} shader engines / dispatch duration; "
+                    f"mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / {n_simd} SIMDs / busy cycles.\n")
+            f.write("# Fraction of the 2.4 GHz dense INT8 peak = mfma_busy x clock / 2.4.\n")
+            f.write(f"# {'kernel':<70} {'clock_GHz':>9} {'mfma_busy':>9} {'of_peak':>8} "
+                    f"{'dur_us':>8} {'n':>3}\n")
+            for k, (clk, busy, dur, n) in sorted(res.items(), key=lambda kv: -kv[1][2]):
+                f.write(f"  {k[:70]:<70} {clk:>9.3f} {busy:>9.3f} {busy * clk / 2.4:>8.3f} "
+                        f"{dur:>8.1f} {n:>3}\n")
+        print(open(os.path.join(PROFILES, "mfma_busy_clock.txt")).read())
 
 
 if __name__ == "__main__":
