@@ -4,8 +4,9 @@
 Workload: 12000 tokens, 5376 -> 7168, block-Hadamard rotation 128, bf16
 activations with 1% outlier channels, bf16 dY, seeded synthetic data (the
 headline shape of OneTrainer PR #1681's measurements).  A step is the whole
-path: rotate + quantize X, forward product, both dY quantizations, dX
-product, un-rotation of dX, dW product, and the SGD stochastic requant.
+path: rotate + quantize X, forward product, both dY quantizations (one
+call), dX product with the un-rotation in its epilogue, dW product, and the
+SGD stochastic requant.
 Metric: int8 TOPS counting the three products (3 * 2 * M * N * K ops) over
 the wall time of the full step, and its fraction of the dense INT8 MFMA peak.
 
@@ -34,23 +35,24 @@ GEMM_OPS = 2.0 * M * N * K
 METRIC = "INT8 linear fwd+bwd TOPS at 12000x5376->7168; % of INT8 MFMA peak"
 
 # Algorithmic bytes per launch of the memory-bound calls (read once + write once).
+# quantize_dy reads dY twice (the column scales must be known before any
+# column code is written) and writes both code arrays.
 ALG_BYTES = {
     "quantize_x": M * K * 2 + M * K + 4 * M,
-    "quantize_dy_rows": M * N * 2 + M * N + 4 * M + 4 * N,
-    "quantize_dy_cols": 2 * (M * N * 2) + M * N + 4 * N + 4 * M,
-    "unrotate_dx": 2 * M * K * 4,
+    "quantize_dy": 2 * (M * N * 2) + 2 * (M * N) + 8 * M + 8 * N,
     "sgd_requant": N * K * (1 + 4 + 1) + 8 * N,
 }
 GEMMS = ("fwd", "bwd_dx", "bwd_dw")
 COPY_BYTES = 512 << 20        # calibration copy: reads and writes this many bytes
-# Kernel symbol behind each call, as rocprofv3 names it.
-KERNEL_OF = {"fwd": "gemm_kernel<256, 256, 2, 4, 128, 1, false, false, 2>",
-             "bwd_dx": "gemm_kernel<256, 256, 2, 4, 128, 1, false, true, 1>",
-             "bwd_dw": "gemm_kernel<256, 256, 2, 4, 128, 1, true, true, 1>",
-             "quantize_x": "quant_rows_kernel<true, 256, 3>",
-             "quantize_dy_rows": "quant_rows_kernel<true, 256, 4>",
-             "unrotate_dx": "hadamard_kernel<false>",
-             "sgd_requant": "sgd_requant_kernel<256, 3>"}
+# Kernel symbols behind each call, as rocprofv3 names them (a call's traffic
+# is the sum over its kernels).
+KERNEL_OF = {"fwd": ["gemm_kernel<256, 256, 2, 4, 128, 1, false, false, 2>"],
+             "bwd_dx": ["gemm_kernel<256, 256, 4, 2, 128, 1, false, true, 3>"],
+             "bwd_dw": ["gemm_kernel<256, 256, 2, 4, 128, 1, true, true, 1>"],
+             "quantize_x": ["quant_rows_kernel<true, 256, 3, 128, false>"],
+             "quantize_dy": ["quant_rows_kernel<true, 256, 4, 0, true>", "grad_cols_reduce_kernel",
+                             "colquant_kernel<true>"],
+             "sgd_requant": ["sgd_requant_kernel<256, 3>"]}
 
 
 def source_digest():
@@ -62,9 +64,10 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def traffic_for(call, launches_key):
-    """Measured HBM bytes per launch from the committed counter summary, or None
-    when the summary is absent or was taken on different kernel sources."""
+def traffic_for(call):
+    """Measured HBM bytes per call (summed over its kernels) from the committed
+    counter summary, or None when the summary is absent, lacks one of the
+    kernels, or was taken on different kernel sources."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     if not os.path.exists(path):
         return None
@@ -72,10 +75,13 @@ def traffic_for(call, launches_key):
         rec = json.load(f)
     if rec.get("source_digest") != source_digest():
         return None
-    for name, ent in rec.get("kernels", {}).items():
-        if launches_key in name:
-            return ent.get("bytes_per_launch")
-    return None
+    total = 0
+    for key in KERNEL_OF.get(call, []):
+        hits = [ent for name, ent in rec.get("kernels", {}).items() if key in name]
+        if len(hits) != 1:
+            return None
+        total += hits[0].get("bytes_per_launch", 0)
+    return total or None
 
 
 def cpu_baseline(d, tokens):
@@ -197,7 +203,7 @@ def main():
     dominant = max(avg, key=avg.get)
     if dominant in GEMMS:
         ach = GEMM_OPS / (avg[dominant] * 1e-3) / 1e12
-        traffic = traffic_for(dominant, KERNEL_OF.get(dominant, dominant))
+        traffic = traffic_for(dominant)
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_INT8_TOPS,
                 "unit": "TFLOP/s", "frac": round(ach / PEAK_INT8_TOPS, 4), "traffic": traffic,
                 "kernel": dominant, "ms_per_launch": round(avg[dominant], 4)}
@@ -205,7 +211,7 @@ def main():
         ach = ALG_BYTES[dominant] / (avg[dominant] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4),
-                "traffic": traffic_for(dominant, KERNEL_OF.get(dominant, dominant)),
+                "traffic": traffic_for(dominant),
                 "kernel": dominant,
                 "ms_per_launch": round(avg[dominant], 4)}
 

@@ -116,6 +116,31 @@ int qlin_quantize_cols(const void *x, int dtype, int64_t rows, int64_t cols,
                        void *stream);
 
 /*
+ * Both quantizations of the output gradient dY in one call, reading dY twice
+ * instead of three times: the row pass of the first also gathers the column
+ * maxima and sums of the second (mini_trainer guide: the backward products
+ * are integer; the scales of each operand sit on its product's output axis).
+ * Results are those of
+ *   qlin_quantize_rows(dy, prescale = sw, had_block = 0) -> (q1, s1)   and
+ *   qlin_quantize_cols(dy, prescale = sx, col_sum)        -> (q2, s2, col_sum)
+ * bit for bit, except col_sum (fp32 sums in an unspecified order).
+ *
+ *   dy       [rows, cols] fp32 or bf16 (rows = tokens, cols = out features).
+ *   sw       [cols] fp32, the weight row scales (required).
+ *   sx       [rows] fp32, the activation row scales (required when rows > 0).
+ *   q1, s1   [rows, cols] int8 and [rows] fp32 outputs (operand of dX).
+ *   q2, s2   [rows, cols] int8 and [cols] fp32 outputs (operand of dW).  q2
+ *            also serves as scratch during the call, so it must not overlap
+ *            any other argument.
+ *   col_sum  [cols] fp32 or NULL (the bias gradient).
+ * rows >= 0 (rows == 0 writes s2 = 0 and col_sum = 0); cols in
+ * [16, QLIN_MAX_ROW], a multiple of 16; rows <= 1,048,560.
+ */
+int qlin_quantize_grad(const void *dy, int dtype, int64_t rows, int64_t cols, const float *sw,
+                       const float *sx, int8_t *q1, float *s1, int8_t *q2, float *s2,
+                       float *col_sum, void *stream);
+
+/*
  * Block-Hadamard rotation of each row (the same transform as in
  * qlin_quantize_rows).  The transform is symmetric and orthogonal, so the
  * same call maps the rotated basis back (OneTrainer PR #1681: the weight

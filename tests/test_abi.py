@@ -111,3 +111,30 @@ def test_sgd_and_hadamard_validation(L):
     assert L.qlin_hadamard(P, 0, 0, 128, 128, P, None) == 0
     assert L.qlin_quantize_cols(P, 0, 4, 16, None, Q, R, R, None) == 1   # s aliases col_sum
     assert L.qlin_quantize_cols(P, 0, 4, 20, None, Q, R, None, None) == 1
+
+
+def test_quantize_grad_validation(L):
+    _cpu_only()
+    # dy, dtype, rows, cols, sw, sx, q1, s1, q2, s2, col_sum
+    ok = (P, 0, 4, 16, Q, R, S, R + 64, 0x50000, 0x60000, 0x70000)
+    def call(**kw):
+        a = list(ok)
+        names = ["dy", "dtype", "rows", "cols", "sw", "sx", "q1", "s1", "q2", "s2", "col_sum"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return L.qlin_quantize_grad(*a, None)
+    assert call(dy=None) == 1
+    assert call(dtype=2) == 1
+    assert call(rows=-1) == 1
+    assert call(cols=24) == 1                     # not a multiple of 16
+    assert call(sw=None) == 1                     # weight scales are required
+    assert call(sx=None) == 1
+    assert call(s2=None) == 1
+    assert call(q2=P + 16) == 1                   # q2 (scratch) overlaps dy
+    assert call(q2=S) == 1                        # q2 overlaps q1
+    assert call(col_sum=0x60000) == 1             # col_sum aliases s2
+    assert call(dy=ODD) == 1
+    far = {k: (i + 1) << 32 for i, k in enumerate(["dy", "sw", "sx", "q1", "s1", "q2", "s2",
+                                                     "col_sum"])}
+    assert call(cols=131072 + 16, **far) == 2     # row longer than the row quantizer takes
+    assert call(rows=1 << 21, **far) == 2         # beyond the column pass's grid

@@ -105,6 +105,52 @@ def test_quantize_cols(T, Q, orc, rows, cols, bf16, pre):
     assert np.all(np.abs(host(cs).astype(np.float64) - csr) <= bound)
 
 
+GRAD_CASES = [
+    # rows, cols, bf16: fused pass (rows >= 512, cols <= 8192) and the fallback
+    (600, 4096, True),
+    (513, 7168, True),         # dY of the headline layer's width, few rows per group
+    (1000, 8192, False),       # widest fused row, fp32 gradient
+    (777, 4112, True),         # ragged last pass of the row workgroup
+    (700, 8208, True),         # wider than the fused pass: separate passes
+    (100, 256, False),         # too few rows for the fused pass
+]
+
+
+@pytest.mark.parametrize("rows,cols,bf16", GRAD_CASES)
+def test_quantize_grad(T, Q, orc, rows, cols, bf16):
+    rng = np.random.default_rng(rows * 7 + cols)
+    x = _x(rng, rows, cols, bf16, scale=0.01)
+    xf = workloads.bf16_bits_to_f32(x) if bf16 else x
+    if rows > 3:
+        x[2] = 0                                  # an all-zero row
+    x[:, 5] = 0                                   # and an all-zero column
+    sw = rng.uniform(1e-3, 1e-2, cols).astype(np.float32)
+    sx = rng.uniform(1e-3, 1e-1, rows).astype(np.float32)
+    announce("quantize_grad", rows, cols, bf16)
+    q1, s1, q2, s2, db = Q.qlin_quantize_grad(dev(x), dev(sw), dev(sx), want_sum=True)
+    T.cuda.synchronize()
+    q1r, s1r = orc.quantize_rows(x, prescale=sw)
+    assert_bitwise(host(s1), s1r, "row scales")
+    assert_bitwise(host(q1), q1r, "row codes")
+    q2r, s2r, dbr = orc.quantize_cols(x, prescale=sx, want_sum=True)
+    assert_bitwise(host(s2), s2r, "column scales")
+    assert_bitwise(host(q2), q2r, "column codes")
+    xf = workloads.bf16_bits_to_f32(x) if bf16 else x
+    bound = 1e-5 * np.abs(xf.astype(np.float64)).sum(axis=0) + 1e-30
+    assert np.all(np.abs(host(db).astype(np.float64) - dbr) <= bound)
+
+
+def test_quantize_grad_no_tokens(T, Q, orc):
+    cols = 64
+    announce("quantize_grad rows=0")
+    s2 = dev(np.full(cols, 7.0, np.float32))
+    db = dev(np.full(cols, 7.0, np.float32))
+    Q.qlin_quantize_grad(dev(np.zeros((0, cols), np.float32)), dev(np.ones(cols, np.float32)),
+                         dev(np.ones(0, np.float32)), s2=s2, col_sum=db)
+    T.cuda.synchronize()
+    assert np.all(host(s2) == 0) and np.all(host(db) == 0)
+
+
 @pytest.mark.parametrize("rows,cols,blk,bf16", [(3, 256, 128, False), (64, 5376, 128, False),
                                                 (5, 1024, 512, True), (7, 64, 2, False),
                                                 (9, 96, 32, True), (1, 16, 8, False),
@@ -159,6 +205,35 @@ def test_gemm_s32_extremes(T, Q, orc):
     c = Q.qlin_gemm_s32(Q.QLIN_OP_FWD, dev(a), dev(b), M, N, K)
     T.cuda.synchronize()
     assert_bitwise(host(c), orc.gemm_s32(0, a, b, M, N, K), "acc")
+
+
+@pytest.mark.parametrize("op", [0, 1, 2])
+def test_gemm_s32_longest_contraction(T, Q, orc, op):
+    """All +-127 codes at the longest contraction the ABI accepts for each
+    product (131,056 for the 16-aligned forward and dX contractions, 131,071
+    tokens for dW), where |acc| reaches 131,071 * 127^2 = 2,114,044,159, just
+    under 2^31."""
+    L = 131071 if op == 2 else 131056
+    if op == 0:
+        M, N, K = 32, 48, L
+        a, b = np.full((M, K), 127, np.int8), np.full((N, K), 127, np.int8)
+    elif op == 1:
+        M, N, K = 32, L, 48
+        a, b = np.full((M, N), 127, np.int8), np.full((N, K), 127, np.int8)
+    else:
+        M, N, K = L, 32, 48
+        a, b = np.full((M, N), 127, np.int8), np.full((M, K), 127, np.int8)
+    if op == 2:
+        a[:, 1] = -127      # output row 1 at the negative extreme
+    else:
+        a[1] = -127
+    b[0, :8] = -1           # a few small codes so outputs differ
+    announce("gemm_s32 longest contraction", op, M, N, K)
+    c = Q.qlin_gemm_s32(op, dev(a), dev(b), M, N, K)
+    T.cuda.synchronize()
+    ref = orc.gemm_s32(op, a, b, M, N, K)
+    assert np.abs(ref.astype(np.int64)).max() >= 2_000_000_000
+    assert_bitwise(host(c), ref, "acc")
 
 
 @pytest.mark.parametrize("M,N,K", PRODUCT_SHAPES)

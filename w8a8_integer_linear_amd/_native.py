@@ -26,6 +26,8 @@ SIGNATURES = {
     "qlin_abi_version": ([], _i32),
     "qlin_quantize_rows": ([_vp, _i32, _i64, _i64, _vp, _i32, _vp, _vp, _vp], _i32),
     "qlin_quantize_cols": ([_vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp], _i32),
+    "qlin_quantize_grad": ([_vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+                           _i32),
     "qlin_hadamard": ([_vp, _i32, _i64, _i64, _i32, _vp, _vp], _i32),
     "qlin_fwd": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp], _i32),
     "qlin_bwd_dx": ([_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp], _i32),
@@ -133,6 +135,33 @@ def qlin_quantize_cols(x, prescale=None, q=None, s=None, col_sum=None, want_sum=
         _ptr(x), code, rows, cols, _ptr(prescale), _ptr(q), _ptr(s), _ptr(col_sum),
         _stream(stream)))
     return (q, s, col_sum) if col_sum is not None else (q, s)
+
+
+def qlin_quantize_grad(dy, sw, sx, q1=None, s1=None, q2=None, s2=None, col_sum=None,
+                       want_sum=False, stream=None):
+    """Both quantizations of dY: (q1, s1) per row of dY * sw, (q2, s2) per column
+    of dY * sx[:, None], and optionally the column sums.  Returns
+    (q1, s1, q2, s2, col_sum)."""
+    rows, cols = dy.shape
+    _need(dy, "dy", dy.dtype)
+    code = _dtype_code(dy)
+    _need(sw, "sw", torch.float32, (cols,))
+    _need(sx, "sx", torch.float32, (rows,))
+    q1 = _empty((rows, cols), torch.int8, dy) if q1 is None else _need(q1, "q1", torch.int8,
+                                                                       (rows, cols))
+    s1 = _empty((rows,), torch.float32, dy) if s1 is None else _need(s1, "s1", torch.float32,
+                                                                     (rows,))
+    q2 = _empty((rows, cols), torch.int8, dy) if q2 is None else _need(q2, "q2", torch.int8,
+                                                                       (rows, cols))
+    s2 = _empty((cols,), torch.float32, dy) if s2 is None else _need(s2, "s2", torch.float32,
+                                                                     (cols,))
+    if col_sum is None and want_sum:
+        col_sum = _empty((cols,), torch.float32, dy)
+    _opt(col_sum, "col_sum", torch.float32, (cols,))
+    _check("qlin_quantize_grad", lib().qlin_quantize_grad(
+        _ptr(dy), code, rows, cols, _ptr(sw), _ptr(sx), _ptr(q1), _ptr(s1), _ptr(q2), _ptr(s2),
+        _ptr(col_sum), _stream(stream)))
+    return q1, s1, q2, s2, col_sum
 
 
 def qlin_hadamard(x, block, y=None, stream=None):

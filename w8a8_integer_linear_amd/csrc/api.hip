@@ -26,6 +26,16 @@ bool opt_aligned(const void *p) { return p == nullptr || aligned16(p); }
 // An array argument: non-null and 16-byte aligned unless it holds no element.
 bool array_ok(const void *p, bool nonempty) { return nonempty ? (p && aligned16(p)) : opt_aligned(p); }
 
+// Whether byte ranges [a, a + na) and [b, b + nb) intersect (empty ranges and
+// null pointers never do).
+bool overlap(const void *a, int64_t na, const void *b, int64_t nb)
+{
+    if (!a || !b || na <= 0 || nb <= 0)
+        return false;
+    const char *x = static_cast<const char *>(a), *y = static_cast<const char *>(b);
+    return x < y + nb && y < x + na;
+}
+
 // Largest token count a call accepts (grid dimensions and int32 tile indices).
 constexpr int64_t kMaxRows = (int64_t)1 << 30;
 
@@ -89,6 +99,37 @@ int qlin_quantize_cols(const void *x, int dtype, int64_t rows, int64_t cols,
         return QLIN_EUNSUPPORTED;
     qlin::launch_quantize_cols(x, dtype == QLIN_BF16, rows, cols, prescale, q, s, col_sum,
                                as_stream(stream));
+    return finish();
+}
+
+int qlin_quantize_grad(const void *dy, int dtype, int64_t rows, int64_t cols, const float *sw,
+                       const float *sx, int8_t *q1, float *s1, int8_t *q2, float *s2,
+                       float *col_sum, void *stream)
+{
+    if (!dtype_ok(dtype) || rows < 0 || !dim16(cols))
+        return QLIN_EINVAL;
+    const bool any = rows > 0;
+    if (!array_ok(dy, any) || !array_ok(q1, any) || !array_ok(q2, any) || !array_ok(s1, any) ||
+        !array_ok(sx, any) || !array_ok(sw, true) || !array_ok(s2, true) || !opt_aligned(col_sum))
+        return QLIN_EINVAL;
+    // q2 is written (as scratch, then codes) while everything else is read or
+    // written, so it overlaps nothing; s2 and col_sum are accumulators.
+    const int64_t eb = dtype == QLIN_BF16 ? 2 : 4;
+    if (any && (overlap(q2, rows * cols, dy, rows * cols * eb) ||
+                overlap(q2, rows * cols, q1, rows * cols) || overlap(q2, rows * cols, s1, rows * 4) ||
+                overlap(q2, rows * cols, sx, rows * 4) || overlap(q2, rows * cols, sw, cols * 4) ||
+                overlap(q2, rows * cols, s2, cols * 4) ||
+                overlap(q2, rows * cols, col_sum, col_sum ? cols * 4 : 0) ||
+                overlap(q1, rows * cols, dy, rows * cols * eb)))
+        return QLIN_EINVAL;
+    if (overlap(s2, cols * 4, col_sum, col_sum ? cols * 4 : 0) ||
+        (any && (overlap(s2, cols * 4, dy, rows * cols * eb) ||
+                 overlap(col_sum, col_sum ? cols * 4 : 0, dy, rows * cols * eb))))
+        return QLIN_EINVAL;
+    if (cols > QLIN_MAX_ROW || rows > 65535LL * 16)
+        return QLIN_EUNSUPPORTED;
+    qlin::launch_quantize_grad(dy, dtype == QLIN_BF16, rows, cols, sw, sx, q1, s1, q2, s2,
+                               col_sum, as_stream(stream));
     return finish();
 }
 

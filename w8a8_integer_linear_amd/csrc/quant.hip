@@ -49,15 +49,23 @@ __device__ __forceinline__ int64_t lane_chunk(int64_t c)
 // end are clamped to its last chunk and the values dropped) so that they all
 // issue back to back.  The per-column prescale of the thread's chunks is
 // loaded into registers once and reused for every row.
-template <bool BF16, int THREADS, int J, int HAD>
+//
+// COLS (no rotation, 256 threads) also gathers, over the workgroup's rows, the
+// column maxima of |x * colpre[row]| and the column sums of the raw x, and
+// writes them to part[2 * blockIdx.x][cols] and part[2 * blockIdx.x + 1][cols]
+// at the end: one read of dY serves both of its quantizations.
+template <bool BF16, int THREADS, int J, int HAD, bool COLS>
 __global__ __launch_bounds__(THREADS) void quant_rows_kernel(
     const void *__restrict__ x, int64_t rows, int64_t cols, const float *__restrict__ prescale,
-    int had, float cb, int8_t *__restrict__ q, float *__restrict__ s)
+    int had, float cb, int8_t *__restrict__ q, float *__restrict__ s,
+    const float *__restrict__ colpre, float *__restrict__ part)
 {
+    static_assert(!COLS || (HAD == 0 && THREADS == 512 && J <= 2),
+                  "column partials: no rotation, 512 threads, at most 16 columns per lane");
     // 1024-thread workgroups have 128 registers per lane: no room for the
     // prescale or the next row's data, which they load when they need it.
-    constexpr bool kKeepPrescale = THREADS <= 256;
-    constexpr bool kPrefetch = THREADS <= 256;
+    constexpr bool kKeepPrescale = THREADS <= 256 || COLS;
+    constexpr bool kPrefetch = THREADS <= 256 || COLS;
     __shared__ float red[THREADS / kWave];
     const int t = threadIdx.x;
     const int64_t nch = cols / 8;
@@ -73,6 +81,16 @@ __global__ __launch_bounds__(THREADS) void quant_rows_kernel(
 #pragma unroll
         for (int j = 0; j < J; j++)
             load8<false>(prescale, chunk(j) * 8, p[kKeepPrescale ? j : 0]);
+    }
+    float cmax[COLS ? J : 1][8], csum[COLS ? J : 1][8];
+    if constexpr (COLS) {
+#pragma unroll
+        for (int j = 0; j < J; j++)
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                cmax[j][e] = 0.0f;
+                csum[j][e] = 0.0f;
+            }
     }
     Raw8<BF16> cur[J];
     int64_t row = blockIdx.x;
@@ -94,6 +112,17 @@ __global__ __launch_bounds__(THREADS) void quant_rows_kernel(
         for (int j = 0; j < J; j++) {
             const bool ok = t + (int64_t)j * THREADS < nch;
             unpack8<BF16>(cur[j], v[j]);
+            if constexpr (COLS) {
+                if (ok) {
+                    const float cp = colpre ? colpre[row] : 1.0f;
+#pragma unroll
+                    for (int e = 0; e < 8; e++) {
+                        csum[COLS ? j : 0][e] = csum[COLS ? j : 0][e] + v[j][e];
+                        const float g = colpre ? v[j][e] * cp : v[j][e];
+                        cmax[COLS ? j : 0][e] = fmaxf(cmax[COLS ? j : 0][e], __builtin_fabsf(g));
+                    }
+                }
+            }
             // Chunk index c is the same function of the lane in every pass, so
             // lanes of one block stay together; a block is all valid or all
             // clamped because had divides cols.
@@ -147,6 +176,16 @@ __global__ __launch_bounds__(THREADS) void quant_rows_kernel(
         for (int j = 0; j < J; j++)
             cur[j] = kPrefetch ? nxt[kPrefetch ? j : 0] : load_raw8<BF16>(x, next * cols + chunk(j) * 8);
     }
+    if constexpr (COLS) {
+#pragma unroll
+        for (int j = 0; j < J; j++) {
+            const int64_t c = t + (int64_t)j * THREADS;
+            if (c < nch) {
+                store8(part + (2 * (int64_t)blockIdx.x) * cols, c * 8, cmax[j]);
+                store8(part + (2 * (int64_t)blockIdx.x + 1) * cols, c * 8, csum[j]);
+            }
+        }
+    }
 }
 
 // Workgroups per launch: enough to fill the GPU several times over; each
@@ -158,8 +197,9 @@ static void launch_rows_t(const void *x, int64_t rows, int64_t cols, const float
                           int had, float cb, int8_t *q, float *s, hipStream_t st)
 {
     const unsigned grid = (unsigned)(rows < kRowGrid ? rows : kRowGrid);
-    hipLaunchKernelGGL((quant_rows_kernel<BF16, THREADS, J, HAD>), dim3(grid), dim3(THREADS), 0,
-                       st, x, rows, cols, prescale, had, cb, q, s);
+    hipLaunchKernelGGL((quant_rows_kernel<BF16, THREADS, J, HAD, false>), dim3(grid),
+                       dim3(THREADS), 0, st, x, rows, cols, prescale, had, cb, q, s, nullptr,
+                       nullptr);
 }
 
 template <bool BF16, int HAD>
@@ -364,6 +404,95 @@ void launch_quantize_cols(const void *x, bool bf16, int64_t rows, int64_t cols,
             hipLaunchKernelGGL(colquant_kernel<false>, g2, dim3(256), 0, st, x, rows, cols,
                                prescale, s, q);
     }
+}
+
+// ------------------------------------------------ both dY quantizations
+
+// Partials from the fused row pass -> column scales s = fl(max / 127) and
+// column sums.  A workgroup owns 64 columns; its 16 waves take every 16th
+// workgroup partial and are combined through LDS (the maximum is exact in any
+// order; the sums run in a fixed order, so the result is deterministic).
+__global__ __launch_bounds__(1024) void grad_cols_reduce_kernel(const float *__restrict__ part,
+                                                                int groups, int64_t cols,
+                                                                float *__restrict__ s,
+                                                                float *__restrict__ col_sum)
+{
+    __shared__ float red_max[16][64], red_sum[16][64];
+    const int lc = threadIdx.x % 64, sl = threadIdx.x / 64;
+    const int64_t c = (int64_t)blockIdx.x * 64 + lc;
+    float m = 0.0f, sum = 0.0f;
+    if (c < cols) {
+#pragma unroll 4
+        for (int g = sl; g < groups; g += 16) {
+            m = fmaxf(m, part[(2 * (int64_t)g) * cols + c]);
+            sum = sum + part[(2 * (int64_t)g + 1) * cols + c];
+        }
+    }
+    red_max[sl][lc] = m;
+    red_sum[sl][lc] = sum;
+    __syncthreads();
+    if (sl == 0 && c < cols) {
+#pragma unroll
+        for (int i = 1; i < 16; i++) {
+            m = fmaxf(m, red_max[i][lc]);
+            sum = sum + red_sum[i][lc];
+        }
+        s[c] = m / 127.0f;
+        if (col_sum)
+            col_sum[c] = sum;
+    }
+}
+
+// The fused pass keeps the prescale and two partials per element it owns in
+// registers, so it takes rows of up to 8192 columns (2 chunks per lane at 512
+// threads).
+// Its workgroups write 8 bytes per column of partials into q2, which must
+// therefore hold at least 8 * groups * cols bytes: groups <= rows / 8.
+constexpr int64_t kGradMaxCols = 8192;
+constexpr int64_t kGradMinRows = 512;
+constexpr int kGradGroups = 512;
+
+template <bool BF16, int J>
+static void launch_grad_rows(const void *x, int64_t rows, int64_t cols, const float *sw,
+                             const float *sx, int8_t *q1, float *s1, float *part, int groups,
+                             hipStream_t st)
+{
+    hipLaunchKernelGGL((quant_rows_kernel<BF16, 512, J, 0, true>), dim3(groups), dim3(512), 0, st,
+                       x, rows, cols, sw, 0, 1.0f, q1, s1, sx, part);
+}
+
+void launch_quantize_grad(const void *x, bool bf16, int64_t rows, int64_t cols, const float *sw,
+                          const float *sx, int8_t *q1, float *s1, int8_t *q2, float *s2,
+                          float *col_sum, hipStream_t st)
+{
+    if (cols > kGradMaxCols || rows < kGradMinRows) {
+        if (rows > 0)
+            launch_quantize_rows(x, bf16, rows, cols, sw, 0, 1.0f, q1, s1, st);
+        launch_quantize_cols(x, bf16, rows, cols, sx, q2, s2, col_sum, st);
+        return;
+    }
+    const int groups = (int)(rows / 8 < kGradGroups ? rows / 8 : kGradGroups);
+    float *part = reinterpret_cast<float *>(q2);
+    const int64_t j = (cols / 8 + 511) / 512;
+    auto go = [&](auto bf) {
+        constexpr bool B = decltype(bf)::value;
+        if (j == 1)
+            launch_grad_rows<B, 1>(x, rows, cols, sw, sx, q1, s1, part, groups, st);
+        else
+            launch_grad_rows<B, 2>(x, rows, cols, sw, sx, q1, s1, part, groups, st);
+    };
+    if (bf16)
+        go(std::true_type());
+    else
+        go(std::false_type());
+    hipLaunchKernelGGL(grad_cols_reduce_kernel, dim3((unsigned)((cols + 63) / 64)), dim3(1024), 0,
+                       st, part, groups, cols, s2, col_sum);
+    dim3 g2((unsigned)((cols / 8 + 255) / 256), (unsigned)((rows + kColRows - 1) / kColRows));
+    if (bf16)
+        hipLaunchKernelGGL(colquant_kernel<true>, g2, dim3(256), 0, st, x, rows, cols, sx, s2, q2);
+    else
+        hipLaunchKernelGGL(colquant_kernel<false>, g2, dim3(256), 0, st, x, rows, cols, sx, s2,
+                           q2);
 }
 
 // --------------------------------------------------------------- rotation

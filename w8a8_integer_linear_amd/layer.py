@@ -9,8 +9,8 @@ saved INT8 input (qx, sx) of the last forward.  Buffers for up to
 Step order of one training step:
   forward   qlin_quantize_rows(x, rotate)          -> qx, sx   (saved)
             qlin_fwd(qx, sx, qw, sw, bias)         -> y
-  backward  qlin_quantize_rows(dY, prescale=sw)    -> qg1, sg1
-            qlin_quantize_cols(dY, prescale=sx)    -> qg2, sg2 (+ db)
+  backward  qlin_quantize_grad(dY, sw, sx)         -> qg1, sg1 (rows of dY*sw),
+                                                      qg2, sg2 (columns of dY*sx), db
             qlin_bwd_dx(qg1, sg1, qw, rotate back) -> dx
             qlin_bwd_dw(qg2, sg2, qx)              -> dw
   update    qlin_sgd_requant(qw, sw, dw, lr, seed, step, bias, db)
@@ -65,12 +65,10 @@ class LinearW8A8Training:
     def backward(self, dy):
         """Returns dx in the original basis; keeps dw (and db) for the update."""
         M = self.M
-        qg1, sg1 = nat.qlin_quantize_rows(dy, prescale=self.sw, q=self._qg1[:M], s=self._sg1[:M])
-        self._tick("quantize_dy_rows")
-        r = nat.qlin_quantize_cols(dy, prescale=self.sx, q=self._qg2[:M], s=self._sg2,
-                                   col_sum=self.db)
-        qg2, sg2 = r[0], r[1]
-        self._tick("quantize_dy_cols")
+        qg1, sg1, qg2, sg2, _ = nat.qlin_quantize_grad(
+            dy, self.sw, self.sx, q1=self._qg1[:M], s1=self._sg1[:M], q2=self._qg2[:M],
+            s2=self._sg2, col_sum=self.db)
+        self._tick("quantize_dy")
         dx = nat.qlin_bwd_dx(qg1, sg1, self.qw, had_block=self.had, dx=self._dx[:M])
         self._tick("bwd_dx")
         nat.qlin_bwd_dw(qg2, sg2, self.qx, dw=self.dw)
