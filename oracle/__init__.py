@@ -80,9 +80,16 @@ def lib():
         L.orc_sr_bits16.restype = ctypes.c_uint32
         L.orc_sgd_requant.argtypes = [vp, vp, vp, i64, i64, f32, u64, u64, vp, vp, vp]
         L.orc_bwd_dw_rows.argtypes = [vp, vp, vp, i64, i64, i64, vp, i64, vp]
+        L.orc_adamw_constants.argtypes = [f32, f32, f32, f32, u64, vp]
+        L.orc_adamw_constants.restype = None
+        L.orc_adamw_update.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, f32, f32, f32, f32,
+                                       u64, vp]
+        L.orc_adamw_requant.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, f32, f32, f32, f32,
+                                        u64, u64, vp, vp, vp, vp, vp]
         for name in ("orc_hadamard", "orc_quantize_rows", "orc_quantize_cols",
                      "orc_gemm_s32", "orc_gemm_s32_at", "orc_fwd", "orc_bwd_dx",
-                     "orc_bwd_dw", "orc_bwd_dw_rows", "orc_op_at", "orc_sgd_requant"):
+                     "orc_bwd_dw", "orc_bwd_dw_rows", "orc_op_at", "orc_sgd_requant",
+                     "orc_adamw_update", "orc_adamw_requant"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -273,6 +280,48 @@ def sgd_requant(qw, sw, dw, lr, seed, step, bias=None, db=None, row_ids=None):
     _chk(lib().orc_sgd_requant(_ptr(qw), _ptr(sw), _ptr(dw), N, K, float(lr), int(seed),
                                int(step), _ptr(b), _ptr(_f32(db)), _ptr(ids)))
     return qw, sw, b
+
+
+def adamw_constants(lr, beta1, beta2, weight_decay, step):
+    """(a1, a2, c1, c2, decay) as the oracle uses them (fp32 values)."""
+    k = (ctypes.c_float * 5)()
+    lib().orc_adamw_constants(ctypes.c_float(lr), ctypes.c_float(beta1), ctypes.c_float(beta2),
+                              ctypes.c_float(weight_decay), ctypes.c_uint64(step), k)
+    return tuple(np.float32(x) for x in k)
+
+
+def adamw_update(qw, sw, dw, m, v, lr, beta1, beta2, eps, weight_decay, step):
+    """The float AdamW update of the represented weight: returns (w, m, v)."""
+    qw = np.ascontiguousarray(qw, np.int8)
+    N, K = qw.shape
+    m = np.array(m, np.float32, copy=True)
+    v = np.array(v, np.float32, copy=True)
+    w = np.empty((N, K), np.float32)
+    _chk(lib().orc_adamw_update(_ptr(qw), _ptr(_f32(sw)), _ptr(_f32(dw)), _ptr(m), _ptr(v), N, K,
+                                ctypes.c_float(lr), ctypes.c_float(beta1), ctypes.c_float(beta2),
+                                ctypes.c_float(eps), ctypes.c_float(weight_decay),
+                                ctypes.c_uint64(step), _ptr(w)))
+    return w, m, v
+
+
+def adamw_requant(qw, sw, dw, m, v, lr, beta1, beta2, eps, weight_decay, seed, step,
+                  bias=None, db=None, bm=None, bv=None, row_ids=None):
+    """AdamW + stochastic requant; returns updated copies
+    (qw, sw, m, v, bias, bm, bv).  step >= 1 is AdamW's t and the Philox step."""
+    qw = np.array(qw, np.int8, copy=True, order="C")
+    sw = np.array(sw, np.float32, copy=True)
+    m = np.array(m, np.float32, copy=True)
+    v = np.array(v, np.float32, copy=True)
+    N, K = qw.shape
+    cp = lambda a: None if a is None else np.array(a, np.float32, copy=True)
+    b, bm, bv = cp(bias), cp(bm), cp(bv)
+    ids = None if row_ids is None else np.ascontiguousarray(row_ids, np.int64)
+    _chk(lib().orc_adamw_requant(_ptr(qw), _ptr(sw), _ptr(_f32(dw)), _ptr(m), _ptr(v), N, K,
+                                 ctypes.c_float(lr), ctypes.c_float(beta1), ctypes.c_float(beta2),
+                                 ctypes.c_float(eps), ctypes.c_float(weight_decay),
+                                 ctypes.c_uint64(seed), ctypes.c_uint64(step), _ptr(b),
+                                 _ptr(_f32(db)), _ptr(bm), _ptr(bv), _ptr(ids)))
+    return qw, sw, m, v, b, bm, bv
 
 
 def prepare_weight(w, had_block=0):

@@ -32,6 +32,14 @@
  *    scale, then q' = floor(y) + (u < frac(y)) with y = fl(w / s') and u a
  *    16-bit uniform from Philox4x32-10 keyed by (seed) with counter
  *    (element_index >> 3, step).
+ *  - AdamW stochastic requant (the guide lists AdamW among the update paths
+ *    with coverage on INT8 weights; its arithmetic is not given): the
+ *    published decoupled-weight-decay algorithm with bias-corrected moments,
+ *    in fp32 with host constants rounded once from double:
+ *      m' = fl(fl(b1*m) + fl(a1*g)), v' = fl(fl(b2*v) + fl(fl(a2*g)*g)),
+ *      d = fl(fl(sqrt(v')*c2) + eps), w = fl(fl(fl(s*q)*decay) - fl(c1*fl(m'/d)))
+ *    with a1 = 1-b1, a2 = 1-b2, c1 = lr/(1-b1^t), c2 = 1/sqrt(1-b2^t),
+ *    decay = 1-lr*wd, then the same row requant as SGD with Philox step t.
  *  - fp32 arithmetic: IEEE binary32, round to nearest even, no FMA
  *    contraction (built with -ffp-contract=off), IEEE division.
  *
@@ -479,6 +487,40 @@ uint32_t orc_sr_bits16(uint64_t seed, uint64_t step, uint64_t i)
     return (word >> (16 * (i & 1))) & 0xFFFFu;
 }
 
+/* Stochastic requant of one updated row w [K] (the tail shared by the SGD and
+ * AdamW updates): s' = fl(amax / 127) (0 for an all-zero row), y = fl(w / s'),
+ * q' = clamp(floor(y) + (u < y - floor(y)), -127, 127) with u the 16-bit
+ * Philox uniform of global element index grow * K + j. */
+static float requant_row(const float *w, int64_t K, int64_t grow, uint64_t seed,
+                         uint64_t step, int8_t *q)
+{
+    float amax = 0.0f;
+    for (int64_t j = 0; j < K; j++) {
+        float a = fabsf(w[j]);
+        if (a > amax)
+            amax = a;
+    }
+    float s_new = amax == 0.0f ? 0.0f : amax / 127.0f;
+    for (int64_t j = 0; j < K; j++) {
+        int8_t code = 0;
+        if (s_new != 0.0f) {
+            float y = w[j] / s_new;
+            float f = floorf(y);
+            float frac = y - f;
+            float u = (float)orc_sr_bits16(seed, step, (uint64_t)(grow * K + j)) *
+                      (1.0f / 65536.0f);
+            float v = f + (u < frac ? 1.0f : 0.0f);
+            if (v > 127.0f)
+                v = 127.0f;
+            if (v < -127.0f)
+                v = -127.0f;
+            code = (int8_t)v;
+        }
+        q[j] = code;
+    }
+    return s_new;
+}
+
 /* --------------------------------------- SGD with stochastic requantization */
 
 /* One plain SGD step on the represented weight, then stochastic requant of
@@ -499,40 +541,97 @@ int orc_sgd_requant(int8_t *qw, float *sw, const float *dw, int64_t N, int64_t K
 #pragma omp for schedule(static)
         for (int64_t n = 0; n < N; n++) {
             float s = sw[n];
-            float amax = 0.0f;
             for (int64_t j = 0; j < K; j++) {
                 float cur = s * (float)qw[n * K + j];
                 float upd = lr * dw[n * K + j];
                 w[j] = cur - upd;
-                float a = fabsf(w[j]);
-                if (a > amax)
-                    amax = a;
             }
-            float s_new = amax == 0.0f ? 0.0f : amax / 127.0f;
-            for (int64_t j = 0; j < K; j++) {
-                int8_t code = 0;
-                if (s_new != 0.0f) {
-                    float y = w[j] / s_new;
-                    float f = floorf(y);
-                    float frac = y - f;
-                    int64_t gn = row_ids ? row_ids[n] : n;
-                    float u = (float)orc_sr_bits16(seed, step, (uint64_t)(gn * K + j)) *
-                              (1.0f / 65536.0f);
-                    float v = f + (u < frac ? 1.0f : 0.0f);
-                    if (v > 127.0f)
-                        v = 127.0f;
-                    if (v < -127.0f)
-                        v = -127.0f;
-                    code = (int8_t)v;
-                }
-                qw[n * K + j] = code;
-            }
-            sw[n] = s_new;
+            sw[n] = requant_row(w, K, row_ids ? row_ids[n] : n, seed, step, qw + n * K);
         }
         free(w);
     }
     if (bias && db)
         for (int64_t n = 0; n < N; n++)
             bias[n] = bias[n] - lr * db[n];
+    return ORC_OK;
+}
+
+/* ------------------------------------- AdamW with stochastic requantization */
+
+/* Step-dependent constants of AdamW, each computed in double from the fp32
+ * hyperparameters and rounded once to fp32 (t >= 1):
+ * k[0] = a1 = 1 - b1, k[1] = a2 = 1 - b2, k[2] = c1 = lr / (1 - b1^t),
+ * k[3] = c2 = 1 / sqrt(1 - b2^t), k[4] = decay = 1 - lr * wd. */
+void orc_adamw_constants(float lr, float b1, float b2, float wd, uint64_t t, float k[5])
+{
+    double db1 = b1, db2 = b2, dt = (double)t;
+    k[0] = (float)(1.0 - db1);
+    k[1] = (float)(1.0 - db2);
+    k[2] = (float)((double)lr / (1.0 - pow(db1, dt)));
+    k[3] = (float)(1.0 / sqrt(1.0 - pow(db2, dt)));
+    k[4] = (float)(1.0 - (double)lr * (double)wd);
+}
+
+/* One AdamW update of n float parameters p (in place), with moments m, v (in
+ * place) and gradient g, in the order given in the header. */
+static void adamw_elems(float *p, float *m, float *v, const float *g, int64_t n, float b1,
+                        float b2, float eps, const float k[5])
+{
+    for (int64_t j = 0; j < n; j++) {
+        float mj = b1 * m[j] + k[0] * g[j];
+        float vj = b2 * v[j] + (k[1] * g[j]) * g[j];
+        float d = sqrtf(vj) * k[3] + eps;
+        p[j] = p[j] * k[4] - k[2] * (mj / d);
+        m[j] = mj;
+        v[j] = vj;
+    }
+}
+
+/* The float update alone on the represented weight w = fl(s * q): writes the
+ * updated w [N, K] and moments (test hook for pinning against a reference
+ * AdamW on the same starting point). */
+int orc_adamw_update(const int8_t *qw, const float *sw, const float *dw, float *m, float *v,
+                     int64_t N, int64_t K, float lr, float b1, float b2, float eps, float wd,
+                     uint64_t t, float *w)
+{
+    if (N < 0 || K < 1 || t < 1)
+        return ORC_EINVAL;
+    float k[5];
+    orc_adamw_constants(lr, b1, b2, wd, t, k);
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t j = 0; j < K; j++)
+            w[n * K + j] = sw[n] * (float)qw[n * K + j];
+        adamw_elems(w + n * K, m + n * K, v + n * K, dw + n * K, K, b1, b2, eps, k);
+    }
+    return ORC_OK;
+}
+
+/* AdamW step on the represented weight, then the stochastic requant of each
+ * row (Philox step = t).  In place on qw, sw, m, v; the float bias, when
+ * given with db and its moments bm, bv, takes the same float update. */
+int orc_adamw_requant(int8_t *qw, float *sw, const float *dw, float *m, float *v, int64_t N,
+                      int64_t K, float lr, float b1, float b2, float eps, float wd,
+                      uint64_t seed, uint64_t t, float *bias, const float *db, float *bm,
+                      float *bv, const int64_t *row_ids)
+{
+    if (N < 0 || K < 1 || t < 1)
+        return ORC_EINVAL;
+    float k[5];
+    orc_adamw_constants(lr, b1, b2, wd, t, k);
+#pragma omp parallel
+    {
+        float *w = (float *)malloc((size_t)K * sizeof(float));
+#pragma omp for schedule(static)
+        for (int64_t n = 0; n < N; n++) {
+            for (int64_t j = 0; j < K; j++)
+                w[j] = sw[n] * (float)qw[n * K + j];
+            adamw_elems(w, m + n * K, v + n * K, dw + n * K, K, b1, b2, eps, k);
+            sw[n] = requant_row(w, K, row_ids ? row_ids[n] : n, seed, t, qw + n * K);
+        }
+        free(w);
+    }
+    if (bias && db && bm && bv)
+        adamw_elems(bias, bm, bv, db, N, b1, b2, eps, k);
     return ORC_OK;
 }
