@@ -41,6 +41,8 @@ ALG_BYTES = {
     "quantize_x": M * K * 2 + M * K + 4 * M,
     "quantize_dy": 2 * (M * N * 2) + 2 * (M * N) + 8 * M + 8 * N,
     "sgd_requant": N * K * (1 + 4 + 1) + 8 * N,
+    # AdamW: codes in and out, gradient in, both fp32 moments in and out.
+    "adamw_requant": N * K * (1 + 4 + 8 + 8 + 1) + 8 * N,
 }
 GEMMS = ("fwd", "bwd_dx", "bwd_dw")
 COPY_BYTES = 512 << 20        # calibration copy: reads and writes this many bytes
@@ -229,6 +231,23 @@ def main():
         "roofline": roof,
         "breakdown": breakdown,
     }
+    # Outside the timed step: the AdamW update on the same weight (the second
+    # optimizer of the update row), timed over a few calls after the step.
+    layer.timer = None
+    layer.adamw_step(LR, SEED, 1, weight_decay=0.01)
+    torch.cuda.synchronize()
+    a_begin = torch.cuda.Event(enable_timing=True)
+    a_end = torch.cuda.Event(enable_timing=True)
+    a_begin.record(stream)
+    for t in range(2, 12):
+        layer.adamw_step(LR, SEED, t, weight_decay=0.01)
+    a_end.record(stream)
+    torch.cuda.synchronize()
+    a_ms = a_begin.elapsed_time(a_end) / 10
+    a_gbs = ALG_BYTES["adamw_requant"] / (a_ms * 1e-3) / 1e9
+    out["extras"] = {"adamw_requant": {"ms": round(a_ms, 4), "gbs": round(a_gbs, 1),
+                                       "frac_hbm": round(a_gbs / PEAK_HBM_GBS, 4),
+                                       "shape": [N, K]}}
     if args.cpu_tokens > 0:
         print(f"[bench] cpu baseline on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(d, args.cpu_tokens)

@@ -213,6 +213,35 @@ int qlin_sgd_requant(int8_t *qw, float *sw, const float *dw, int64_t N, int64_t 
                      void *stream);
 
 /*
+ * AdamW step on the represented weight followed by the same stochastic
+ * requantization of each row (mini_trainer guide, feature table: AdamW is
+ * among the update paths covered on INT8 weights; update paragraph: updates
+ * stochastically requantize the represented weight, no float master weight).
+ * The guide gives no arithmetic; this is the published decoupled-weight-decay
+ * algorithm with bias-corrected moments, in fp32:
+ *   m' = fl(fl(b1*m) + fl(a1*g)),  v' = fl(fl(b2*v) + fl(fl(a2*g)*g)),
+ *   d  = fl(fl(sqrt(v')*c2) + eps),
+ *   w  = fl(fl(fl(s*q)*decay) - fl(c1*fl(m'/d)))
+ * with constants computed in double from the fp32 arguments and rounded once:
+ * a1 = 1-b1, a2 = 1-b2, c1 = lr/(1-b1^t), c2 = 1/sqrt(1-b2^t),
+ * decay = 1-lr*weight_decay (t = step).  The row is then requantized exactly
+ * as by qlin_sgd_requant with Philox step = step.
+ *
+ *   qw, sw   in/out as in qlin_sgd_requant; dw [N, K] fp32 gradient.
+ *   m, v     [N, K] fp32 moments, in/out (zero before the first step); they
+ *            must not overlap each other or dw.
+ *   step     t >= 1, the AdamW step count and the Philox step.
+ *   beta1, beta2 in [0, 1); eps > 0; weight_decay >= 0; all finite.
+ *   bias, db, bias_m, bias_v: all four or none; the float bias [N] takes the
+ *            same float update with its own moments [N].
+ * N >= 0; K a multiple of 16, at most QLIN_MAX_ROW.
+ */
+int qlin_adamw_requant(int8_t *qw, float *sw, const float *dw, float *m, float *v, int64_t N,
+                       int64_t K, float lr, float beta1, float beta2, float eps,
+                       float weight_decay, uint64_t seed, uint64_t step, float *bias,
+                       const float *db, float *bias_m, float *bias_v, void *stream);
+
+/*
  * Raw int32 accumulators of one of the three products (same kernels as the
  * fused calls, no dequant), for exact verification.  op is QLIN_OP_FWD,
  * QLIN_OP_DX or QLIN_OP_DW; a, b and the shape arguments mean what they mean

@@ -138,3 +138,29 @@ def test_quantize_grad_validation(L):
                                                      "col_sum"])}
     assert call(cols=131072 + 16, **far) == 2     # row longer than the row quantizer takes
     assert call(rows=1 << 21, **far) == 2         # beyond the column pass's grid
+
+
+def test_adamw_validation(L):
+    _cpu_only()
+    # qw, sw, dw, m, v, N, K, lr, b1, b2, eps, wd, seed, step, bias, db, bm, bv
+    base = [P, Q, R, S, 0x50000, 4, 16, 1e-3, 0.9, 0.999, 1e-8, 0.01, 0, 1, None, None, None,
+            None]
+    names = ["qw", "sw", "dw", "m", "v", "N", "K", "lr", "b1", "b2", "eps", "wd", "seed", "step",
+             "bias", "db", "bm", "bv"]
+    def call(**kw):
+        a = list(base)
+        for k, val in kw.items():
+            a[names.index(k)] = val
+        return L.qlin_adamw_requant(*a, None)
+    assert call(step=0) == 1                      # steps count from 1
+    assert call(b1=1.0) == 1
+    assert call(b2=-0.1) == 1
+    assert call(eps=0.0) == 1
+    assert call(wd=-1.0) == 1
+    assert call(lr=float("nan")) == 1
+    assert call(K=24) == 1
+    assert call(m=None) == 1
+    assert call(v=S + 16) == 1                    # moments overlap
+    assert call(bias=0x60000) == 1                # bias without db and its moments
+    assert call(bias=0x60000, db=0x70000, bm=0x80000) == 1
+    assert call(N=0, qw=None, dw=None, m=None, v=None) == 0

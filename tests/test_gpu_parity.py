@@ -333,6 +333,47 @@ def test_sgd_requant(T, Q, orc, N, K, with_bias):
             assert_bitwise(host(bd), br, "bias")
 
 
+ADAMW_CASES = [(128, 256, True), (64, 5376, False), (7, 16, True), (3, 20480, False),
+               (5, 14336, True)]
+
+
+@pytest.mark.parametrize("N,K,with_bias", ADAMW_CASES)
+def test_adamw_requant(T, Q, orc, N, K, with_bias):
+    """Three chained AdamW steps; each step's inputs on the oracle side are the
+    oracle's own previous outputs."""
+    rng = np.random.default_rng(N * K + 3)
+    qw = _codes(rng, (N, K))
+    qw[:, 0] = 127
+    sw = rng.uniform(1e-4, 1e-2, N).astype(np.float32)
+    m = np.zeros((N, K), np.float32)
+    v = np.zeros((N, K), np.float32)
+    bias = rng.standard_normal(N).astype(np.float32) if with_bias else None
+    bm = np.zeros(N, np.float32) if with_bias else None
+    bv = np.zeros(N, np.float32) if with_bias else None
+    d = {k: (None if a is None else dev(a)) for k, a in
+         dict(qw=qw, sw=sw, m=m, v=v, bias=bias, bm=bm, bv=bv).items()}
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    for t in (1, 2, 3):
+        g = (rng.standard_normal((N, K)) * 10.0 ** rng.uniform(-3, 1)).astype(np.float32)
+        db = rng.standard_normal(N).astype(np.float32) if with_bias else None
+        announce("adamw_requant", N, K, with_bias, t)
+        Q.qlin_adamw_requant(d["qw"], d["sw"], dev(g), d["m"], d["v"], seed=13, step=t,
+                             bias=d["bias"], db=None if db is None else dev(db),
+                             bias_m=d["bm"], bias_v=d["bv"], **hp)
+        T.cuda.synchronize()
+        qw, sw, m, v, bias, bm, bv = orc.adamw_requant(
+            qw, sw, g, m, v, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"],
+            13, t, bias=bias, db=db, bm=bm, bv=bv)
+        assert_bitwise(host(d["m"]), m, f"m step {t}")
+        assert_bitwise(host(d["v"]), v, f"v step {t}")
+        assert_bitwise(host(d["sw"]), sw, f"scales step {t}")
+        assert_bitwise(host(d["qw"]), qw, f"codes step {t}")
+        if with_bias:
+            assert_bitwise(host(d["bias"]), bias, f"bias step {t}")
+            assert_bitwise(host(d["bm"]), bm, f"bias m step {t}")
+            assert_bitwise(host(d["bv"]), bv, f"bias v step {t}")
+
+
 def test_sgd_zero_rows(T, Q, orc):
     N, K = 4, 64
     qw = np.zeros((N, K), np.int8)

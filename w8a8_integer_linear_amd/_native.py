@@ -33,6 +33,8 @@ SIGNATURES = {
     "qlin_bwd_dx": ([_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp], _i32),
     "qlin_bwd_dw": ([_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp], _i32),
     "qlin_sgd_requant": ([_vp, _vp, _vp, _i64, _i64, _f32, _u64, _u64, _vp, _vp, _vp], _i32),
+    "qlin_adamw_requant": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _f32, _f32, _f32, _f32,
+                            _u64, _u64, _vp, _vp, _vp, _vp, _vp], _i32),
     "qlin_gemm_s32": ([_i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp], _i32),
 }
 
@@ -226,6 +228,24 @@ def qlin_sgd_requant(qw, sw, dw, lr, seed, step, bias=None, db=None, stream=None
     _check("qlin_sgd_requant", lib().qlin_sgd_requant(
         _ptr(qw), _ptr(sw), _ptr(dw), N, K, float(lr), int(seed), int(step), _ptr(bias),
         _ptr(db), _stream(stream)))
+    return qw, sw
+
+
+def qlin_adamw_requant(qw, sw, dw, m, v, lr, beta1, beta2, eps, weight_decay, seed, step,
+                       bias=None, db=None, bias_m=None, bias_v=None, stream=None):
+    """In place on qw, sw, m, v (and bias, bias_m, bias_v).  step >= 1."""
+    N, K = qw.shape
+    _need(qw, "qw", torch.int8)
+    _need(sw, "sw", torch.float32, (N,))
+    _need(dw, "dw", torch.float32, (N, K))
+    _need(m, "m", torch.float32, (N, K))
+    _need(v, "v", torch.float32, (N, K))
+    for t, name in ((bias, "bias"), (db, "db"), (bias_m, "bias_m"), (bias_v, "bias_v")):
+        _opt(t, name, torch.float32, (N,))
+    _check("qlin_adamw_requant", lib().qlin_adamw_requant(
+        _ptr(qw), _ptr(sw), _ptr(dw), _ptr(m), _ptr(v), N, K, float(lr), float(beta1),
+        float(beta2), float(eps), float(weight_decay), int(seed), int(step), _ptr(bias),
+        _ptr(db), _ptr(bias_m), _ptr(bias_v), _stream(stream)))
     return qw, sw
 
 

@@ -265,4 +265,45 @@ int qlin_sgd_requant(int8_t *qw, float *sw, const float *dw, int64_t N, int64_t 
     return finish();
 }
 
+int qlin_adamw_requant(int8_t *qw, float *sw, const float *dw, float *m, float *v, int64_t N,
+                       int64_t K, float lr, float beta1, float beta2, float eps,
+                       float weight_decay, uint64_t seed, uint64_t step, float *bias,
+                       const float *db, float *bias_m, float *bias_v, void *stream)
+{
+    if (N < 0 || !dim16(K) || step < 1)
+        return QLIN_EINVAL;
+    const bool any = N > 0;
+    if (!array_ok(qw, any) || !array_ok(dw, any) || !array_ok(m, any) || !array_ok(v, any) ||
+        (any && !sw))
+        return QLIN_EINVAL;
+    const int nb = (bias != nullptr) + (db != nullptr) + (bias_m != nullptr) + (bias_v != nullptr);
+    if (nb != 0 && nb != 4)
+        return QLIN_EINVAL;
+    if (!isfinite(lr) || !isfinite(eps) || !(eps > 0.0f) || !isfinite(weight_decay) ||
+        !(weight_decay >= 0.0f) || !(beta1 >= 0.0f && beta1 < 1.0f) ||
+        !(beta2 >= 0.0f && beta2 < 1.0f))
+        return QLIN_EINVAL;
+    if (any && (overlap(m, N * K * 4, v, N * K * 4) || overlap(m, N * K * 4, dw, N * K * 4) ||
+                overlap(v, N * K * 4, dw, N * K * 4)))
+        return QLIN_EINVAL;
+    if (K > QLIN_MAX_ROW || N > kMaxRows)
+        return QLIN_EUNSUPPORTED;
+    if (N == 0)
+        return QLIN_OK;
+    // Step constants, each computed in double and rounded once.
+    const double b1 = beta1, b2 = beta2, t = (double)step;
+    qlin::AdamConsts k;
+    k.b1 = beta1;
+    k.b2 = beta2;
+    k.eps = eps;
+    k.a1 = (float)(1.0 - b1);
+    k.a2 = (float)(1.0 - b2);
+    k.c1 = (float)((double)lr / (1.0 - pow(b1, t)));
+    k.c2 = (float)(1.0 / sqrt(1.0 - pow(b2, t)));
+    k.decay = (float)(1.0 - (double)lr * (double)weight_decay);
+    qlin::launch_adamw_requant(qw, sw, dw, m, v, N, K, k, seed, step, bias, db, bias_m, bias_v,
+                               as_stream(stream));
+    return finish();
+}
+
 } // extern "C"

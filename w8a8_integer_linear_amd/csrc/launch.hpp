@@ -46,4 +46,13 @@ void launch_sgd_requant(int8_t *qw, float *sw, const float *dw, int64_t N, int64
                         uint64_t seed, uint64_t step, float *bias, const float *db,
                         hipStream_t st);
 
+// AdamW hyperparameters and the step constants derived from them on the host.
+struct AdamConsts {
+    float b1, b2, eps, a1, a2, c1, c2, decay;
+};
+
+void launch_adamw_requant(int8_t *qw, float *sw, const float *dw, float *m, float *v, int64_t N,
+                          int64_t K, const AdamConsts &k, uint64_t seed, uint64_t step,
+                          float *bias, const float *db, float *bm, float *bv, hipStream_t st);
+
 } // namespace qlin

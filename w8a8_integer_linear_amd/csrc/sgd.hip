@@ -1,8 +1,9 @@
-// Fused SGD step with stochastic requantization of each weight row
+// Fused SGD and AdamW steps with stochastic requantization of each weight row
 // (mini_trainer guide: updates stochastically requantize the represented
 // weight; no floating master weight is retained; row kernels fuse the
-// update).  One workgroup per row; the updated row lives only in registers
-// between the absmax reduction and the rounding.
+// update; AdamW is among the covered update paths).  One workgroup per row;
+// the updated row lives only in registers between the absmax reduction and
+// the rounding.  AdamW reads and writes its fp32 moments in the same pass.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -33,11 +34,30 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32
     }
 }
 
-template <int THREADS, int J>
+// AdamW state and step constants (computed on the host, each rounded once
+// from double): a1 = 1 - b1, a2 = 1 - b2, c1 = lr / (1 - b1^t),
+// c2 = 1 / sqrt(1 - b2^t), decay = 1 - lr * wd.
+struct AdamParams {
+    float *m, *v;          // [N, K] moments
+    float *bm, *bv;        // [N] bias moments (with bias and db)
+    float b1, b2, eps, a1, a2, c1, c2, decay;
+};
+
+// One AdamW element update: moments in place, returns the updated weight.
+__device__ __forceinline__ float adamw_elem(const AdamParams &a, float w0, float g, float &m,
+                                            float &v)
+{
+    m = a.b1 * m + a.a1 * g;
+    v = a.b2 * v + (a.a2 * g) * g;
+    const float d = __builtin_sqrtf(v) * a.c2 + a.eps;
+    return w0 * a.decay - a.c1 * (m / d);
+}
+
+template <int THREADS, int J, bool ADAM>
 __global__ __launch_bounds__(THREADS) void sgd_requant_kernel(
     int8_t *__restrict__ qw, float *__restrict__ sw, const float *__restrict__ dw, int64_t K,
     float lr, uint32_t seed_lo, uint32_t seed_hi, uint32_t step_lo, uint32_t step_hi,
-    float *__restrict__ bias, const float *__restrict__ db)
+    float *__restrict__ bias, const float *__restrict__ db, AdamParams ap)
 {
     __shared__ float red[THREADS / kWave];
     const int64_t row = blockIdx.x;
@@ -52,15 +72,27 @@ __global__ __launch_bounds__(THREADS) void sgd_requant_kernel(
         const int64_t c = t + (int64_t)j * THREADS;
         if (c < nch) {
             const i32x2 qv = *reinterpret_cast<const i32x2 *>(qw + base + c * 8);
-            float d[8];
+            float d[8], m[8], v[8];
             load8<false>(dw, base + c * 8, d);
+            if constexpr (ADAM) {
+                load8<false>(ap.m, base + c * 8, m);
+                load8<false>(ap.v, base + c * 8, v);
+            }
 #pragma unroll
             for (int e = 0; e < 8; e++) {
                 const int code = (int)(int8_t)((uint32_t)qv[e / 4] >> (8 * (e % 4)));
                 const float cur = s * (float)code;
-                const float upd = lr * d[e];
-                w[j][e] = cur - upd;
+                if constexpr (ADAM) {
+                    w[j][e] = adamw_elem(ap, cur, d[e], m[e], v[e]);
+                } else {
+                    const float upd = lr * d[e];
+                    w[j][e] = cur - upd;
+                }
                 amax = fmaxf(amax, __builtin_fabsf(w[j][e]));
+            }
+            if constexpr (ADAM) {
+                store8(ap.m, base + c * 8, m);
+                store8(ap.v, base + c * 8, v);
             }
         } else {
 #pragma unroll
@@ -107,18 +139,55 @@ __global__ __launch_bounds__(THREADS) void sgd_requant_kernel(
     }
     if (t == 0) {
         sw[row] = s2;
-        if (bias && db)
+        if constexpr (ADAM) {
+            if (bias && db && ap.bm && ap.bv) {
+                float m = ap.bm[row], v = ap.bv[row];
+                bias[row] = adamw_elem(ap, bias[row], db[row], m, v);
+                ap.bm[row] = m;
+                ap.bv[row] = v;
+            }
+        } else if (bias && db) {
             bias[row] = bias[row] - lr * db[row];
+        }
     }
 }
 
-template <int THREADS, int J>
+template <int THREADS, int J, bool ADAM>
 void launch_t(int8_t *qw, float *sw, const float *dw, int64_t N, int64_t K, float lr,
-              uint64_t seed, uint64_t step, float *bias, const float *db, hipStream_t st)
+              uint64_t seed, uint64_t step, float *bias, const float *db, const AdamParams &ap,
+              hipStream_t st)
 {
-    hipLaunchKernelGGL((sgd_requant_kernel<THREADS, J>), dim3((unsigned)N), dim3(THREADS), 0, st,
-                       qw, sw, dw, K, lr, (uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)step,
-                       (uint32_t)(step >> 32), bias, db);
+    hipLaunchKernelGGL((sgd_requant_kernel<THREADS, J, ADAM>), dim3((unsigned)N), dim3(THREADS),
+                       0, st, qw, sw, dw, K, lr, (uint32_t)seed, (uint32_t)(seed >> 32),
+                       (uint32_t)step, (uint32_t)(step >> 32), bias, db, ap);
+}
+
+template <bool ADAM>
+void launch_update(int8_t *qw, float *sw, const float *dw, int64_t N, int64_t K, float lr,
+                   uint64_t seed, uint64_t step, float *bias, const float *db,
+                   const AdamParams &ap, hipStream_t st)
+{
+    const int64_t nch = K / 8;
+    const int64_t j256 = (nch + 255) / 256;
+#define QLIN_LAUNCH(T, J) return launch_t<T, J, ADAM>(qw, sw, dw, N, K, lr, seed, step, bias, db, ap, st)
+    switch (j256) {
+    case 1: QLIN_LAUNCH(256, 1);
+    case 2: QLIN_LAUNCH(256, 2);
+    case 3: QLIN_LAUNCH(256, 3);
+    case 4: QLIN_LAUNCH(256, 4);
+    case 5: QLIN_LAUNCH(256, 5);
+    case 6: QLIN_LAUNCH(256, 6);
+    case 7: QLIN_LAUNCH(256, 7);
+    case 8: QLIN_LAUNCH(256, 8);
+    default: break;
+    }
+    const int64_t j1024 = (nch + 1023) / 1024;
+    if (j1024 <= 4)
+        QLIN_LAUNCH(1024, 4);
+    if (j1024 <= 8)
+        QLIN_LAUNCH(1024, 8);
+    QLIN_LAUNCH(1024, 16);
+#undef QLIN_LAUNCH
 }
 
 } // namespace
@@ -127,25 +196,15 @@ void launch_sgd_requant(int8_t *qw, float *sw, const float *dw, int64_t N, int64
                         uint64_t seed, uint64_t step, float *bias, const float *db,
                         hipStream_t st)
 {
-    const int64_t nch = K / 8;
-    const int64_t j256 = (nch + 255) / 256;
-    switch (j256) {
-    case 1: return launch_t<256, 1>(qw, sw, dw, N, K, lr, seed, step, bias, db, st);
-    case 2: return launch_t<256, 2>(qw, sw, dw, N, K, lr, seed, step, bias, db, st);
-    case 3: return launch_t<256, 3>(qw, sw, dw, N, K, lr, seed, step, bias, db, st);
-    case 4: return launch_t<256, 4>(qw, sw, dw, N, K, lr, seed, step, bias, db, st);
-    case 5: return launch_t<256, 5>(qw, sw, dw, N, K, lr, seed, step, bias, db, st);
-    case 6: return launch_t<256, 6>(qw, sw, dw, N, K, lr, seed, step, bias, db, st);
-    case 7: return launch_t<256, 7>(qw, sw, dw, N, K, lr, seed, step, bias, db, st);
-    case 8: return launch_t<256, 8>(qw, sw, dw, N, K, lr, seed, step, bias, db, st);
-    default: break;
-    }
-    const int64_t j1024 = (nch + 1023) / 1024;
-    if (j1024 <= 4)
-        return launch_t<1024, 4>(qw, sw, dw, N, K, lr, seed, step, bias, db, st);
-    if (j1024 <= 8)
-        return launch_t<1024, 8>(qw, sw, dw, N, K, lr, seed, step, bias, db, st);
-    return launch_t<1024, 16>(qw, sw, dw, N, K, lr, seed, step, bias, db, st);
+    launch_update<false>(qw, sw, dw, N, K, lr, seed, step, bias, db, AdamParams{}, st);
+}
+
+void launch_adamw_requant(int8_t *qw, float *sw, const float *dw, float *m, float *v, int64_t N,
+                          int64_t K, const AdamConsts &k, uint64_t seed, uint64_t step,
+                          float *bias, const float *db, float *bm, float *bv, hipStream_t st)
+{
+    AdamParams ap{m, v, bm, bv, k.b1, k.b2, k.eps, k.a1, k.a2, k.c1, k.c2, k.decay};
+    launch_update<true>(qw, sw, dw, N, K, 0.0f, seed, step, bias, db, ap, st);
 }
 
 } // namespace qlin

@@ -79,6 +79,23 @@ class LinearW8A8Training:
         nat.qlin_sgd_requant(self.qw, self.sw, self.dw, lr, seed, step, bias=self.bias, db=self.db)
         self._tick("sgd_requant")
 
+    def adamw_step(self, lr, seed, step, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0):
+        """AdamW update + stochastic requant (step >= 1).  The fp32 moments (and
+        the bias moments) are allocated, zeroed, on the first call."""
+        if getattr(self, "_m", None) is None:
+            self._m = torch.zeros_like(self.dw)
+            self._v = torch.zeros_like(self.dw)
+            if self.bias is not None:
+                self._bm = torch.zeros_like(self.bias)
+                self._bv = torch.zeros_like(self.bias)
+        has_b = self.bias is not None
+        nat.qlin_adamw_requant(self.qw, self.sw, self.dw, self._m, self._v, lr, betas[0],
+                               betas[1], eps, weight_decay, seed, step,
+                               bias=self.bias, db=self.db if has_b else None,
+                               bias_m=self._bm if has_b else None,
+                               bias_v=self._bv if has_b else None)
+        self._tick("adamw_requant")
+
     def _tick(self, label):
         if self.timer is not None:
             self.timer(label)
