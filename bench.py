@@ -108,6 +108,46 @@ def cpu_baseline(d, tokens):
                       f"(SGD requant over the whole weight), {t:.2f} s"}
 
 
+def skinny_forward(torch, reps=240, copies=24):
+    """The weight-streaming forward for M <= 16 rows (4096 -> 4096, no rotation,
+    seeded inputs of the skinny workload): HBM GB/s per call, where a call moves
+    the weight once plus the small activation and output arrays.  Calls cycle
+    through `copies` copies of the weight (403 MB, more than the 256 MB
+    infinity cache), so each call streams its weight from HBM."""
+    import numpy as np
+
+    import workloads
+    from w8a8_integer_linear_amd import _native as nat
+    res = {}
+    for m in (1, 4, 16):
+        d = workloads.skinny(m)
+        kk = d["w"].shape[1]
+        nn = d["w"].shape[0]
+        x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).cuda()
+        w = torch.from_numpy(d["w"]).cuda()
+        qw, sw = nat.qlin_quantize_rows(w)
+        qws = [qw.clone() for _ in range(copies)]
+        qx, sx = nat.qlin_quantize_rows(x)
+        y = torch.empty((m, nn), dtype=torch.float32, device="cuda")
+        for i in range(copies):
+            nat.qlin_fwd(qx, sx, qws[i], sw, y=y)
+        torch.cuda.synchronize()
+        b = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        b.record()
+        for i in range(reps):
+            nat.qlin_fwd(qx, sx, qws[i % copies], sw, y=y)
+        e.record()
+        torch.cuda.synchronize()
+        ms = b.elapsed_time(e) / reps
+        nbytes = nn * kk + m * kk + 4 * (m + nn) + 4 * m * nn
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[f"skinny_fwd_m{m}"] = {"ms": round(ms, 5), "gbs": round(gbs, 1),
+                                   "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                                   "shape": [m, kk, nn]}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -248,6 +288,7 @@ def main():
     out["extras"] = {"adamw_requant": {"ms": round(a_ms, 4), "gbs": round(a_gbs, 1),
                                        "frac_hbm": round(a_gbs / PEAK_HBM_GBS, 4),
                                        "shape": [N, K]}}
+    out["extras"].update(skinny_forward(torch))
     if args.cpu_tokens > 0:
         print(f"[bench] cpu baseline on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(d, args.cpu_tokens)
