@@ -80,6 +80,7 @@ def lib():
         L.orc_sr_bits16.restype = ctypes.c_uint32
         L.orc_sgd_requant.argtypes = [vp, vp, vp, i64, i64, f32, u64, u64, vp, vp, vp]
         L.orc_bwd_dw_rows.argtypes = [vp, vp, vp, i64, i64, i64, vp, i64, vp]
+        L.orc_dequantize_weight.argtypes = [vp, vp, i64, i64, i32, vp]
         L.orc_adamw_constants.argtypes = [f32, f32, f32, f32, u64, vp]
         L.orc_adamw_constants.restype = None
         L.orc_adamw_update.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, f32, f32, f32, f32,
@@ -89,7 +90,7 @@ def lib():
         for name in ("orc_hadamard", "orc_quantize_rows", "orc_quantize_cols",
                      "orc_gemm_s32", "orc_gemm_s32_at", "orc_fwd", "orc_bwd_dx",
                      "orc_bwd_dw", "orc_bwd_dw_rows", "orc_op_at", "orc_sgd_requant",
-                     "orc_adamw_update", "orc_adamw_requant"):
+                     "orc_adamw_update", "orc_adamw_requant", "orc_dequantize_weight"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -138,6 +139,15 @@ def hadamard(x, block):
     y = np.empty((rows, cols), np.float32)
     _chk(lib().orc_hadamard(_ptr(x), dt, rows, cols, int(block), _ptr(y)))
     return y
+
+
+def dequantize_weight(qw, sw, had_block=0):
+    """The represented weight fl(s * q) per row, un-rotated when had_block != 0."""
+    qw = np.ascontiguousarray(qw, np.int8)
+    N, K = qw.shape
+    w = np.empty((N, K), np.float32)
+    _chk(lib().orc_dequantize_weight(_ptr(qw), _ptr(_f32(sw)), N, K, int(had_block), _ptr(w)))
+    return w
 
 
 def quantize_rows(x, prescale=None, had_block=0):

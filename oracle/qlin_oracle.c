@@ -144,6 +144,27 @@ int orc_hadamard(const void *x, int dtype, int64_t rows, int64_t cols, int b, fl
     return ORC_OK;
 }
 
+/* The represented weight in the original basis (OneTrainer PR #1681, commit
+ * note 2: callers that need the unquantized weight, such as LoRA, offload or
+ * export, un-rotate it): w = fl(s[n] * q[n, k]) per row, then, when b != 0,
+ * the rotation of each block (its own inverse).  w is [N, K] fp32. */
+int orc_dequantize_weight(const int8_t *qw, const float *sw, int64_t N, int64_t K, int b,
+                          float *w)
+{
+    if (N < 0 || K < 1 || (b != 0 && orc_check_block(K, b) != ORC_OK))
+        return ORC_EINVAL;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        float *row = w + n * K;
+        for (int64_t k = 0; k < K; k++)
+            row[k] = sw[n] * (float)qw[n * K + k];
+        if (b != 0)
+            for (int64_t c0 = 0; c0 < K; c0 += b)
+                fwht_block(row + c0, b);
+    }
+    return ORC_OK;
+}
+
 /* ------------------------------------------------------------ quantizers */
 
 /* Symmetric absmax quantization of one vector g[0..n) with element stride
