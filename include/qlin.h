@@ -153,6 +153,19 @@ int qlin_hadamard(const void *x, int dtype, int64_t rows, int64_t cols, int bloc
                   float *y, void *stream);
 
 /*
+ * The represented weight in the original basis, for callers that need the
+ * unquantized weight (OneTrainer PR #1681, commit note 2: LoRA, DoRA, offload
+ * and export un-rotate the weight; the rotation is its own inverse):
+ *   w[n, k] = fl(sw[n] * qw[n, k]), then, when had_block != 0, the rotation of
+ *   each block of had_block elements (as in qlin_hadamard).
+ *   qw [N, K] int8, sw [N] fp32 inputs; w [N, K] fp32 output, not overlapping
+ *   them.  had_block: 0 or a power of two in [2, 512] dividing K; K a multiple
+ *   of 16.
+ */
+int qlin_dequantize_weight(const int8_t *qw, const float *sw, int64_t N, int64_t K,
+                           int had_block, float *w, void *stream);
+
+/*
  * Forward product with fused dequant (mini_trainer guide: integer forward
  * product on INT8 weights; OneTrainer PR #1681: int8 x int8 -> int32
  * product of quantized activations and weights).

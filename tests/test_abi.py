@@ -164,3 +164,13 @@ def test_adamw_validation(L):
     assert call(bias=0x60000) == 1                # bias without db and its moments
     assert call(bias=0x60000, db=0x70000, bm=0x80000) == 1
     assert call(N=0, qw=None, dw=None, m=None, v=None) == 0
+
+
+def test_dequantize_weight_validation(L):
+    _cpu_only()
+    assert L.qlin_dequantize_weight(P, Q, 4, 24, 0, R, None) == 1        # K % 16
+    assert L.qlin_dequantize_weight(P, Q, 4, 96, 64, R, None) == 1       # block does not divide K
+    assert L.qlin_dequantize_weight(P, Q, 4, 128, 3, R, None) == 1       # not a power of two
+    assert L.qlin_dequantize_weight(None, Q, 4, 128, 0, R, None) == 1
+    assert L.qlin_dequantize_weight(P, Q, 4, 128, 0, P + 16, None) == 1  # w overlaps the codes
+    assert L.qlin_dequantize_weight(P, Q, 0, 128, 128, R, None) == 0

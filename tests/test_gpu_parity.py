@@ -155,10 +155,17 @@ def test_quantize_grad_no_tokens(T, Q, orc):
                                                 (5, 1024, 512, True), (7, 64, 2, False),
                                                 (9, 96, 32, True), (1, 16, 8, False),
                                                 (4, 384, 64, True), (6, 160, 16, False),
-                                                (2, 48, 16, True), (5, 4096, 128, True)])
+                                                (2, 48, 16, True), (5, 4096, 128, True),
+                                                (64, 1024, 128, False), (32, 512, 64, False),
+                                                (16, 256, 16, False)])
 def test_hadamard(T, Q, orc, rows, cols, blk, bf16):
     rng = np.random.default_rng(blk + rows)
     x = _x(rng, rows, cols, bf16)
+    if cols in (1024, 512, 256) and not bf16:
+        # small integers (and some -0.0): exact cancellations, signed zeros
+        x = rng.integers(-3, 4, (rows, cols)).astype(np.float32)
+        x[0, ::7] = np.float32(-0.0)
+        x[1, :blk] = np.float32(-0.0)            # a block of -0.0: the oracle keeps some -0.0
     announce("hadamard", rows, cols, blk, bf16)
     xd = dev(x)
     if bf16:
@@ -167,6 +174,19 @@ def test_hadamard(T, Q, orc, rows, cols, blk, bf16):
         y = Q.qlin_hadamard(xd, blk, y=xd)          # in place
     T.cuda.synchronize()
     assert_bitwise(host(y), orc.hadamard(x, blk), "rotation")
+
+
+@pytest.mark.parametrize("N,K,had", [(128, 256, 0), (64, 5376, 128), (7, 1024, 512),
+                                     (9, 96, 32), (33, 1088, 64), (5, 48, 16), (3, 64, 2),
+                                     (2, 4096, 256), (7168, 5376, 128)])
+def test_dequantize_weight(T, Q, orc, N, K, had):
+    rng = np.random.default_rng(N + K + had)
+    q = _codes(rng, (N, K))
+    s = rng.uniform(1e-4, 1e-1, N).astype(np.float32)
+    announce("dequantize_weight", N, K, had)
+    w = Q.qlin_dequantize_weight(dev(q), dev(s), had_block=had)
+    T.cuda.synchronize()
+    assert_bitwise(host(w), orc.dequantize_weight(q, s, had_block=had), "weight")
 
 
 # ----------------------------------------------------------------- products

@@ -29,6 +29,7 @@ SIGNATURES = {
     "qlin_quantize_grad": ([_vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
                            _i32),
     "qlin_hadamard": ([_vp, _i32, _i64, _i64, _i32, _vp, _vp], _i32),
+    "qlin_dequantize_weight": ([_vp, _vp, _i64, _i64, _i32, _vp, _vp], _i32),
     "qlin_fwd": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp], _i32),
     "qlin_bwd_dx": ([_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp], _i32),
     "qlin_bwd_dw": ([_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp], _i32),
@@ -175,6 +176,17 @@ def qlin_hadamard(x, block, y=None, stream=None):
     _check("qlin_hadamard", lib().qlin_hadamard(_ptr(x), code, rows, cols, int(block), _ptr(y),
                                                 _stream(stream)))
     return y
+
+
+def qlin_dequantize_weight(qw, sw, had_block=0, w=None, stream=None):
+    """fl(sw * qw) per row, rotated back to the original basis when had_block."""
+    N, K = qw.shape
+    _need(qw, "qw", torch.int8)
+    _need(sw, "sw", torch.float32, (N,))
+    w = _empty((N, K), torch.float32, qw) if w is None else _need(w, "w", torch.float32, (N, K))
+    _check("qlin_dequantize_weight", lib().qlin_dequantize_weight(
+        _ptr(qw), _ptr(sw), N, K, int(had_block), _ptr(w), _stream(stream)))
+    return w
 
 
 def qlin_fwd(qx, sx, qw, sw, bias=None, y=None, stream=None):

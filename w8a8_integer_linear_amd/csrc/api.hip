@@ -133,6 +133,27 @@ int qlin_quantize_grad(const void *dy, int dtype, int64_t rows, int64_t cols, co
     return finish();
 }
 
+int qlin_dequantize_weight(const int8_t *qw, const float *sw, int64_t N, int64_t K,
+                           int had_block, float *w, void *stream)
+{
+    if (N < 0 || !dim16(K))
+        return QLIN_EINVAL;
+    if (!array_ok(qw, N > 0) || !array_ok(sw, N > 0) || !array_ok(w, N > 0))
+        return QLIN_EINVAL;
+    if (had_block != 0 && !hadamard_block_ok(K, had_block))
+        return QLIN_EINVAL;
+    if (N > 0 && (overlap(w, N * K * 4, qw, N * K) || overlap(w, N * K * 4, sw, N * 4)))
+        return QLIN_EINVAL;
+    if ((N * K) / 8 / 256 >= ((int64_t)1 << 31))
+        return QLIN_EUNSUPPORTED;
+    if (N == 0)
+        return QLIN_OK;
+    qlin::launch_dequantize_weight(qw, sw, N, K, had_block,
+                                   had_block ? hadamard_scale(had_block) : 1.0f, w,
+                                   as_stream(stream));
+    return finish();
+}
+
 int qlin_hadamard(const void *x, int dtype, int64_t rows, int64_t cols, int block, float *y,
                   void *stream)
 {

@@ -130,7 +130,13 @@ __device__ __forceinline__ void fwht8_lanes(float v[8], int blk, float cb)
 // sigma (hi - lo) = -sigma (lo - hi), i.e. sigma flips on upper lanes.  Each
 // value is one correctly rounded sum of +-lo and +-hi (the product by c is
 // exact), so with the sign undone (exactly, in the final scaling by
-// sigma * cb) the result is bit-identical to lo + hi and lo - hi.
+// sigma * cb) the result is bit-identical to lo + hi and lo - hi, except
+// for the sign of an exact zero (x - x is +0 whatever sign is carried).
+// That is immaterial to a quantizer (a zero of either sign gives code 0 and
+// leaves the absmax unchanged).  Kernels that output the rotated floats use
+// the exact form (EXACT): v = fma(c, v, partner), i.e. lo + hi on the lower
+// lane and lo - hi on the upper one, with the partner read by a separate DPP
+// move: two instructions per value and stage, and no sign to undo.
 template <int BLK>
 __device__ __forceinline__ int64_t had_chunk(int64_t c)
 {
@@ -160,22 +166,34 @@ __device__ __forceinline__ int64_t had_chunk(int64_t c)
           "+v"(v[7])                                                                             \
         : "v"(c))
 
-template <int BLK, int K>
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int BLK, int K, bool EXACT>
 __device__ __forceinline__ void fwht_lane_stage(float v[8], int p)
 {
     static_assert(K < 4 && (8 << K) < BLK, "stage outside the block");
     const float c = ((p >> K) & 1) ? -1.0f : 1.0f;
-    if constexpr (K == 0)
+    if constexpr (EXACT) {
+        constexpr int kCtrl = K == 0 ? 0xB1 : K == 1 ? 0x4E : K == 2 ? 0x141 : 0x128;
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            v[i] = __builtin_fmaf(c, v[i], dpp_mov<kCtrl>(v[i]));
+    } else if constexpr (K == 0) {
         QLIN_FWHT_DPP_STAGE("quad_perm:[1,0,3,2]");
-    else if constexpr (K == 1)
+    } else if constexpr (K == 1) {
         QLIN_FWHT_DPP_STAGE("quad_perm:[2,3,0,1]");
-    else if constexpr (K == 2)
+    } else if constexpr (K == 2) {
         QLIN_FWHT_DPP_STAGE("row_half_mirror");
-    else
+    } else {
         QLIN_FWHT_DPP_STAGE("row_ror:8");
+    }
 }
 
-template <int BLK>
+template <int BLK, bool EXACT>
 __device__ __forceinline__ void fwht8_fixed(float v[8], float cb)
 {
     static_assert(BLK >= 16 && BLK <= 128 && (BLK & (BLK - 1)) == 0, "block size");
@@ -191,14 +209,14 @@ __device__ __forceinline__ void fwht8_fixed(float v[8], float cb)
         }
     }
     const int p = (int)had_chunk<BLK>(__lane_id() & 15) & (BLK / 8 - 1);
-    fwht_lane_stage<BLK, 0>(v, p);
+    fwht_lane_stage<BLK, 0, EXACT>(v, p);
     if constexpr (BLK > 16)
-        fwht_lane_stage<BLK, 1>(v, p);
+        fwht_lane_stage<BLK, 1, EXACT>(v, p);
     if constexpr (BLK > 32)
-        fwht_lane_stage<BLK, 2>(v, p);
+        fwht_lane_stage<BLK, 2, EXACT>(v, p);
     if constexpr (BLK > 64)
-        fwht_lane_stage<BLK, 3>(v, p);
-    const float scale = (__builtin_popcount(p) & 1) ? -cb : cb;
+        fwht_lane_stage<BLK, 3, EXACT>(v, p);
+    const float scale = (!EXACT && (__builtin_popcount(p) & 1)) ? -cb : cb;
 #pragma unroll
     for (int i = 0; i < 8; i++)
         v[i] = v[i] * scale;

@@ -22,6 +22,9 @@ void launch_quantize_grad(const void *x, bool bf16, int64_t rows, int64_t cols, 
                           const float *sx, int8_t *q1, float *s1, int8_t *q2, float *s2,
                           float *col_sum, hipStream_t st);
 
+void launch_dequantize_weight(const int8_t *q, const float *sw, int64_t rows, int64_t cols,
+                              int blk, float cb, float *w, hipStream_t st);
+
 void launch_hadamard(const void *x, bool bf16, int64_t rows, int64_t cols, int blk, float cb,
                      float *y, hipStream_t st);
 

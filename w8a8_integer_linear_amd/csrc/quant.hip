@@ -24,12 +24,13 @@ namespace qlin {
 // Rotation of one 8-element chunk: HAD is the block size when it is known at
 // compile time (16 .. 128; 0: no rotation), -1 for a block size given at run
 // time.  With a fixed block the lane processes chunk had_chunk<HAD>(c) in
-// place of c.
-template <int HAD>
+// place of c.  EXACT keeps the oracle's sign of exact zeros (needed where the
+// rotated floats are the output; a quantizer does not need it).
+template <int HAD, bool EXACT = false>
 __device__ __forceinline__ void rotate8(float v[8], int had, float cb)
 {
     if constexpr (HAD > 0)
-        fwht8_fixed<HAD>(v, cb);
+        fwht8_fixed<HAD, EXACT>(v, cb);
     else if constexpr (HAD < 0)
         fwht8_lanes(v, had, cb);
 }
@@ -515,9 +516,57 @@ __global__ __launch_bounds__(256) void hadamard_kernel(const void *__restrict__ 
         for (int e = 0; e < 8; e++)
             v[e] = 0.0f;
     }
-    rotate8<HAD>(v, blk, cb);
+    rotate8<HAD, true>(v, blk, cb);
     if (ok)
         store8(y, c * 8, v);
+}
+
+// The represented weight in the original basis: w = fl(s[row] * q) for 8
+// consecutive codes per lane, then (HAD != 0) the rotation of each block.
+// Flat over 8-element chunks like the rotation kernel.
+template <int HAD>
+__global__ __launch_bounds__(256) void dequant_weight_kernel(const int8_t *__restrict__ q,
+                                                             const float *__restrict__ sw,
+                                                             int64_t nch, int64_t cols, int blk,
+                                                             float cb, float *__restrict__ w)
+{
+    const int64_t c = lane_chunk<HAD>((int64_t)blockIdx.x * 256 + threadIdx.x);
+    const bool ok = c < nch;
+    float v[8];
+    if (ok) {
+        const i32x2 qv = *reinterpret_cast<const i32x2 *>(q + c * 8);
+        const float s = sw[(c * 8) / cols];
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            v[e] = s * (float)(int8_t)((uint32_t)qv[e / 4] >> (8 * (e % 4)));
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            v[e] = 0.0f;
+    }
+    if (HAD != 0)
+        rotate8<HAD, true>(v, blk, cb);
+    if (ok)
+        store8(w, c * 8, v);
+}
+
+void launch_dequantize_weight(const int8_t *q, const float *sw, int64_t rows, int64_t cols,
+                              int blk, float cb, float *w, hipStream_t st)
+{
+    const int64_t nch = rows * cols / 8;
+    const unsigned grid = (unsigned)((nch + 255) / 256);
+    auto go = [&](auto h) {
+        hipLaunchKernelGGL((dequant_weight_kernel<decltype(h)::value>), dim3(grid), dim3(256), 0,
+                           st, q, sw, nch, cols, blk, cb, w);
+    };
+    switch (blk) {
+    case 0: return go(std::integral_constant<int, 0>());
+    case 16: return go(std::integral_constant<int, 16>());
+    case 32: return go(std::integral_constant<int, 32>());
+    case 64: return go(std::integral_constant<int, 64>());
+    case 128: return go(std::integral_constant<int, 128>());
+    default: return go(std::integral_constant<int, -1>());
+    }
 }
 
 void launch_hadamard(const void *x, bool bf16, int64_t rows, int64_t cols, int blk, float cb,

@@ -96,6 +96,11 @@ class LinearW8A8Training:
                                bias_v=self._bv if has_b else None)
         self._tick("adamw_requant")
 
+    def unquantized_weight(self):
+        """The represented weight fl(s_w * Q_w), rotated back to the original
+        basis (a new [N, K] fp32 tensor)."""
+        return nat.qlin_dequantize_weight(self.qw, self.sw, had_block=self.had)
+
     def _tick(self, label):
         if self.timer is not None:
             self.timer(label)
