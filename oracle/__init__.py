@@ -81,6 +81,8 @@ def lib():
         L.orc_sgd_requant.argtypes = [vp, vp, vp, i64, i64, f32, u64, u64, vp, vp, vp]
         L.orc_bwd_dw_rows.argtypes = [vp, vp, vp, i64, i64, i64, vp, i64, vp]
         L.orc_dequantize_weight.argtypes = [vp, vp, i64, i64, i32, vp]
+        L.orc_gemm_s64_at.argtypes = [i32, vp, vp, i64, i64, i64, vp, vp, i64, vp]
+        L.orc_op_at_long.argtypes = [i32, vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, i64, vp]
         L.orc_adamw_constants.argtypes = [f32, f32, f32, f32, u64, vp]
         L.orc_adamw_constants.restype = None
         L.orc_adamw_update.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, f32, f32, f32, f32,
@@ -90,7 +92,8 @@ def lib():
         for name in ("orc_hadamard", "orc_quantize_rows", "orc_quantize_cols",
                      "orc_gemm_s32", "orc_gemm_s32_at", "orc_fwd", "orc_bwd_dx",
                      "orc_bwd_dw", "orc_bwd_dw_rows", "orc_op_at", "orc_sgd_requant",
-                     "orc_adamw_update", "orc_adamw_requant", "orc_dequantize_weight"):
+                     "orc_adamw_update", "orc_adamw_requant", "orc_dequantize_weight",
+                     "orc_gemm_s64_at", "orc_op_at_long"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -254,6 +257,32 @@ def op_at(op, a, srow, b, scol, bias, M, N, K, ii, jj):
     _chk(lib().orc_op_at(op, _ptr(a), _ptr(_f32(srow)), _ptr(b), _ptr(_f32(scol)),
                          _ptr(_f32(bias)), M, N, K, _ptr(ii), _ptr(jj), len(ii),
                          _ptr(out)))
+    return out
+
+
+def gemm_s64_at(op, a, b, M, N, K, ii, jj):
+    """Exact (int64) accumulators at positions, for any contraction length."""
+    a = np.ascontiguousarray(a, np.int8)
+    b = np.ascontiguousarray(b, np.int8)
+    ii = np.ascontiguousarray(ii, np.int64)
+    jj = np.ascontiguousarray(jj, np.int64)
+    out = np.empty(len(ii), np.int64)
+    _chk(lib().orc_gemm_s64_at(op, _ptr(a), _ptr(b), M, N, K, _ptr(ii), _ptr(jj), len(ii),
+                               _ptr(out)))
+    return out
+
+
+def op_at_long(op, a, srow, b, scol, bias, M, N, K, ii, jj):
+    """op_at for any contraction length: int32 chunk sums combined in int64
+    (equal to the exact dot product), converted once to fp32, dequantized."""
+    a = np.ascontiguousarray(a, np.int8)
+    b = np.ascontiguousarray(b, np.int8)
+    ii = np.ascontiguousarray(ii, np.int64)
+    jj = np.ascontiguousarray(jj, np.int64)
+    out = np.empty(len(ii), np.float32)
+    _chk(lib().orc_op_at_long(op, _ptr(a), _ptr(_f32(srow)), _ptr(b), _ptr(_f32(scol)),
+                              _ptr(_f32(bias)), M, N, K, _ptr(ii), _ptr(jj), len(ii),
+                              _ptr(out)))
     return out
 
 

@@ -335,10 +335,9 @@ int orc_gemm_s32_at(int op, const int8_t *a, const int8_t *b, int64_t M, int64_t
  *   dW     : dw = fl(fl32(acc) * sg2[n])
  * srow is the scale of the output row (sx, sg1 or sg2), scol the scale of the
  * output column (sw for the forward product, unused otherwise). */
-static float dequant(int op, int64_t acc, const float *srow, const float *scol,
-                     const float *bias, int64_t i, int64_t j)
+static float dequant_f(int op, float v, const float *srow, const float *scol,
+                       const float *bias, int64_t i, int64_t j)
 {
-    float v = (float)(int32_t)acc;
     v = v * srow[i];
     if (op == 0) {
         v = v * scol[j];
@@ -346,6 +345,12 @@ static float dequant(int op, int64_t acc, const float *srow, const float *scol,
             v = v + bias[j];
     }
     return v;
+}
+
+static float dequant(int op, int64_t acc, const float *srow, const float *scol,
+                     const float *bias, int64_t i, int64_t j)
+{
+    return dequant_f(op, (float)(int32_t)acc, srow, scol, bias, i, j);
 }
 
 /* Forward: y[M, N] from (qx, sx) and (qw, sw), optional bias. */
@@ -654,5 +659,38 @@ int orc_adamw_requant(int8_t *qw, float *sw, const float *dw, float *m, float *v
     }
     if (bias && db && bm && bv)
         adamw_elems(bias, bm, bv, db, N, b1, b2, eps, k);
+    return ORC_OK;
+}
+
+/* ------------------------------------------- contractions above 131,071 */
+
+/* The guide's rule for contractions above 131,071: bounded int32 partial dot
+ * products (each over at most 131,071 terms, so exact) are combined in int64
+ * before scaling.  Integer addition is exact and associative, so the result
+ * is the exact dot product whatever the chunking; it is converted to fp32
+ * once (round to nearest even) and then dequantized as usual.  These entry
+ * points take any contraction length. */
+int orc_gemm_s64_at(int op, const int8_t *a, const int8_t *b, int64_t M, int64_t N,
+                    int64_t K, const int64_t *ii, const int64_t *jj, int64_t count,
+                    int64_t *out)
+{
+    if (op < 0 || op > 2 || M < 0 || N < 1 || K < 1)
+        return ORC_EINVAL;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < count; t++)
+        out[t] = dot_op(op, a, b, M, N, K, ii[t], jj[t]);
+    return ORC_OK;
+}
+
+int orc_op_at_long(int op, const int8_t *a, const float *srow, const int8_t *b,
+                   const float *scol, const float *bias, int64_t M, int64_t N, int64_t K,
+                   const int64_t *ii, const int64_t *jj, int64_t count, float *out)
+{
+    if (op < 0 || op > 2 || M < 0 || N < 1 || K < 1)
+        return ORC_EINVAL;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < count; t++)
+        out[t] = dequant_f(op, (float)dot_op(op, a, b, M, N, K, ii[t], jj[t]), srow, scol,
+                           bias, ii[t], jj[t]);
     return ORC_OK;
 }
