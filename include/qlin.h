@@ -26,7 +26,8 @@
  *  - Shapes: M (tokens) >= 0 is arbitrary; M == 0 is a no-op (except that
  *    qlin_bwd_dw then writes an all-zero dW).  N (out
  *    features) and K (in features) are multiples of 16.  A contraction longer
- *    than QLIN_MAX_CONTRACTION is rejected with QLIN_EUNSUPPORTED.
+ *    than QLIN_MAX_CONTRACTION is rejected with QLIN_EUNSUPPORTED, except by
+ *    qlin_product_ws, which combines int32 chunks in int64.
  *  - Arithmetic: IEEE binary32, round to nearest even, no fused multiply-add,
  *    IEEE division.  Results are deterministic and do not depend on the
  *    launch configuration, except col_sum of qlin_quantize_cols (fp32 sums
@@ -203,6 +204,35 @@ int qlin_bwd_dx(const int8_t *qg1, const float *sg1, const int8_t *qw, int64_t M
  */
 int qlin_bwd_dw(const int8_t *qg2, const float *sg2, const int8_t *qx, int64_t M,
                 int64_t N, int64_t K, float *dw, void *stream);
+
+/*
+ * Any of the three products with a contraction of any length up to 2^31 - 1
+ * (mini_trainer guide, arithmetic paragraph: contractions above 131,071
+ * combine bounded int32 dot products in int64 before scaling).  The
+ * contraction is split into chunks of at most 131,071 terms whose exact int32
+ * sums are combined in int64 in 'workspace'; fl32 of the int64 total then
+ * goes through the product's usual epilogue.  Up to the bound the call is
+ * exactly qlin_fwd / qlin_bwd_dx / qlin_bwd_dw and the workspace is unused.
+ *
+ *   op        QLIN_OP_FWD: a = qx [M,K], srow = sx, b = qw [N,K], scol = sw,
+ *                          bias optional, out = y [M,N], had_block = 0;
+ *             QLIN_OP_DX:  a = qg1 [M,N], srow = sg1, b = qw [N,K],
+ *                          out = dx [M,K], had_block as in qlin_bwd_dx;
+ *             QLIN_OP_DW:  a = qg2 [M,N], srow = sg2, b = qx [M,K],
+ *                          out = dw [N,K], had_block = 0.
+ *             scol and bias must be NULL except for the forward product.
+ *   workspace device memory of at least qlin_product_ws_bytes(op, M, N, K)
+ *             bytes (8 per output element), 16-byte aligned, overlapping no
+ *             other argument; its contents are scratch.
+ */
+int qlin_product_ws(int op, const int8_t *a, const float *srow, const int8_t *b,
+                    const float *scol, const float *bias, int64_t M, int64_t N, int64_t K,
+                    int had_block, float *out, void *workspace, size_t ws_bytes,
+                    void *stream);
+
+/* Workspace bytes qlin_product_ws needs: 0 up to the int32 bound, else 8 per
+ * output element.  Returns 0 for invalid arguments. */
+size_t qlin_product_ws_bytes(int op, int64_t M, int64_t N, int64_t K);
 
 /*
  * SGD step with stochastic requantization of each weight row, in place

@@ -174,3 +174,28 @@ def test_dequantize_weight_validation(L):
     assert L.qlin_dequantize_weight(None, Q, 4, 128, 0, R, None) == 1
     assert L.qlin_dequantize_weight(P, Q, 4, 128, 0, P + 16, None) == 1  # w overlaps the codes
     assert L.qlin_dequantize_weight(P, Q, 0, 128, 128, R, None) == 0
+
+
+def test_product_ws_validation(L):
+    _cpu_only()
+    F = lambda i: (i + 1) << 33     # widely spaced fake addresses
+    assert L.qlin_product_ws_bytes(2, 200000, 16, 32) == 8 * 16 * 32
+    assert L.qlin_product_ws_bytes(2, 1000, 16, 32) == 0
+    assert L.qlin_product_ws_bytes(0, 4, 16, 262144) == 8 * 4 * 16
+    # op, a, srow, b, scol, bias, M, N, K, had, out, ws, ws_bytes
+    long_dw = [2, F(0), F(1), F(2), None, None, 200000, 16, 32, 0, F(3), F(4), 8 * 16 * 32]
+    def call(**kw):
+        a = list(long_dw)
+        names = ["op", "a", "srow", "b", "scol", "bias", "M", "N", "K", "had", "out", "ws",
+                 "ws_bytes"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return L.qlin_product_ws(*a, None)
+    assert call(op=3) == 1
+    assert call(scol=F(5)) == 1                     # column scales: forward only
+    assert call(had=128) == 1                       # rotation: dX only
+    assert call(ws=None) == 1                       # a long contraction needs the workspace
+    assert call(ws_bytes=8 * 16 * 32 - 8) == 1      # too small
+    assert call(ws=F(3) + 16) == 1                  # overlaps the output
+    assert call(K=24) == 1
+    assert call(M=1 << 31) == 2                     # beyond the longest contraction

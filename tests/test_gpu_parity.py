@@ -324,6 +324,64 @@ def test_dw_empty_tokens(T, Q, orc):
     assert np.all(host(dw) == 0)
 
 
+LONG_CASES = [
+    # op, M, N, K, had: contractions above 131,071 (3 chunks, 2 chunks)
+    (2, 300_000, 32, 48, 0),
+    (1, 32, 200_000, 256, 128),
+    (1, 20, 140_000, 512, 256),      # rotation block too wide to fuse: separate pass
+    (0, 20, 48, 262_144, 0),         # forward with bias; 20 rows use the tiled kernel
+    (0, 3, 32, 140_032, 0),          # a skinny M takes the tiled kernel too
+]
+
+
+@pytest.mark.parametrize("op,M,N,K,had", LONG_CASES)
+def test_long_contraction(T, Q, orc, op, M, N, K, had):
+    rng = np.random.default_rng(op * 7 + M)
+    sa = (M, K) if op == 0 else (M, N)
+    sb = (N, K) if op in (0, 1) else (M, K)
+    a = _codes(rng, sa)
+    b = _codes(rng, sb)
+    # output row 0 has columns whose sums pass 2^31
+    if op == 0:
+        a[0] = 127
+        b[:4] = 127
+    elif op == 1:
+        a[0] = 127
+        b[:, :4] = 127
+    else:
+        a[:, 0] = 127
+        b[:, :4] = 127
+    R, C = {0: (M, N), 1: (M, K), 2: (N, K)}[op]
+    srow = rng.uniform(1e-4, 1e-2, R).astype(np.float32)
+    scol = rng.uniform(1e-2, 1e-1, N).astype(np.float32) if op == 0 else None
+    bias = rng.standard_normal(N).astype(np.float32) if op == 0 else None
+    announce("long contraction", op, M, N, K, had)
+    out = Q.qlin_product_ws(op, dev(a), dev(srow), dev(b), M, N, K,
+                            scol=None if scol is None else dev(scol),
+                            bias=None if bias is None else dev(bias), had_block=had)
+    T.cuda.synchronize()
+    ii, jj = np.repeat(np.arange(R), C), np.tile(np.arange(C), R)
+    acc = orc.gemm_s64_at(op, a, b, M, N, K, ii[:C], jj[:C])
+    assert np.abs(acc).max() > 2 ** 31          # row 0 overflows int32
+    ref = orc.op_at_long(op, a, srow, b, scol, bias, M, N, K, ii, jj).reshape(R, C)
+    if had:
+        ref = orc.hadamard(ref, had)
+    assert_bitwise(host(out), ref, "long product")
+
+
+def test_product_ws_within_bound_is_the_plain_call(T, Q, orc):
+    rng = np.random.default_rng(1)
+    M, N, K = 130, 272, 208
+    qg = _codes(rng, (M, N))
+    qx = _codes(rng, (M, K))
+    s = rng.uniform(1e-3, 1e-2, N).astype(np.float32)
+    announce("product_ws within the bound")
+    a = Q.qlin_product_ws(2, dev(qg), dev(s), dev(qx), M, N, K)
+    b = Q.qlin_bwd_dw(dev(qg), dev(s), dev(qx))
+    T.cuda.synchronize()
+    assert_bitwise(host(a), host(b), "dW")
+
+
 # ------------------------------------------------------------------ update
 
 SGD_CASES = [(128, 256, True), (64, 5376, False), (7, 16, True), (3, 20480, False),

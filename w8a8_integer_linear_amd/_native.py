@@ -37,6 +37,9 @@ SIGNATURES = {
     "qlin_adamw_requant": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _f32, _f32, _f32, _f32,
                             _u64, _u64, _vp, _vp, _vp, _vp, _vp], _i32),
     "qlin_gemm_s32": ([_i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp], _i32),
+    "qlin_product_ws": ([_i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp,
+                         ctypes.c_size_t, _vp], _i32),
+    "qlin_product_ws_bytes": ([_i32, _i64, _i64, _i64], ctypes.c_size_t),
 }
 
 
@@ -259,6 +262,32 @@ def qlin_adamw_requant(qw, sw, dw, m, v, lr, beta1, beta2, eps, weight_decay, se
         float(beta2), float(eps), float(weight_decay), int(seed), int(step), _ptr(bias),
         _ptr(db), _ptr(bias_m), _ptr(bias_v), _stream(stream)))
     return qw, sw
+
+
+def qlin_product_ws_bytes(op, M, N, K):
+    return int(lib().qlin_product_ws_bytes(int(op), int(M), int(N), int(K)))
+
+
+def qlin_product_ws(op, a, srow, b, M, N, K, scol=None, bias=None, had_block=0, out=None,
+                    workspace=None, stream=None):
+    """Any product with a contraction of any length (int32 chunks combined in
+    int64 in the workspace, allocated here when not given)."""
+    shape = {QLIN_OP_FWD: (M, N), QLIN_OP_DX: (M, K), QLIN_OP_DW: (N, K)}[op]
+    _need(a, "a", torch.int8)
+    _need(b, "b", torch.int8)
+    _need(srow, "srow", torch.float32)
+    _opt(scol, "scol", torch.float32, (N,))
+    _opt(bias, "bias", torch.float32, (N,))
+    out = _empty(shape, torch.float32, a) if out is None else _need(out, "out", torch.float32,
+                                                                     shape)
+    need = qlin_product_ws_bytes(op, M, N, K)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("qlin_product_ws", lib().qlin_product_ws(
+        int(op), _ptr(a), _ptr(srow), _ptr(b), _ptr(scol), _ptr(bias), M, N, K, int(had_block),
+        _ptr(out), _ptr(workspace), nbytes, _stream(stream)))
+    return out
 
 
 def qlin_gemm_s32(op, a, b, M, N, K, c=None, stream=None):

@@ -36,6 +36,9 @@ bool overlap(const void *a, int64_t na, const void *b, int64_t nb)
     return x < y + nb && y < x + na;
 }
 
+// Longest contraction qlin_product_ws accepts (chunked into int32-exact pieces).
+constexpr int64_t kMaxLongContraction = ((int64_t)1 << 31) - 1;
+
 // Largest token count a call accepts (grid dimensions and int32 tile indices).
 constexpr int64_t kMaxRows = (int64_t)1 << 30;
 
@@ -181,7 +184,7 @@ int qlin_hadamard(const void *x, int dtype, int64_t rows, int64_t cols, int bloc
 // bound.  'a_rows' / 'b_rows' tell whether the operands hold any element and
 // 'out_rows' whether the output does.
 static int check_product(int op, const void *a, const void *b, void *out, int64_t M, int64_t N,
-                         int64_t K)
+                         int64_t K, int64_t max_contraction = QLIN_MAX_CONTRACTION)
 {
     if (M < 0 || !dim16(N) || !dim16(K))
         return QLIN_EINVAL;
@@ -192,7 +195,7 @@ static int check_product(int op, const void *a, const void *b, void *out, int64_
     if (!array_ok(a, has_m) || !array_ok(b, b_nonempty && has_m) || !array_ok(out, out_nonempty))
         return QLIN_EINVAL;
     const int64_t contraction = op == QLIN_OP_FWD ? K : (op == QLIN_OP_DX ? N : M);
-    if (contraction > QLIN_MAX_CONTRACTION || M > kMaxRows || N > kMaxRows || K > kMaxRows)
+    if (contraction > max_contraction || M > kMaxRows || N > kMaxRows || K > kMaxRows)
         return QLIN_EUNSUPPORTED;
     return QLIN_OK;
 }
@@ -249,6 +252,64 @@ int qlin_bwd_dw(const int8_t *qg2, const float *sg2, const int8_t *qx, int64_t M
     // An empty token range still defines dW (all zero).
     qlin::ProductArgs p{QLIN_OP_DW, qg2, qx, M, N, K, sg2, nullptr, nullptr, dw, false};
     qlin::launch_product(p, as_stream(stream));
+    return finish();
+}
+
+size_t qlin_product_ws_bytes(int op, int64_t M, int64_t N, int64_t K)
+{
+    if (op < QLIN_OP_FWD || op > QLIN_OP_DW || M < 0 || N < 0 || K < 0)
+        return 0;
+    const int64_t contraction = op == QLIN_OP_FWD ? K : (op == QLIN_OP_DX ? N : M);
+    if (contraction <= QLIN_MAX_CONTRACTION)
+        return 0;
+    const int64_t rows = op == QLIN_OP_DW ? N : M, cols = op == QLIN_OP_FWD ? N : K;
+    return (size_t)(8 * rows * cols);
+}
+
+int qlin_product_ws(int op, const int8_t *a, const float *srow, const int8_t *b,
+                    const float *scol, const float *bias, int64_t M, int64_t N, int64_t K,
+                    int had_block, float *out, void *workspace, size_t ws_bytes, void *stream)
+{
+    if (op < QLIN_OP_FWD || op > QLIN_OP_DW)
+        return QLIN_EINVAL;
+    if (op != QLIN_OP_FWD && (scol || bias))
+        return QLIN_EINVAL;
+    if (op != QLIN_OP_DX && had_block != 0)
+        return QLIN_EINVAL;
+    const int64_t contraction = op == QLIN_OP_FWD ? K : (op == QLIN_OP_DX ? N : M);
+    if (contraction <= QLIN_MAX_CONTRACTION) {
+        if (op == QLIN_OP_FWD)
+            return qlin_fwd(a, srow, b, scol, bias, M, N, K, out, stream);
+        if (op == QLIN_OP_DX)
+            return qlin_bwd_dx(a, srow, b, M, N, K, had_block, out, stream);
+        return qlin_bwd_dw(a, srow, b, M, N, K, out, stream);
+    }
+    int st = check_product(op, a, b, out, M, N, K, kMaxLongContraction);
+    if (st != QLIN_OK)
+        return st;
+    if (had_block != 0 && !hadamard_block_ok(K, had_block))
+        return QLIN_EINVAL;
+    if (M == 0)
+        return QLIN_OK;     // forward and dX outputs are empty (dW has M > 0 here)
+    if (!srow || (op == QLIN_OP_FWD && !scol))
+        return QLIN_EINVAL;
+    const int64_t rows = op == QLIN_OP_DW ? N : M, cols = op == QLIN_OP_FWD ? N : K;
+    const int64_t need = 8 * rows * cols;
+    const int64_t la = op == QLIN_OP_FWD ? M * K : M * N, lb = op == QLIN_OP_DW ? M * K : N * K;
+    if (!workspace || !aligned16(workspace) || (int64_t)ws_bytes < need ||
+        overlap(workspace, need, out, 4 * rows * cols) || overlap(workspace, need, a, la) ||
+        overlap(workspace, need, b, lb))
+        return QLIN_EINVAL;
+    qlin::ProductArgs p{op, a, b, M, N, K, srow, scol, bias, out, false};
+    const hipStream_t s = as_stream(stream);
+    int64_t *ws = static_cast<int64_t *>(workspace);
+    if (op == QLIN_OP_DX && had_block >= 2 && had_block <= 128) {
+        p.had = had_block;
+        p.had_scale = hadamard_scale(had_block);
+    }
+    qlin::launch_product_long(p, ws, s);
+    if (op == QLIN_OP_DX && had_block > 128)
+        qlin::launch_hadamard(out, false, M, K, had_block, hadamard_scale(had_block), out, s);
     return finish();
 }
 

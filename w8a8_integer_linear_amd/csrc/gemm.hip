@@ -49,6 +49,11 @@ struct GemmParams {
     int tiles_i, tiles_j;
     int had;          // EPI_ROWSCALE_HAD: rotation block (2 .. 128, power of two)
     float had_scale;  // fl32(1 / sqrt(had))
+    // Contractions split into chunks: ws [R, S] int64 (row stride ldc) holds
+    // the running sum.  ws_mode 0: none; 1: store this chunk's sums; 2: add
+    // them; 3: the epilogue takes acc + ws (the last chunk).
+    int64_t *ws;
+    int ws_mode;
 };
 
 // ------------------------------------------------------------------ staging
@@ -237,7 +242,10 @@ __device__ __forceinline__ void tile_of(int pid, int tiles_i, int tiles_j, int &
 
 // ------------------------------------------------------------------- kernel
 
-template <int BM, int BN, int WM, int WN, int kBK, int OCC, bool AKM, bool BKM, int EPI>
+// WS: the launch is one chunk of a split contraction (ws_mode 1-3); kernels
+// of ordinary launches carry no workspace code.
+template <int BM, int BN, int WM, int WN, int kBK, int OCC, bool AKM, bool BKM, int EPI,
+          bool WS>
 __global__ __launch_bounds__(WM *WN * 64, OCC) void gemm_kernel(GemmParams p)
 {
     constexpr int NT = WM * WN * 64;
@@ -377,6 +385,55 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void gemm_kernel(GemmParams p)
     // block holds C transposed: lane l has output row l % 32 and, in register
     // 4 g + e, output column 8 g + 4 (l / 32) + e.  Every lane therefore
     // writes 16-byte runs of four columns of its row.
+    typedef long long i64x2 __attribute__((ext_vector_type(2)));
+    auto ws_at = [&](int i, int j) { return p.ws + (int64_t)i * p.ldc + j; };
+    // Four consecutive int64 running sums of row i from column j, or zeros
+    // when this is not the last chunk of a split contraction.
+    auto ws4 = [&](int i, int j, int64_t e[4]) {
+        if (WS && p.ws_mode == 3 && j < p.S) {
+            const i64x2 *w = reinterpret_cast<const i64x2 *>(ws_at(i, j));
+            const i64x2 lo = w[0], hi = w[1];
+            e[0] = lo[0]; e[1] = lo[1]; e[2] = hi[0]; e[3] = hi[1];
+        } else {
+            e[0] = e[1] = e[2] = e[3] = 0;
+        }
+    };
+    // fl32 of the accumulator (plus the running sum of earlier chunks).
+    auto tofloat = [&](int32_t c, int64_t e) {
+        if constexpr (WS)
+            return p.ws_mode == 3 ? (float)((int64_t)c + e) : (float)c;
+        else
+            return (float)c;
+    };
+    if constexpr (WS && EPI != EPI_RAW) {
+        if (p.ws_mode == 1 || p.ws_mode == 2) {
+#pragma unroll
+            for (int a = 0; a < FM; a++) {
+                const int i = i0 + wi * (BM / WM) + a * 32 + lane % 32;
+                if (i >= p.R)
+                    continue;
+#pragma unroll
+                for (int b = 0; b < FN; b++) {
+#pragma unroll
+                    for (int g = 0; g < 4; g++) {
+                        const int j = j0 + wj * (BN / WN) + b * 32 + 8 * g + 4 * (lane / 32);
+                        if (j >= p.S)
+                            continue;
+                        i64x2 *w = reinterpret_cast<i64x2 *>(ws_at(i, j));
+                        i64x2 lo = {acc[a][b][4 * g], acc[a][b][4 * g + 1]};
+                        i64x2 hi = {acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]};
+                        if (p.ws_mode == 2) {
+                            lo = lo + w[0];
+                            hi = hi + w[1];
+                        }
+                        w[0] = lo;
+                        w[1] = hi;
+                    }
+                }
+            }
+            return;
+        }
+    }
     if constexpr (EPI == EPI_ROWSCALE_HAD) {
         static_assert(FN == 4, "the rotating epilogue needs 128-column wave tiles");
         // Within the wave's 128 columns, column c = 32 b + 8 g + 4 h + e with
@@ -397,8 +454,13 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void gemm_kernel(GemmParams p)
 #pragma unroll
             for (int b = 0; b < FN; b++)
 #pragma unroll
-                for (int r = 0; r < 16; r++)
-                    v[b][r] = (float)acc[a][b][r] * rs;
+                for (int g = 0; g < 4; g++) {
+                    int64_t e[4];
+                    ws4(i, j0 + wj * (BN / WN) + b * 32 + 8 * g + 4 * (lane / 32), e);
+#pragma unroll
+                    for (int r = 0; r < 4; r++)
+                        v[b][4 * g + r] = tofloat(acc[a][b][4 * g + r], e[r]) * rs;
+                }
             auto pair = [](float &lo, float &hi) {
                 const float x = lo, y = hi;
                 lo = x + y;
@@ -496,9 +558,11 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void gemm_kernel(GemmParams p)
                         i32x4{c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]};
                 } else {
                     f32x4 v;
+                    int64_t w[4];
+                    ws4(i, j, w);
 #pragma unroll
                     for (int e = 0; e < 4; e++)
-                        v[e] = (float)c[4 * g + e] * rs;
+                        v[e] = tofloat(c[4 * g + e], w[e]) * rs;
                     if constexpr (EPI == EPI_FWD) {
                         const f32x4 cs = *reinterpret_cast<const f32x4 *>(p.scol + j);
 #pragma unroll
@@ -525,8 +589,14 @@ void run_gemm(const GemmParams &p0, hipStream_t st)
     p.tiles_i = (p.R + BM - 1) / BM;
     p.tiles_j = (p.S + BN - 1) / BN;
     const unsigned grid = (unsigned)(p.tiles_i * p.tiles_j);
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, OCC, AKM, BKM, EPI>), dim3(grid),
-                       dim3(WM * WN * 64), 0, st, p);
+    if (p.ws_mode != 0) {
+        if constexpr (EPI != EPI_RAW)
+            hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, OCC, AKM, BKM, EPI, true>),
+                               dim3(grid), dim3(WM * WN * 64), 0, st, p);
+    } else {
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, OCC, AKM, BKM, EPI, false>),
+                           dim3(grid), dim3(WM * WN * 64), 0, st, p);
+    }
 }
 
 // Forward product for M <= 16 (decode-like shapes): the weight is streamed
@@ -614,8 +684,10 @@ void launch_product(const ProductArgs &a, hipStream_t st)
     p.srow = a.srow;
     p.scol = a.scol;
     p.bias = a.bias;
+    p.ws = a.ws;
+    p.ws_mode = a.ws_mode;
     if (a.op == 0) {
-        if (a.M <= 16) {
+        if (a.M <= 16 && a.ws_mode == 0) {
             const unsigned grid = (unsigned)(a.N / 16);
             if (a.raw)
                 hipLaunchKernelGGL(skinny_fwd_kernel<true>, dim3(grid), dim3(256), 0, st, a.a,
@@ -629,7 +701,7 @@ void launch_product(const ProductArgs &a, hipStream_t st)
         }
         p.a = a.a; p.lda = a.K;
         p.b = a.b; p.ldb = a.K;
-        p.R = (int)a.M; p.S = (int)a.N; p.T = (int)a.K; p.ldc = a.N;
+        p.R = (int)a.M; p.S = (int)a.N; p.T = (int)(a.t_len ? a.t_len : a.K); p.ldc = a.N;
         if (a.raw)
             run_cfg<false, false, EPI_RAW>(p, st);
         else
@@ -637,7 +709,7 @@ void launch_product(const ProductArgs &a, hipStream_t st)
     } else if (a.op == 1) {
         p.a = a.a; p.lda = a.N;
         p.b = a.b; p.ldb = a.K;
-        p.R = (int)a.M; p.S = (int)a.K; p.T = (int)a.N; p.ldc = a.K;
+        p.R = (int)a.M; p.S = (int)a.K; p.T = (int)(a.t_len ? a.t_len : a.N); p.ldc = a.K;
         if (a.raw) {
             run_cfg<false, true, EPI_RAW>(p, st);
         } else if (a.had >= 2 && a.had <= 128) {
@@ -651,11 +723,40 @@ void launch_product(const ProductArgs &a, hipStream_t st)
     } else {
         p.a = a.a; p.lda = a.N;
         p.b = a.b; p.ldb = a.K;
-        p.R = (int)a.N; p.S = (int)a.K; p.T = (int)a.M; p.ldc = a.K;
+        p.R = (int)a.N; p.S = (int)a.K; p.T = (int)(a.t_len ? a.t_len : a.M); p.ldc = a.K;
         if (a.raw)
             run_cfg<true, true, EPI_RAW>(p, st);
         else
             run_cfg<true, true, EPI_ROWSCALE>(p, st);
+    }
+}
+
+// Products whose contraction exceeds the int32-exact bound: chunks of 1023
+// stages (130,944 terms, within the bound) run as ordinary products on the
+// operands' sub-ranges; the first stores its int32 sums into the int64
+// workspace, the middle ones add theirs, and the last one's epilogue takes
+// acc + workspace through the usual dequant (and rotation) arithmetic.
+void launch_product_long(const ProductArgs &a, int64_t *ws, hipStream_t st)
+{
+    constexpr int64_t kChunk = 1023 * 128;
+    const int64_t T = a.op == 0 ? a.K : (a.op == 1 ? a.N : a.M);
+    for (int64_t k0 = 0; k0 < T; k0 += kChunk) {
+        ProductArgs c = a;
+        const int64_t len = T - k0 < kChunk ? T - k0 : kChunk;
+        c.t_len = len;
+        c.ws = ws;
+        c.ws_mode = k0 == 0 ? 1 : (k0 + len >= T ? 3 : 2);
+        if (a.op == 0) {
+            c.a = a.a + k0;
+            c.b = a.b + k0;
+        } else if (a.op == 1) {
+            c.a = a.a + k0;
+            c.b = a.b + k0 * a.K;
+        } else {
+            c.a = a.a + k0 * a.N;
+            c.b = a.b + k0 * a.K;
+        }
+        launch_product(c, st);
     }
 }
 

@@ -41,9 +41,16 @@ struct ProductArgs {
     bool raw;           // int32 accumulators instead of dequantized floats
     int had = 0;        // dX only: rotate each output row in blocks of 'had' (<= 128)
     float had_scale = 1.0f;
+    int64_t t_len = 0;        // contraction length of this launch (0: the full one)
+    int64_t *ws = nullptr;    // int64 running sums of a split contraction
+    int ws_mode = 0;          // 0 none, 1 store, 2 add, 3 finish from acc + ws
 };
 
 void launch_product(const ProductArgs &p, hipStream_t st);
+
+// A product whose contraction exceeds the int32 bound, in chunks combined in
+// the int64 workspace ws [rows, cols] (8 bytes per output).
+void launch_product_long(const ProductArgs &p, int64_t *ws, hipStream_t st);
 
 void launch_sgd_requant(int8_t *qw, float *sw, const float *dw, int64_t N, int64_t K, float lr,
                         uint64_t seed, uint64_t step, float *bias, const float *db,
