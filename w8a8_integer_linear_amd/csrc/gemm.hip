@@ -12,11 +12,12 @@
 //   dX       A = qg1 [M,N] row, B = qw [N,K] km (t = n)   C = dx [M,K]
 //   dW       A = qg2 [M,N] km,  B = qx [M,K] km (t = m)   C = dw [N,K]
 //
-// Tiles of BM x BN outputs and 64 contraction bytes per stage are copied
-// straight from global memory into LDS by 16-byte buffer loads, in the layout
-// they have in memory (XOR-swizzled at 16-byte granularity), through a ring of
-// up to four stages so that several stages of loads are in flight while one
-// is multiplied.  Fragments for v_mfma_i32_32x32x32_i8 are read with
+// Tiles of BM x BN outputs (256 x 256) and kBK (128) contraction bytes per
+// stage are copied straight from global memory into LDS by 16-byte buffer
+// loads, in the layout they have in memory (XOR-swizzled at 16-byte
+// granularity), through a ring of stages (two at 128 bytes, as many as fit in
+// 160 KiB of LDS, at most four) so the next stage's loads are in flight while
+// one is multiplied.  Fragments for v_mfma_i32_32x32x32_i8 are read with
 // ds_read_b128 from a row operand and with two ds_read_b64_tr_b8 from a km
 // operand: in each 16-lane group the transpose read hands lane i byte i & 7
 // of the row addressed by lane 2e + (i >> 3) as its byte e, so pointing lane
@@ -26,14 +27,15 @@
 //
 // Exactness: int32 accumulation of int8 products is exact for contractions up
 // to 131,071 and does not depend on the order of k, so the placement of k
-// inside a fragment only has to agree between A and B, which it does.
+// inside a fragment only has to agree between A and B, which it does.  Longer
+// contractions run in chunks whose int32 sums are combined in an int64
+// workspace (the WS kernel variant, launch_product_long).
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace qlin {
 
 namespace {
-
 
 typedef int i32x2v __attribute__((ext_vector_type(2)));
 

@@ -1,9 +1,10 @@
 // Row and column INT8 quantizers and the block-Hadamard rotation.
 //
 // Row quantization (OneTrainer PR #1681: activations rotated along the
-// contraction dimension and quantized per row on every call): one workgroup
-// per row, the row held in registers (eight consecutive elements per lane),
-// rotation done with in-lane and cross-lane butterflies, absmax reduced over
+// contraction dimension and quantized per row on every call): a workgroup
+// holds one row at a time in registers (eight consecutive elements per lane)
+// and walks rows grid-stride with the next row's loads in flight; rotation is
+// done with in-lane and cross-lane (DPP) butterflies, the absmax reduced over
 // the workgroup, then codes written as packed bytes.  One HBM read of x and
 // one write of q.
 //
@@ -11,7 +12,12 @@
 // product's output axis): pass 1 reduces |x * prescale[r]| over row slabs and
 // merges slabs with an order-free integer atomicMax on the fp32 bits of the
 // non-negative maxima; a tiny kernel turns maxima into scales; pass 2
-// quantizes elementwise.
+// quantizes elementwise.  Both quantizations of dY in one call share the read
+// of pass 1 with the row quantizer (column partials per workgroup, then a
+// reduce).
+//
+// Also here: the standalone rotation and the weight export (dequantize and
+// rotate back).
 #include <type_traits>
 
 #include "common.hpp"
