@@ -115,6 +115,62 @@ def test_mlp_layer_step(orc, which):
                 np.random.default_rng(10 + which))
 
 
+def _gelu64(h):
+    from scipy.special import erf
+    h = h.astype(np.float64)
+    return 0.5 * h * (1.0 + erf(h / np.sqrt(2.0)))
+
+
+def _gelu_grad64(h):
+    from scipy.special import erf
+    h = h.astype(np.float64)
+    return 0.5 * (1.0 + erf(h / np.sqrt(2.0))) + h * np.exp(-0.5 * h * h) / np.sqrt(2 * np.pi)
+
+
+def test_mlp_chain(orc):
+    """The transformer MLP chained on the GPU (8192 tokens: fc1 4096 -> 14336,
+    erf-GELU in fp32, fc2 14336 -> 4096; forward, backward to the input).  The
+    output and the input gradient of each row depend only on that row, so the
+    oracle recomputes 48 sampled rows from the seeded inputs, with the GELU in
+    float64.  The GELU is outside the INT8 path (the GPU's fp32 erf and libm
+    differ in the last bits), so rows are compared by a tight norm tolerance:
+    a GELU ulp can only move a code across a rounding boundary."""
+    import torch
+    from w8a8_integer_linear_amd import LinearW8A8Training
+    T = torch_cuda()
+    d = workloads.mlp()
+    announce("mlp chain", 8192)
+    fc1 = LinearW8A8Training(dev(d["w1"]), had_block=128, max_tokens=8192)
+    fc2 = LinearW8A8Training(dev(d["w2"]), had_block=128, max_tokens=8192)
+    h = fc1.forward(dev(d["x"])).clone()
+    a = torch.nn.functional.gelu(h)
+    y = fc2.forward(a).clone()
+    da = fc2.backward(dev(d["dy2"])).clone()
+    hh = h.double()
+    gp = 0.5 * (1 + torch.erf(hh / 2 ** 0.5)) + hh * torch.exp(-0.5 * hh * hh) / (2 * torch.pi) ** 0.5
+    dh = (da.double() * gp).float()
+    dx = fc1.backward(dh.contiguous())
+    T.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(21).choice(8192, 48, replace=False))
+    qw1, sw1 = orc.prepare_weight(d["w1"], had_block=128)
+    qw2, sw2 = orc.prepare_weight(d["w2"], had_block=128)
+    qx, sx = orc.quantize_rows(d["x"][rows], had_block=128)
+    h_ref = orc.fwd(qx, sx, qw1, sw1)
+    assert_bitwise(host(h)[rows], h_ref, "fc1 output")          # exact up to the GELU
+    a_ref = _gelu64(h_ref).astype(np.float32)
+    qa, sa = orc.quantize_rows(a_ref, had_block=128)
+    y_ref = orc.fwd(qa, sa, qw2, sw2)
+    qg, sg = orc.quantize_rows(d["dy2"][rows], prescale=sw2)
+    da_ref = orc.hadamard(orc.bwd_dx(qg, sg, qw2), 128)
+    assert_bitwise(host(da)[rows], da_ref, "fc2 input gradient")
+    dh_ref = (da_ref.astype(np.float64) * _gelu_grad64(h_ref)).astype(np.float32)
+    qg1, sg1 = orc.quantize_rows(dh_ref, prescale=sw1)
+    dx_ref = orc.hadamard(orc.bwd_dx(qg1, sg1, qw1), 128)
+    for name, got, ref in (("y", host(y)[rows], y_ref), ("dx", host(dx)[rows], dx_ref)):
+        err = np.linalg.norm(got.astype(np.float64) - ref, axis=1)
+        assert np.all(err <= 1e-3 * np.linalg.norm(ref.astype(np.float64), axis=1)), name
+
+
 def test_deterministic(orc):
     """Two runs of the headline step give bitwise identical results."""
     T = torch_cuda()
