@@ -179,11 +179,21 @@ def test_dequantize_weight_validation(L):
 def test_product_ws_validation(L):
     _cpu_only()
     F = lambda i: (i + 1) << 33     # widely spaced fake addresses
-    assert L.qlin_product_ws_bytes(2, 200000, 16, 32) == 8 * 16 * 32
-    assert L.qlin_product_ws_bytes(2, 1000, 16, 32) == 0
-    assert L.qlin_product_ws_bytes(0, 4, 16, 262144) == 8 * 4 * 16
+    C, BLK = 4096, 256 * 256 * 4       # counter area; one tile of int32 partial sums
+    # beyond the int32 bound: the counter area, then 8 bytes per output
+    assert L.qlin_product_ws_bytes(2, 200000, 16, 32) == C + 8 * 16 * 32
+    assert L.qlin_product_ws_bytes(0, 4, 16, 262144) == C + 8 * 4 * 16
+    # within it: the partial sums of the split tiles of the last round
+    assert L.qlin_product_ws_bytes(0, 12000, 7168, 5376) == C + 36 * 3 * BLK  # 1316 tiles
+    assert L.qlin_product_ws_bytes(1, 12000, 7168, 5376) == 0     # 987 tiles: 219 left, no split
+    assert L.qlin_product_ws_bytes(2, 12000, 7168, 5376) == C + 76 * 2 * BLK  # 588 tiles
+    assert L.qlin_product_ws_bytes(2, 8192, 14336, 4096) == 0     # 896 tiles: 128 left, 2 x 128 > 160
+    assert L.qlin_product_ws_bytes(2, 1000, 16, 32) == C + 2 * BLK   # 8 stages in 2 pieces
+    assert L.qlin_product_ws_bytes(2, 100, 16, 32) == 0           # one stage: nothing to split
+    assert L.qlin_product_ws_bytes(0, 16, 7168, 5376) == 0        # weight-streaming kernel
+    assert L.qlin_product_ws_bytes(0, 1792, 7168, 5376) == 0      # 196 tiles: 256 / 196 < 2 pieces
     # op, a, srow, b, scol, bias, M, N, K, had, out, ws, ws_bytes
-    long_dw = [2, F(0), F(1), F(2), None, None, 200000, 16, 32, 0, F(3), F(4), 8 * 16 * 32]
+    long_dw = [2, F(0), F(1), F(2), None, None, 200000, 16, 32, 0, F(3), F(4), C + 8 * 16 * 32]
     def call(**kw):
         a = list(long_dw)
         names = ["op", "a", "srow", "b", "scol", "bias", "M", "N", "K", "had", "out", "ws",
@@ -195,7 +205,13 @@ def test_product_ws_validation(L):
     assert call(scol=F(5)) == 1                     # column scales: forward only
     assert call(had=128) == 1                       # rotation: dX only
     assert call(ws=None) == 1                       # a long contraction needs the workspace
-    assert call(ws_bytes=8 * 16 * 32 - 8) == 1      # too small
+    assert call(ws_bytes=C + 8 * 16 * 32 - 8) == 1  # too small
     assert call(ws=F(3) + 16) == 1                  # overlaps the output
     assert call(K=24) == 1
     assert call(M=1 << 31) == 2                     # beyond the longest contraction
+    # a within-bound product that splits its last round needs the workspace
+    need = C + 36 * 3 * BLK
+    split_fwd = dict(op=0, M=12000, N=7168, K=5376, scol=F(5), ws_bytes=need)
+    assert call(**split_fwd, ws=None) == 1
+    assert call(**{**split_fwd, "ws_bytes": need - 1}) == 1
+    assert call(**split_fwd, ws=F(3) + 64) == 1      # overlaps the output

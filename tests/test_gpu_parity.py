@@ -382,6 +382,66 @@ def test_product_ws_within_bound_is_the_plain_call(T, Q, orc):
     assert_bitwise(host(a), host(b), "dW")
 
 
+SPLIT_CASES = [
+    # op, M, N, K, had, bias.  A grid of more tiles than one round of the chip
+    # (256) leaves a partial last round; with a workspace those tiles are split
+    # along the contraction (here 272 tiles: 256 whole, 16 in 3 pieces each).
+    (0, 4352, 4096, 4096, 0, True),
+    (1, 4352, 4096, 4096, 128, False),   # rotation in the epilogue of the last piece
+    (2, 4096, 4352, 4096, 0, False),
+    # Fewer tiles than one round: every tile split; ragged rows, columns and
+    # contraction (the last piece of a dW split gets the partial stage).
+    (0, 700, 1040, 1008, 0, True),
+    (2, 3000, 1040, 528, 0, False),
+    (1, 600, 2048, 512, 64, False),
+    (1, 300, 1024, 1024, 256, False),    # rotation too wide to fuse: separate pass
+]
+
+
+@pytest.mark.parametrize("op,M,N,K,had,with_bias", SPLIT_CASES)
+def test_product_split_tail(T, Q, orc, op, M, N, K, had, with_bias):
+    """Products through the workspace entry point with their last round of
+    tiles split along the contraction: bitwise equal to the ordinary call over
+    the whole output (twice on one workspace, whose arrival counters the
+    first call must leave at zero), and to the oracle on whole sampled output
+    rows, taken from the split tiles and from whole ones."""
+    rng = np.random.default_rng(op * 1009 + M + K)
+    need = Q.qlin_product_ws_bytes(op, M, N, K)
+    assert need > 0, "the case must split"
+    sa = (M, K) if op == 0 else (M, N)
+    sb = (N, K) if op in (0, 1) else (M, K)
+    a, b = _codes(rng, sa), _codes(rng, sb)
+    R, C = {0: (M, N), 1: (M, K), 2: (N, K)}[op]
+    srow = rng.uniform(1e-4, 1e-2, R).astype(np.float32)
+    scol = rng.uniform(1e-2, 1e-1, N).astype(np.float32) if op == 0 else None
+    bias = rng.standard_normal(N).astype(np.float32) if with_bias else None
+    da, db_, ds = dev(a), dev(b), dev(srow)
+    dsc = None if scol is None else dev(scol)
+    dbias = None if bias is None else dev(bias)
+    announce("split tail", op, M, N, K, had, need)
+    ws = T.zeros(need, dtype=T.uint8, device="cuda")
+    outs = [host(Q.qlin_product_ws(op, da, ds, db_, M, N, K, scol=dsc, bias=dbias,
+                                   had_block=had, workspace=ws)) for _ in range(2)]
+    if op == 0:
+        plain = Q.qlin_fwd(da, ds, db_, dsc, dbias)
+    elif op == 1:
+        plain = Q.qlin_bwd_dx(da, ds, db_, had_block=had)
+    else:
+        plain = Q.qlin_bwd_dw(da, ds, db_)
+    T.cuda.synchronize()
+    assert np.all(host(ws[:4096]) == 0), "arrival counters left non-zero"
+    plain = host(plain)
+    assert_bitwise(outs[0], plain, "split vs plain")
+    assert_bitwise(outs[1], plain, "second call on the workspace")
+    # whole output rows: the last two (in the last, split, tile row) and two others
+    rows = np.unique(np.r_[R - 1, R - 2, rng.integers(0, R, 2)])
+    ii, jj = np.repeat(rows, C), np.tile(np.arange(C), len(rows))
+    ref = orc.op_at(op, a, srow, b, scol, bias, M, N, K, ii, jj).reshape(len(rows), C)
+    if had:
+        ref = orc.hadamard(ref, had)
+    assert_bitwise(outs[0][rows], ref, "sampled rows")
+
+
 # ------------------------------------------------------------------ update
 
 SGD_CASES = [(128, 256, True), (64, 5376, False), (7, 16, True), (3, 20480, False),

@@ -270,8 +270,11 @@ def qlin_product_ws_bytes(op, M, N, K):
 
 def qlin_product_ws(op, a, srow, b, M, N, K, scol=None, bias=None, had_block=0, out=None,
                     workspace=None, stream=None):
-    """Any product with a contraction of any length (int32 chunks combined in
-    int64 in the workspace, allocated here when not given)."""
+    """Any product with a contraction of any length, using a caller workspace
+    (allocated zero-filled here when not given; a reused workspace comes back
+    from every call with its arrival counters zero again).  Within the int32
+    bound the workspace lets the last round of tiles be split along the
+    contraction; beyond it, int32 chunks are combined in int64 there."""
     shape = {QLIN_OP_FWD: (M, N), QLIN_OP_DX: (M, K), QLIN_OP_DW: (N, K)}[op]
     _need(a, "a", torch.int8)
     _need(b, "b", torch.int8)
@@ -282,7 +285,7 @@ def qlin_product_ws(op, a, srow, b, M, N, K, scol=None, bias=None, had_block=0, 
                                                                      shape)
     need = qlin_product_ws_bytes(op, M, N, K)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=a.device)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("qlin_product_ws", lib().qlin_product_ws(
         int(op), _ptr(a), _ptr(srow), _ptr(b), _ptr(scol), _ptr(bias), M, N, K, int(had_block),

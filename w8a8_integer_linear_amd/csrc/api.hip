@@ -261,9 +261,9 @@ size_t qlin_product_ws_bytes(int op, int64_t M, int64_t N, int64_t K)
         return 0;
     const int64_t contraction = op == QLIN_OP_FWD ? K : (op == QLIN_OP_DX ? N : M);
     if (contraction <= QLIN_MAX_CONTRACTION)
-        return 0;
+        return qlin::split_ws_bytes(qlin::split_plan(op, M, N, K));
     const int64_t rows = op == QLIN_OP_DW ? N : M, cols = op == QLIN_OP_FWD ? N : K;
-    return (size_t)(8 * rows * cols);
+    return qlin::kSplitCountBytes + (size_t)(8 * rows * cols);
 }
 
 int qlin_product_ws(int op, const int8_t *a, const float *srow, const int8_t *b,
@@ -277,7 +277,10 @@ int qlin_product_ws(int op, const int8_t *a, const float *srow, const int8_t *b,
     if (op != QLIN_OP_DX && had_block != 0)
         return QLIN_EINVAL;
     const int64_t contraction = op == QLIN_OP_FWD ? K : (op == QLIN_OP_DX ? N : M);
-    if (contraction <= QLIN_MAX_CONTRACTION) {
+    const bool is_long = contraction > QLIN_MAX_CONTRACTION;
+    const size_t need = qlin_product_ws_bytes(op, M, N, K);
+    if (!is_long && need == 0) {
+        // Nothing to balance: the ordinary product.
         if (op == QLIN_OP_FWD)
             return qlin_fwd(a, srow, b, scol, bias, M, N, K, out, stream);
         if (op == QLIN_OP_DX)
@@ -294,20 +297,26 @@ int qlin_product_ws(int op, const int8_t *a, const float *srow, const int8_t *b,
     if (!srow || (op == QLIN_OP_FWD && !scol))
         return QLIN_EINVAL;
     const int64_t rows = op == QLIN_OP_DW ? N : M, cols = op == QLIN_OP_FWD ? N : K;
-    const int64_t need = 8 * rows * cols;
     const int64_t la = op == QLIN_OP_FWD ? M * K : M * N, lb = op == QLIN_OP_DW ? M * K : N * K;
-    if (!workspace || !aligned16(workspace) || (int64_t)ws_bytes < need ||
-        overlap(workspace, need, out, 4 * rows * cols) || overlap(workspace, need, a, la) ||
-        overlap(workspace, need, b, lb))
+    const int64_t nb = (int64_t)need;
+    if (!workspace || !aligned16(workspace) || ws_bytes < need ||
+        overlap(workspace, nb, out, 4 * rows * cols) || overlap(workspace, nb, a, la) ||
+        overlap(workspace, nb, b, lb))
         return QLIN_EINVAL;
     qlin::ProductArgs p{op, a, b, M, N, K, srow, scol, bias, out, false};
     const hipStream_t s = as_stream(stream);
-    int64_t *ws = static_cast<int64_t *>(workspace);
     if (op == QLIN_OP_DX && had_block >= 2 && had_block <= 128) {
         p.had = had_block;
         p.had_scale = hadamard_scale(had_block);
     }
-    qlin::launch_product_long(p, ws, s);
+    if (is_long) {
+        int64_t *ws = reinterpret_cast<int64_t *>(static_cast<char *>(workspace) +
+                                                  qlin::kSplitCountBytes);
+        qlin::launch_product_long(p, ws, s);
+    } else {
+        p.split_ws = workspace;
+        qlin::launch_product(p, s);
+    }
     if (op == QLIN_OP_DX && had_block > 128)
         qlin::launch_hadamard(out, false, M, K, had_block, hadamard_scale(had_block), out, s);
     return finish();

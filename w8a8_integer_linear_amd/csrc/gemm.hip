@@ -29,7 +29,7 @@
 // to 131,071 and does not depend on the order of k, so the placement of k
 // inside a fragment only has to agree between A and B, which it does.  Longer
 // contractions run in chunks whose int32 sums are combined in an int64
-// workspace (the WS kernel variant, launch_product_long).
+// workspace (the MODE_CHUNK kernel variant, launch_product_long).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -56,6 +56,14 @@ struct GemmParams {
     // them; 3: the epilogue takes acc + ws (the last chunk).
     int64_t *ws;
     int ws_mode;
+    // Balanced last round (MODE_SPLIT): work units [0, full) are whole tiles;
+    // each tile after them is covered by 'split' units, each owning a range
+    // of its contraction stages.  part holds one BM x BN block of int32
+    // partial sums per such unit; count[u] counts the units of tail tile u
+    // that have stored theirs (returned to zero by the last one).
+    int full, split;
+    int32_t *part;
+    unsigned *count;
 };
 
 // ------------------------------------------------------------------ staging
@@ -65,6 +73,9 @@ struct GemmParams {
 // the buffer range check turns into a zero fill of the lane's 16 LDS bytes.
 constexpr uint32_t kOob = 0x7FFFFFF0u;
 constexpr int kRsrcWord3 = 0x00020000;   // raw 32-bit buffer format
+// Cache policy of buffer accesses that must be coherent across the XCDs'
+// L2s (sc1, the device-scope bit).
+constexpr int kCoherent = 16;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const int8_t *base)
 {
@@ -223,16 +234,20 @@ enum { EPI_RAW = 0, EPI_ROWSCALE = 1, EPI_FWD = 2, EPI_ROWSCALE_HAD = 3 };
 
 // Tile order: workgroups are dispatched round-robin over the 8 XCDs, so
 // consecutive ids are first regrouped per XCD (each XCD gets a contiguous
-// range of tiles), then walked in groups of kGroup tile rows so that tiles
-// running together share their A rows and B columns in that XCD's L2.
+// range of the first n tiles), then walked in groups of kGroup tile rows so
+// that tiles running together share their A rows and B columns in that XCD's
+// L2.
 constexpr int kGroup = 8;
 
-__device__ __forceinline__ void tile_of(int pid, int tiles_i, int tiles_j, int &ti, int &tj)
+__device__ __forceinline__ int xcd_order(int pid, int n)
 {
-    const int n = tiles_i * tiles_j;
     const int q = n / 8, rem = n % 8;
     const int xcd = pid % 8, idx = pid / 8;
-    const int lin = xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
+    return xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
+}
+
+__device__ __forceinline__ void tile_at(int lin, int tiles_i, int tiles_j, int &ti, int &tj)
+{
     const int per_group = kGroup * tiles_j;
     const int g = lin / per_group;
     const int first = g * kGroup;
@@ -244,10 +259,14 @@ __device__ __forceinline__ void tile_of(int pid, int tiles_i, int tiles_j, int &
 
 // ------------------------------------------------------------------- kernel
 
-// WS: the launch is one chunk of a split contraction (ws_mode 1-3); kernels
-// of ordinary launches carry no workspace code.
+// Launch modes.  MODE_CHUNK: the launch is one chunk of a contraction longer
+// than the int32 bound (ws_mode 1-3).  MODE_SPLIT: the tiles left over after
+// the last whole round of the grid are split along the contraction (full,
+// split, part, count).  Ordinary launches carry neither's code.
+enum { MODE_PLAIN = 0, MODE_CHUNK = 1, MODE_SPLIT = 2 };
+
 template <int BM, int BN, int WM, int WN, int kBK, int OCC, bool AKM, bool BKM, int EPI,
-          bool WS>
+          int MODE>
 __global__ __launch_bounds__(WM *WN * 64, OCC) void gemm_kernel(GemmParams p)
 {
     constexpr int NT = WM * WN * 64;
@@ -262,8 +281,21 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void gemm_kernel(GemmParams p)
     constexpr int kLoads = OpA::kLoads + OpB::kLoads;     // per lane per stage
     __shared__ __attribute__((aligned(1024))) int8_t smem[kStages * kStage];
 
+    // Work unit -> tile and range of contraction stages [kb, kb + KT).
+    const int KT_all = (p.T + kBK - 1) / kBK;
+    int lin, kb = 0, KT = KT_all, tail = -1, piece = 0;
+    if (MODE == MODE_SPLIT && (int)blockIdx.x >= p.full) {
+        const int q = (int)blockIdx.x - p.full;
+        tail = q / p.split;
+        piece = q % p.split;
+        lin = p.full + tail;
+        kb = piece * KT_all / p.split;
+        KT = (piece + 1) * KT_all / p.split - kb;
+    } else {
+        lin = xcd_order(blockIdx.x, MODE == MODE_SPLIT ? p.full : p.tiles_i * p.tiles_j);
+    }
     int ti, tj;
-    tile_of(blockIdx.x, p.tiles_i, p.tiles_j, ti, tj);
+    tile_at(lin, p.tiles_i, p.tiles_j, ti, tj);
     const int i0 = ti * BM, j0 = tj * BN;
     const int lane = __lane_id();
     const int w = threadIdx.x / kWave;
@@ -275,13 +307,13 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void gemm_kernel(GemmParams p)
     const int8_t *bbase = BKM ? p.b + j0 : p.b + (int64_t)j0 * p.ldb;
     const int alim = p.R - i0, blim = p.S - j0;
 
-    const int KT = (p.T + kBK - 1) / kBK;
-    // Stage s of the contraction goes to buffer s % kStages.  Stages past the
-    // end are issued as all-out-of-range loads (zero fills of a buffer that is
-    // never read) so every iteration waits for the same number of loads.
+    // Stage s of the unit (stage kb + s of the contraction) goes to buffer
+    // s % kStages.  Stages past the end are issued as all-out-of-range loads
+    // (zero fills of a buffer that is never read) so every iteration waits
+    // for the same number of loads.
     auto issue = [&](int s) {
         const bool live = s < KT;
-        const int k0 = live ? s * kBK : 0;
+        const int k0 = live ? (kb + s) * kBK : 0;
         int8_t *dst = smem + (s % kStages) * kStage;
         const int8_t *ak = AKM ? abase + (int64_t)k0 * p.lda : abase;
         const int8_t *bk = BKM ? bbase + (int64_t)k0 * p.ldb : bbase;
@@ -392,7 +424,7 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void gemm_kernel(GemmParams p)
     // Four consecutive int64 running sums of row i from column j, or zeros
     // when this is not the last chunk of a split contraction.
     auto ws4 = [&](int i, int j, int64_t e[4]) {
-        if (WS && p.ws_mode == 3 && j < p.S) {
+        if (MODE == MODE_CHUNK && p.ws_mode == 3 && j < p.S) {
             const i64x2 *w = reinterpret_cast<const i64x2 *>(ws_at(i, j));
             const i64x2 lo = w[0], hi = w[1];
             e[0] = lo[0]; e[1] = lo[1]; e[2] = hi[0]; e[3] = hi[1];
@@ -402,12 +434,103 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void gemm_kernel(GemmParams p)
     };
     // fl32 of the accumulator (plus the running sum of earlier chunks).
     auto tofloat = [&](int32_t c, int64_t e) {
-        if constexpr (WS)
+        if constexpr (MODE == MODE_CHUNK)
             return p.ws_mode == 3 ? (float)((int64_t)c + e) : (float)c;
         else
             return (float)c;
     };
-    if constexpr (WS && EPI != EPI_RAW) {
+    if constexpr (MODE == MODE_SPLIT) {
+        if (tail >= 0) {
+            // Store this unit's int32 sums in register order (coalesced
+            // 16-byte runs) and count its arrival; the last of the tile's
+            // units to arrive adds the others' sums (exact: int32 addition of
+            // bounded partials) and runs the epilogue.
+            //
+            // The partial sums cross XCDs, whose L2s are not coherent with
+            // one another.  They are written and read with the device-scope
+            // coherence bit (sc1: the bit a device-scope relaxed atomic access
+            // carries), so they never sit in an L2 as stale or dirty lines;
+            // each wave waits for its stores to complete before the barrier
+            // that precedes the arrival count, and the reader's loads are
+            // issued after it observes the count.  A device-scope fence would
+            // do the same by writing back and invalidating whole L2s, which
+            // stalls the chip while the rest of the grid is still storing
+            // outputs.
+            //
+            // The arrival flag lives in the stage buffers, free once every
+            // wave has passed the barrier below: a second LDS object would
+            // make the compiler wait for each stage's buffer-to-LDS loads
+            // before any LDS read.
+            int *last_unit = reinterpret_cast<int *>(smem);
+            // Unit o's sums: wave w's FM x FN x 4 16-byte slots per lane, the
+            // wave's slots contiguous.  Buffer resources start at this wave's
+            // run (so slot offsets are constants); an empty resource reads
+            // zeros.
+            constexpr int kSlots = FM * FN * 4;
+            const int wave = __builtin_amdgcn_readfirstlane(w);
+            auto part_rsrc = [&](int o) {
+                const int32_t *base = p.part + ((int64_t)tail * p.split + o) * (BM * BN) +
+                                      (int64_t)wave * kSlots * kWave * 4;
+                return make_rsrc(reinterpret_cast<const int8_t *>(base));
+            };
+            const uint32_t lane_off = (uint32_t)lane * 16;
+            const __amdgpu_buffer_rsrc_t mine = part_rsrc(piece);
+#pragma unroll
+            for (int a = 0; a < FM; a++)
+#pragma unroll
+                for (int b = 0; b < FN; b++)
+#pragma unroll
+                    for (int g = 0; g < 4; g++) {
+                        const int slot = (a * FN + b) * 4 + g;
+                        const i32x16 &c = acc[a][b];
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            i32x4{c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]}, mine,
+                            lane_off, slot * kWave * 16, kCoherent);
+                    }
+            wait_vmcnt<0>();
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                const unsigned arrived = atomicAdd(p.count + tail, 1u);
+                *last_unit = arrived == (unsigned)(p.split - 1);
+                if (*last_unit)
+                    atomicExch(p.count + tail, 0u);
+            }
+            __syncthreads();
+            if (!*last_unit)
+                return;
+            // The other units' sums, four units at a time: sixteen 16-byte
+            // loads per lane in flight per accumulator block.
+            const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<int32_t *>(p.part), (short)0, 0, kRsrcWord3);
+            for (int o0 = 0; o0 < p.split; o0 += 4) {
+                __amdgpu_buffer_rsrc_t rs[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    rs[u] = o0 + u < p.split && o0 + u != piece ? part_rsrc(o0 + u) : none;
+#pragma unroll
+                for (int a = 0; a < FM; a++)
+#pragma unroll
+                    for (int b = 0; b < FN; b++) {
+                        i32x4 t[4][4];
+#pragma unroll
+                        for (int u = 0; u < 4; u++)
+#pragma unroll
+                            for (int g = 0; g < 4; g++)
+                                t[u][g] = __builtin_amdgcn_raw_buffer_load_b128(
+                                    rs[u], lane_off, ((a * FN + b) * 4 + g) * kWave * 16,
+                                    kCoherent);
+#pragma unroll
+                        for (int u = 0; u < 4; u++)
+#pragma unroll
+                            for (int g = 0; g < 4; g++)
+#pragma unroll
+                                for (int e = 0; e < 4; e++)
+                                    acc[a][b][4 * g + e] += t[u][g][e];
+                    }
+            }
+        }
+    }
+    if constexpr (MODE == MODE_CHUNK && EPI != EPI_RAW) {
         if (p.ws_mode == 1 || p.ws_mode == 2) {
 #pragma unroll
             for (int a = 0; a < FM; a++) {
@@ -590,14 +713,19 @@ void run_gemm(const GemmParams &p0, hipStream_t st)
     GemmParams p = p0;
     p.tiles_i = (p.R + BM - 1) / BM;
     p.tiles_j = (p.S + BN - 1) / BN;
-    const unsigned grid = (unsigned)(p.tiles_i * p.tiles_j);
+    const int tiles = p.tiles_i * p.tiles_j;
     if (p.ws_mode != 0) {
         if constexpr (EPI != EPI_RAW)
-            hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, OCC, AKM, BKM, EPI, true>),
+            hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, OCC, AKM, BKM, EPI, MODE_CHUNK>),
+                               dim3(tiles), dim3(WM * WN * 64), 0, st, p);
+    } else if (p.split >= 2) {
+        const unsigned grid = (unsigned)(p.full + (tiles - p.full) * p.split);
+        if constexpr (EPI != EPI_RAW)
+            hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, OCC, AKM, BKM, EPI, MODE_SPLIT>),
                                dim3(grid), dim3(WM * WN * 64), 0, st, p);
     } else {
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, OCC, AKM, BKM, EPI, false>),
-                           dim3(grid), dim3(WM * WN * 64), 0, st, p);
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, OCC, AKM, BKM, EPI, MODE_PLAIN>),
+                           dim3(tiles), dim3(WM * WN * 64), 0, st, p);
     }
 }
 
@@ -679,6 +807,50 @@ void run_cfg(const GemmParams &p, hipStream_t st)
 
 } // namespace
 
+// Compute units of the chip: each runs one workgroup of the 256 x 256 tile
+// configuration at a time, so a grid runs in rounds of this many tiles.
+constexpr int kRound = 256;
+// Fewest contraction stages a piece of a split tile gets, most pieces per
+// tile, and most pieces in the balanced round.  The last round's pieces
+// share no operand data with one another, so a nearly full round of them runs
+// slower than a partly full one, and every piece past the first adds a 256 KiB
+// partial that the last one must read: on the 12000 x 5376 x 7168 products
+// three pieces (forward, 36 tiles left) and two (dW, 76 tiles left) measured
+// best.
+constexpr int kMinPieceStages = 4;
+constexpr int kMaxPieces = 3;
+constexpr int kMaxPieceUnits = 160;
+
+SplitPlan split_plan(int op, int64_t M, int64_t N, int64_t K)
+{
+    SplitPlan none{0, 0, 1};
+    if (op == 0 && M <= 16)
+        return none;    // weight-streaming kernel
+    const int64_t R = op == 2 ? N : M, S = op == 0 ? N : K, T = op == 0 ? K : (op == 1 ? N : M);
+    const int64_t tiles = ((R + 255) / 256) * ((S + 255) / 256);
+    const int64_t full = tiles / kRound * kRound, tail = tiles - full;
+    if (tail == 0)
+        return none;
+    int64_t split = kRound / tail;
+    const int64_t by_len = ((T + 127) / 128) / kMinPieceStages;
+    split = split < by_len ? split : by_len;
+    split = split < kMaxPieces ? split : kMaxPieces;
+    if (split > 2 && tail * split > kMaxPieceUnits)
+        split--;
+    if (split == 2 && tail * split > kMaxPieceUnits)
+        split = 1;
+    if (split < 2)
+        return none;
+    return SplitPlan{(int)full, (int)tail, (int)split};
+}
+
+size_t split_ws_bytes(const SplitPlan &sp)
+{
+    if (sp.split < 2)
+        return 0;
+    return kSplitCountBytes + (size_t)sp.tail * sp.split * 256 * 256 * sizeof(int32_t);
+}
+
 void launch_product(const ProductArgs &a, hipStream_t st)
 {
     GemmParams p{};
@@ -688,6 +860,17 @@ void launch_product(const ProductArgs &a, hipStream_t st)
     p.bias = a.bias;
     p.ws = a.ws;
     p.ws_mode = a.ws_mode;
+    p.split = 1;
+    if (a.split_ws && !a.raw && a.ws_mode == 0) {
+        const SplitPlan sp = split_plan(a.op, a.M, a.N, a.K);
+        if (sp.split >= 2) {
+            p.full = sp.full;
+            p.split = sp.split;
+            p.count = static_cast<unsigned *>(a.split_ws);
+            p.part = reinterpret_cast<int32_t *>(static_cast<char *>(a.split_ws) +
+                                                 kSplitCountBytes);
+        }
+    }
     if (a.op == 0) {
         if (a.M <= 16 && a.ws_mode == 0) {
             const unsigned grid = (unsigned)(a.N / 16);

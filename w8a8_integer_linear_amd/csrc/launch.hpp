@@ -44,9 +44,24 @@ struct ProductArgs {
     int64_t t_len = 0;        // contraction length of this launch (0: the full one)
     int64_t *ws = nullptr;    // int64 running sums of a split contraction
     int ws_mode = 0;          // 0 none, 1 store, 2 add, 3 finish from acc + ws
+    // Workspace for balancing the last round of tiles (split_plan): arrival
+    // counters in its first kSplitCountBytes (zero on entry, zero on exit),
+    // then the pieces' int32 partial sums.  Null: no balancing.
+    void *split_ws = nullptr;
 };
 
 void launch_product(const ProductArgs &p, hipStream_t st);
+
+// How a product balances its last round of 256 x 256 tiles over the chip:
+// 'full' whole tiles, then each of the 'tail' remaining tiles in 'split'
+// pieces along the contraction (split 1: no balancing).
+struct SplitPlan {
+    int full, tail, split;
+};
+constexpr size_t kSplitCountBytes = 4096;
+SplitPlan split_plan(int op, int64_t M, int64_t N, int64_t K);
+// Workspace bytes the plan needs (0 when it splits nothing).
+size_t split_ws_bytes(const SplitPlan &sp);
 
 // A product whose contraction exceeds the int32 bound, in chunks combined in
 // the int64 workspace ws [rows, cols] (8 bytes per output).

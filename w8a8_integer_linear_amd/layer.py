@@ -8,12 +8,18 @@ saved INT8 input (qx, sx) of the last forward.  Buffers for up to
 
 Step order of one training step:
   forward   qlin_quantize_rows(x, rotate)          -> qx, sx   (saved)
-            qlin_fwd(qx, sx, qw, sw, bias)         -> y
+            qlin_product_ws(FWD: qx, sx, qw, sw, bias)          -> y
   backward  qlin_quantize_grad(dY, sw, sx)         -> qg1, sg1 (rows of dY*sw),
                                                       qg2, sg2 (columns of dY*sx), db
-            qlin_bwd_dx(qg1, sg1, qw, rotate back) -> dx
-            qlin_bwd_dw(qg2, sg2, qx)              -> dw
+            qlin_product_ws(DX: qg1, sg1, qw, rotate back)      -> dx
+            qlin_product_ws(DW: qg2, sg2, qx)                   -> dw
   update    qlin_sgd_requant(qw, sw, dw, lr, seed, step, bias, db)
+
+The products go through the workspace entry point (the same kernels as
+qlin_fwd / qlin_bwd_dx / qlin_bwd_dw): its workspace, zero-filled once and
+shared by the three calls, lets each product split the tiles of its last
+partial round along the contraction, and takes contractions past the int32
+bound.
 """
 import torch
 
@@ -35,7 +41,20 @@ class LinearW8A8Training:
         self.max_tokens = 0
         self.dw = torch.empty((N, K), dtype=torch.float32, device=dev)
         self.db = None if bias is None else torch.empty(N, dtype=torch.float32, device=dev)
+        self._ws = torch.zeros(0, dtype=torch.uint8, device=dev)
+        self._ws_for = set()
         self._alloc(max_tokens, dev)
+
+    def _workspace(self, M):
+        """The shared product workspace, grown (zero-filled) to what the three
+        products need at M tokens."""
+        if M not in self._ws_for:
+            need = max(nat.qlin_product_ws_bytes(op, M, self.N, self.K)
+                       for op in (nat.QLIN_OP_FWD, nat.QLIN_OP_DX, nat.QLIN_OP_DW))
+            if need > self._ws.numel():
+                self._ws = torch.zeros(need, dtype=torch.uint8, device=self._ws.device)
+            self._ws_for.add(M)
+        return self._ws
 
     def _alloc(self, M, dev):
         if M <= self.max_tokens:
@@ -58,7 +77,9 @@ class LinearW8A8Training:
         self.qx, self.sx = nat.qlin_quantize_rows(x, had_block=self.had, q=self._qx[:M],
                                                   s=self._sx[:M])
         self._tick("quantize_x")
-        y = nat.qlin_fwd(self.qx, self.sx, self.qw, self.sw, self.bias, y=self._y[:M])
+        y = nat.qlin_product_ws(nat.QLIN_OP_FWD, self.qx, self.sx, self.qw, M, self.N, self.K,
+                                scol=self.sw, bias=self.bias, out=self._y[:M],
+                                workspace=self._workspace(M))
         self._tick("fwd")
         return y
 
@@ -69,9 +90,12 @@ class LinearW8A8Training:
             dy, self.sw, self.sx, q1=self._qg1[:M], s1=self._sg1[:M], q2=self._qg2[:M],
             s2=self._sg2, col_sum=self.db)
         self._tick("quantize_dy")
-        dx = nat.qlin_bwd_dx(qg1, sg1, self.qw, had_block=self.had, dx=self._dx[:M])
+        ws = self._workspace(M)
+        dx = nat.qlin_product_ws(nat.QLIN_OP_DX, qg1, sg1, self.qw, M, self.N, self.K,
+                                 had_block=self.had, out=self._dx[:M], workspace=ws)
         self._tick("bwd_dx")
-        nat.qlin_bwd_dw(qg2, sg2, self.qx, dw=self.dw)
+        nat.qlin_product_ws(nat.QLIN_OP_DW, qg2, sg2, self.qx, M, self.N, self.K, out=self.dw,
+                            workspace=ws)
         self._tick("bwd_dw")
         return dx
 
