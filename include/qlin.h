@@ -206,13 +206,20 @@ int qlin_bwd_dw(const int8_t *qg2, const float *sg2, const int8_t *qx, int64_t M
                 int64_t N, int64_t K, float *dw, void *stream);
 
 /*
- * Any of the three products with a contraction of any length up to 2^31 - 1
- * (mini_trainer guide, arithmetic paragraph: contractions above 131,071
- * combine bounded int32 dot products in int64 before scaling).  The
- * contraction is split into chunks of at most 131,071 terms whose exact int32
- * sums are combined in int64 in 'workspace'; fl32 of the int64 total then
- * goes through the product's usual epilogue.  Up to the bound the call is
- * exactly qlin_fwd / qlin_bwd_dx / qlin_bwd_dw and the workspace is unused.
+ * Any of the three products with a caller workspace: the same results, bit
+ * for bit, as qlin_fwd / qlin_bwd_dx / qlin_bwd_dw, for a contraction of any
+ * length up to 2^31 - 1.
+ *  - Beyond QLIN_MAX_CONTRACTION (mini_trainer guide, arithmetic paragraph:
+ *    contractions above 131,071 combine bounded int32 dot products in int64
+ *    before scaling) the contraction runs in chunks of at most 131,071 terms
+ *    whose exact int32 sums are combined in int64 in the workspace; fl32 of
+ *    the int64 total then goes through the product's usual epilogue.
+ *  - Within the bound the workspace balances the grid: the 256 x 256 output
+ *    tiles left over after the last whole round of the chip's 256 compute
+ *    units are each computed in two or three pieces along the contraction,
+ *    whose int32 partial sums (exact) are added by the last piece to finish
+ *    before the usual epilogue.  When a shape leaves nothing to balance,
+ *    qlin_product_ws_bytes is 0 and the workspace is not touched.
  *
  *   op        QLIN_OP_FWD: a = qx [M,K], srow = sx, b = qw [N,K], scol = sw,
  *                          bias optional, out = y [M,N], had_block = 0;
@@ -222,16 +229,22 @@ int qlin_bwd_dw(const int8_t *qg2, const float *sg2, const int8_t *qx, int64_t M
  *                          out = dw [N,K], had_block = 0.
  *             scol and bias must be NULL except for the forward product.
  *   workspace device memory of at least qlin_product_ws_bytes(op, M, N, K)
- *             bytes (8 per output element), 16-byte aligned, overlapping no
- *             other argument; its contents are scratch.
+ *             bytes, 16-byte aligned, overlapping no other argument (NULL
+ *             when that size is 0).  Its first 4096 bytes hold arrival
+ *             counters: they must be zero before the workspace's first use
+ *             (allocate it zero-filled), and every completed call leaves them
+ *             zero again.  The rest is scratch.  Calls that share a workspace
+ *             must not run concurrently.
  */
 int qlin_product_ws(int op, const int8_t *a, const float *srow, const int8_t *b,
                     const float *scol, const float *bias, int64_t M, int64_t N, int64_t K,
                     int had_block, float *out, void *workspace, size_t ws_bytes,
                     void *stream);
 
-/* Workspace bytes qlin_product_ws needs: 0 up to the int32 bound, else 8 per
- * output element.  Returns 0 for invalid arguments. */
+/* Workspace bytes qlin_product_ws needs for this shape: beyond the int32
+ * bound 4096 + 8 per output element; within it 4096 + 256 KiB per balancing
+ * piece (at most 160 pieces), or 0 when nothing is balanced.  Returns 0 for
+ * invalid arguments. */
 size_t qlin_product_ws_bytes(int op, int64_t M, int64_t N, int64_t K);
 
 /*
