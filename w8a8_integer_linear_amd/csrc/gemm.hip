@@ -329,10 +329,8 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void gemm_kernel(GemmParams p)
         for (int b = 0; b < FN; b++)
             acc[a][b] = i32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 
-    // Two fragment sets: the LDS reads of one are in flight while the MFMAs
-    // of the other run.  f0 holds contraction step 0 of a stage, f1 step 1.
-    typename OpA::Raw fa0[FM], fa1[FM];
-    typename OpB::Raw fb0[FN], fb1[FN];
+    // Fragment reads of contraction step kk of a stage (into fa, fb), their
+    // wait, and the MFMAs of one step.
     auto load = [&](const int8_t *stage, int kk, typename OpA::Raw *fa, typename OpB::Raw *fb) {
         const int8_t *lb = stage + OpA::kBytes;
 #pragma unroll

@@ -85,18 +85,38 @@ def busy_clock(out_dir):
             for k, vals in by.items()}, n_se, n_simd
 
 
+def bench_line(out_dir):
+    """The JSON line bench.py printed in the traced run (None if absent)."""
+    path = os.path.join(out_dir, "kt.log")
+    if not os.path.exists(path):
+        return None
+    lines = [ln for ln in open(path) if ln.startswith("{")]
+    return json.loads(lines[-1]) if lines else None
+
+
 def main(out_dir, digest=None):
     os.makedirs(PROFILES, exist_ok=True)
     stats = kernel_stats(out_dir)
+    sys.path.insert(0, ROOT)
+    import bench
     with open(os.path.join(PROFILES, "kernels_headline_step.txt"), "w") as f:
         f.write("# rocprofv3 --kernel-trace --stats of the headline training step\n")
         f.write("# (12000 tokens, 5376 -> 7168, Hadamard block 128).  Command:\n")
         f.write("#   rocprofv3 --kernel-trace --stats -d OUT/kt -o kt --output-format csv -- "
-                "python bench.py --steps 5 --warmup 2 --cpu-tokens 0\n")
+                "python bench.py --cpu-tokens 0\n")
         f.write(f"# {'kernel':<70} {'calls':>5} {'avg_us':>9} {'pct':>6}\n")
         for s in sorted(stats, key=lambda r: -r["total_ns"]):
             f.write(f"  {s['kernel'][:70]:<70} {s['calls']:>5} {s['avg_ns'] / 1e3:>9.2f} "
                     f"{s['pct']:>6.2f}\n")
+        line = bench_line(out_dir)
+        if line:
+            f.write("# The same run's bench line: per-call time from HIP events over the timed\n"
+                    "# steps, against the profiler's average over every call (warmup included).\n")
+            f.write(f"# {'call':<14} {'bench_us':>9} {'rocprof_us':>11}\n")
+            for call, ent in line.get("breakdown", {}).items():
+                keys = bench.KERNEL_OF.get(call, [])
+                prof = sum(st["avg_ns"] for k in keys for st in stats if k in st["kernel"]) / 1e3
+                f.write(f"  {call:<14} {ent['ms'] * 1e3:>9.1f} {prof:>11.1f}\n")
     fetch = dispatches(out_dir, "fetch", "FETCH_SIZE")
     write = dispatches(out_dir, "write", "WRITE_SIZE")
     # The calibration copies are the 'copy' dispatches that wrote COPY_BYTES
@@ -120,8 +140,6 @@ def main(out_dir, digest=None):
         kernels[n] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
                       "bytes_per_launch": round(fb + wb), "launches": len(vals)}
     if digest is None:
-        sys.path.insert(0, ROOT)
-        import bench
         digest = bench.source_digest()
     rec = {"source_digest": digest, "calibration_dispatches": cal, "fetch_scale": f_fac,
            "write_scale": w_fac, "kernels": kernels,
