@@ -415,14 +415,13 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void gemm_kernel(GemmParams p)
 
     // Epilogue.  The MFMA ran with B as its first operand, so each 32x32
     // block holds C transposed: lane l has output row l % 32 and, in register
-    // 4 g + e, output column 8 g + 4 (l / 32) + e.  Every lane therefore
-    // writes 16-byte runs of four columns of its row.
+    // 4 g + e, output column 8 g + 4 (l / 32) + e.
     typedef long long i64x2 __attribute__((ext_vector_type(2)));
     auto ws_at = [&](int i, int j) { return p.ws + (int64_t)i * p.ldc + j; };
     // Four consecutive int64 running sums of row i from column j, or zeros
     // when this is not the last chunk of a split contraction.
-    auto ws4 = [&](int i, int j, int64_t e[4]) {
-        if (MODE == MODE_CHUNK && p.ws_mode == 3 && j < p.S) {
+    auto ws4 = [&](bool ok, int i, int j, int64_t e[4]) {
+        if (MODE == MODE_CHUNK && p.ws_mode == 3 && ok && j < p.S) {
             const i64x2 *w = reinterpret_cast<const i64x2 *>(ws_at(i, j));
             const i64x2 lo = w[0], hi = w[1];
             e[0] = lo[0]; e[1] = lo[1]; e[2] = hi[0]; e[3] = hi[1];
@@ -456,9 +455,9 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void gemm_kernel(GemmParams p)
             // outputs.
             //
             // The arrival flag lives in the stage buffers, free once every
-            // wave has passed the barrier below: a second LDS object would
-            // make the compiler wait for each stage's buffer-to-LDS loads
-            // before any LDS read.
+            // wave has passed the main loop's last barrier: a second LDS
+            // object would make the compiler wait for each stage's
+            // buffer-to-LDS loads before any LDS read.
             int *last_unit = reinterpret_cast<int *>(smem);
             // Unit o's sums: wave w's FM x FN x 4 16-byte slots per lane, the
             // wave's slots contiguous.  Buffer resources start at this wave's
@@ -494,7 +493,11 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void gemm_kernel(GemmParams p)
                     atomicExch(p.count + tail, 0u);
             }
             __syncthreads();
-            if (!*last_unit)
+            const bool is_last = *last_unit;
+            // Every wave has read the flag before any reuses the stage
+            // buffers for the output.
+            __syncthreads();
+            if (!is_last)
                 return;
             // The other units' sums, four units at a time: sixteen 16-byte
             // loads per lane in flight per accumulator block.
@@ -557,29 +560,36 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void gemm_kernel(GemmParams p)
             return;
         }
     }
-    if constexpr (EPI == EPI_ROWSCALE_HAD) {
-        static_assert(FN == 4, "the rotating epilogue needs 128-column wave tiles");
-        // Within the wave's 128 columns, column c = 32 b + 8 g + 4 h + e with
-        // h = lane / 32: butterfly strides 1 and 2 pair registers e, stride 4
-        // pairs lane l with lane l ^ 32, strides 8 and 16 pair registers g and
-        // strides 32 and 64 pair blocks b.  Stages run in ascending stride,
-        // the lower element becoming lo + hi and the upper lo - hi, then every
-        // element is scaled once: the same operations, in the same order, as
-        // the separate rotation of the dequantized row.
-        const bool upper = lane >= 32;
-#pragma unroll
-        for (int a = 0; a < FM; a++) {
-            const int i = i0 + wi * (BM / WM) + a * 32 + lane % 32;
-            if (i >= p.R)
-                continue;   // lanes l and l ^ 32 share the row, so both skip
-            const float rs = p.srow[i];
+    // Output values of row block a of this wave, as 32-bit patterns in the
+    // accumulator layout: v[b][4 g + e] belongs to row i0 + wi RW + 32 a +
+    // lane % 32 and column j0 + wj CW + 32 b + 8 g + 4 (lane / 32) + e.  Rows
+    // and columns past the output give zeros (they are never stored).
+    constexpr int RW = BM / WM, CW = BN / WN;
+    auto row_values = [&](int a, uint32_t (&out)[FN][16]) {
+        const int i = i0 + wi * RW + a * 32 + lane % 32;
+        const bool row_ok = i < p.R;
+        float rs = 0.0f;
+        if constexpr (EPI != EPI_RAW)
+            rs = row_ok ? p.srow[i] : 0.0f;
+        if constexpr (EPI == EPI_ROWSCALE_HAD) {
+            static_assert(FN == 4, "the rotating epilogue needs 128-column wave tiles");
+            // Within the wave's 128 columns, column c = 32 b + 8 g + 4 h + e
+            // with h = lane / 32: butterfly strides 1 and 2 pair registers e,
+            // stride 4 pairs lane l with lane l ^ 32, strides 8 and 16 pair
+            // registers g and strides 32 and 64 pair blocks b.  Stages run in
+            // ascending stride, the lower element becoming lo + hi and the
+            // upper lo - hi, then every element is scaled once: the same
+            // operations, in the same order, as the separate rotation of the
+            // dequantized row.  (Lanes l and l ^ 32 share the row, so a row
+            // past the output is all zeros on both.)
+            const bool upper = lane >= 32;
             float v[FN][16];
 #pragma unroll
             for (int b = 0; b < FN; b++)
 #pragma unroll
                 for (int g = 0; g < 4; g++) {
                     int64_t e[4];
-                    ws4(i, j0 + wj * (BN / WN) + b * 32 + 8 * g + 4 * (lane / 32), e);
+                    ws4(row_ok, i, j0 + wj * CW + b * 32 + 8 * g + 4 * (lane / 32), e);
 #pragma unroll
                     for (int r = 0; r < 4; r++)
                         v[b][4 * g + r] = tofloat(acc[a][b][4 * g + r], e[r]) * rs;
@@ -642,66 +652,98 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void gemm_kernel(GemmParams p)
                     pair(v[1][r], v[3][r]);
                 }
 #pragma unroll
-            for (int b = 0; b < FN; b++) {
+            for (int b = 0; b < FN; b++)
+#pragma unroll
+                for (int r = 0; r < 16; r++)
+                    out[b][r] = __float_as_uint(v[b][r] * p.had_scale);
+        } else {
+#pragma unroll
+            for (int b = 0; b < FN; b++)
 #pragma unroll
                 for (int g = 0; g < 4; g++) {
-                    const int j = j0 + wj * (BN / WN) + b * 32 + 8 * g + 4 * (lane / 32);
-                    if (j >= p.S)
-                        continue;
-                    f32x4 o;
-#pragma unroll
-                    for (int e = 0; e < 4; e++)
-                        o[e] = v[b][4 * g + e] * p.had_scale;
-                    *reinterpret_cast<f32x4 *>(static_cast<float *>(p.out) + (int64_t)i * p.ldc +
-                                               j) = o;
-                }
-            }
-        }
-        return;
-    }
-#pragma unroll
-    for (int a = 0; a < FM; a++) {
-        const int i = i0 + wi * (BM / WM) + a * 32 + lane % 32;
-        if (i >= p.R)
-            continue;
-        float rs = 0.0f;
-        if constexpr (EPI != EPI_RAW)
-            rs = p.srow[i];
-#pragma unroll
-        for (int b = 0; b < FN; b++) {
-#pragma unroll
-            for (int g = 0; g < 4; g++) {
-                const int j = j0 + wj * (BN / WN) + b * 32 + 8 * g + 4 * (lane / 32);
-                if (j >= p.S)
-                    continue;
-                const int64_t off = (int64_t)i * p.ldc + j;
-                const i32x16 &c = acc[a][b];
-                if constexpr (EPI == EPI_RAW) {
-                    *reinterpret_cast<i32x4 *>(static_cast<int32_t *>(p.out) + off) =
-                        i32x4{c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]};
-                } else {
-                    f32x4 v;
-                    int64_t w[4];
-                    ws4(i, j, w);
-#pragma unroll
-                    for (int e = 0; e < 4; e++)
-                        v[e] = tofloat(c[4 * g + e], w[e]) * rs;
-                    if constexpr (EPI == EPI_FWD) {
-                        const f32x4 cs = *reinterpret_cast<const f32x4 *>(p.scol + j);
+                    const int j = j0 + wj * CW + b * 32 + 8 * g + 4 * (lane / 32);
+                    const i32x16 &c = acc[a][b];
+                    if constexpr (EPI == EPI_RAW) {
 #pragma unroll
                         for (int e = 0; e < 4; e++)
-                            v[e] = v[e] * cs[e];
-                        if (p.bias) {
-                            const f32x4 bj = *reinterpret_cast<const f32x4 *>(p.bias + j);
+                            out[b][4 * g + e] = (uint32_t)c[4 * g + e];
+                    } else {
+                        const bool ok = row_ok && j < p.S;
+                        int64_t w[4];
+                        ws4(ok, i, j, w);
+                        f32x4 v;
+#pragma unroll
+                        for (int e = 0; e < 4; e++)
+                            v[e] = tofloat(c[4 * g + e], w[e]) * rs;
+                        if constexpr (EPI == EPI_FWD) {
+                            const f32x4 cs = ok ? *reinterpret_cast<const f32x4 *>(p.scol + j)
+                                                : f32x4{0, 0, 0, 0};
 #pragma unroll
                             for (int e = 0; e < 4; e++)
-                                v[e] = v[e] + bj[e];
+                                v[e] = v[e] * cs[e];
+                            if (p.bias) {
+                                const f32x4 bj = ok ? *reinterpret_cast<const f32x4 *>(p.bias + j)
+                                                    : f32x4{0, 0, 0, 0};
+#pragma unroll
+                                for (int e = 0; e < 4; e++)
+                                    v[e] = v[e] + bj[e];
+                            }
                         }
+#pragma unroll
+                        for (int e = 0; e < 4; e++)
+                            out[b][4 * g + e] = __float_as_uint(v[e]);
                     }
-                    *reinterpret_cast<f32x4 *>(static_cast<float *>(p.out) + off) = v;
                 }
-            }
         }
+    };
+
+    // Stores go through LDS so that each store instruction writes whole row
+    // segments (16 lanes per 256 bytes) instead of 32 bytes of 32 rows: each
+    // wave owns a 16 KiB slice of the (now idle) stage buffers and passes its
+    // RW x CW values through it in passes of 4096 words.  Within a row the
+    // 16-byte chunks are XOR-swizzled by the row, so both the column-wise
+    // writes and the row-wise reads spread over the banks.
+    constexpr int kChunks = CW / 4;                  // 16-byte chunks per row
+    constexpr int kPassRows = 4096 / CW;             // rows per pass
+    constexpr int kPassBlocks = kPassRows / 32;      // 32-row blocks per pass
+    static_assert(kPassBlocks >= 1 && FM % kPassBlocks == 0, "staging pass shape");
+    static_assert(kStages * kStage >= NT / kWave * 4096 * 4, "staging needs 16 KiB per wave");
+    lds_i8 *stage_base = (lds_i8 *)smem + w * 4096 * 4;
+    auto slot = [&](int row, int chunk) { return row * CW + ((chunk ^ (row & (kChunks - 1))) * 4); };
+#pragma unroll
+    for (int pass = 0; pass < FM / kPassBlocks; pass++) {
+#pragma unroll
+        for (int q = 0; q < kPassBlocks; q++) {
+            const int a = pass * kPassBlocks + q;
+            uint32_t v[FN][16];
+            row_values(a, v);
+            const int row = q * 32 + lane % 32;
+#pragma unroll
+            for (int b = 0; b < FN; b++)
+#pragma unroll
+                for (int g = 0; g < 4; g++) {
+                    const int chunk = b * 8 + 2 * g + lane / 32;
+                    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+                    *reinterpret_cast<__attribute__((address_space(3))) u32x4 *>(
+                        stage_base + 4 * slot(row, chunk)) =
+                        u32x4{v[b][4 * g], v[b][4 * g + 1], v[b][4 * g + 2], v[b][4 * g + 3]};
+                }
+        }
+        wait_lgkmcnt0();
+#pragma unroll
+        for (int k = 0; k < 16; k++) {
+            const int s16 = k * kWave + lane;            // 16-byte slot of the pass
+            const int row = s16 / kChunks, chunk = s16 % kChunks;
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 t = *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(
+                stage_base + 4 * slot(row, chunk));
+            const int i = i0 + wi * RW + pass * kPassRows + row;
+            const int j = j0 + wj * CW + chunk * 4;
+            if (i < p.R && j < p.S)
+                *reinterpret_cast<u32x4 *>(static_cast<uint32_t *>(p.out) + (int64_t)i * p.ldc +
+                                           j) = t;
+        }
+        wait_lgkmcnt0();
     }
 }
 
