@@ -620,7 +620,14 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void gemm_kernel(GemmParams p)
                 for (int b = 0; b < FN; b++)
 #pragma unroll
                     for (int r = 0; r < 16; r++) {
-                        const float o = __shfl_xor(v[b][r], 32);
+                        // v_permlane32_swap exchanges the upper half of its
+                        // first operand with the lower half of its second:
+                        // with both the same value, lane l finds lane
+                        // l ^ 32's value in the second result (l < 32) or
+                        // the first (l >= 32).
+                        const uint32_t u = __float_as_uint(v[b][r]);
+                        const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+                        const float o = __uint_as_float(upper ? sw[0] : sw[1]);
                         v[b][r] = upper ? o - v[b][r] : v[b][r] + o;
                     }
             if (p.had > 8)
