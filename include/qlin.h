@@ -17,7 +17,7 @@
  *    contiguous, 16-byte aligned.  A pointer to an array with no element
  *    (for example any [M, *] array when M == 0) may be NULL.  The library
  *    allocates nothing and keeps no mutable global state; calls on different
- *    streams are independent.
+ *    streams are independent unless they share a qlin_product_ws workspace.
  *  - 'stream' is a hipStream_t (NULL means the null stream).  Every call only
  *    enqueues kernels on that stream and returns without synchronizing.
  *  - Arguments are validated before anything is launched: on any error the
