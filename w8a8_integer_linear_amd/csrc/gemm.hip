@@ -25,11 +25,18 @@
 // eight contraction values of column c0 + i: the same lane -> (column, k)
 // map as a row operand's 16-byte read.
 //
+// The epilogue dequantizes (and for dX may rotate) in the accumulator layout,
+// then passes the values through the idle stage buffers so that global
+// stores write whole row segments.
+//
 // Exactness: int32 accumulation of int8 products is exact for contractions up
 // to 131,071 and does not depend on the order of k, so the placement of k
 // inside a fragment only has to agree between A and B, which it does.  Longer
 // contractions run in chunks whose int32 sums are combined in an int64
-// workspace (the MODE_CHUNK kernel variant, launch_product_long).
+// workspace (the MODE_CHUNK kernel variant, launch_product_long).  With a
+// workspace, the tiles of a grid's partial last round are split along the
+// contraction and their int32 partial sums added by the last piece to finish
+// (the MODE_SPLIT variant, split_plan); the sum is the same integer.
 #include "common.hpp"
 #include "launch.hpp"
 
