@@ -282,6 +282,23 @@ def test_products_dequant(T, Q, orc, M, N, K, with_bias):
     assert_bitwise(host(dw), orc.bwd_dw(qg, sg2, qx), "dw")
 
 
+@pytest.mark.parametrize("M,N,K", [(2, 48, 4112), (16, 32, 8192), (1, 16, 12352), (7, 64, 16)])
+def test_skinny_forward_chunks(T, Q, orc, M, N, K):
+    """The weight-streaming kernel walks the contraction in chunks of 4096
+    bytes: several chunks, a ragged last one, a one-step contraction."""
+    rng = np.random.default_rng(M * 7 + K)
+    qx, qw = _codes(rng, (M, K)), _codes(rng, (N, K))
+    sx = rng.uniform(1e-3, 1e-1, M).astype(np.float32)
+    sw = rng.uniform(1e-4, 1e-2, N).astype(np.float32)
+    bias = rng.standard_normal(N).astype(np.float32)
+    announce("skinny chunks", M, N, K)
+    c = Q.qlin_gemm_s32(Q.QLIN_OP_FWD, dev(qx), dev(qw), M, N, K)
+    y = Q.qlin_fwd(dev(qx), dev(sx), dev(qw), dev(sw), dev(bias))
+    T.cuda.synchronize()
+    assert_bitwise(host(c), orc.gemm_s32(0, qx, qw, M, N, K), "acc")
+    assert_bitwise(host(y), orc.fwd(qx, sx, qw, sw, bias), "y")
+
+
 @pytest.mark.parametrize("M", [1, 4, 15, 16])
 def test_skinny_forward(T, Q, orc, M):
     """M <= 16 takes the weight-streaming kernel (skinny workload: 4096 -> 4096)."""

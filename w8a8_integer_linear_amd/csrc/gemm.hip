@@ -784,12 +784,22 @@ void run_gemm(const GemmParams &p0, hipStream_t st)
 }
 
 // Forward product for M <= 16 (decode-like shapes): the weight is streamed
-// once; each workgroup owns 16 output columns and its 4 waves split the
-// contraction in interleaved 64-byte steps, combining their int32 partials
-// through LDS.  One 16x16x64 MFMA per step with A = the (zero-padded) 16
-// rows of qx.  16x16 accumulator layout: lane l, register r holds column
-// l % 16 and row 4 * (l / 16) + r.
-template <bool RAW>
+// once.  Each workgroup owns 16 output columns, i.e. 16 weight rows, whose
+// bytes are copied into LDS in chunks of CHUNK per row by buffer-to-LDS
+// loads: each wave instruction fetches 1 KiB of one row, so every access is
+// a whole contiguous run and a whole chunk (16 rows) is in flight at once,
+// with the next chunk's loads issued before the current one is multiplied.
+// Grids of at most one workgroup per compute unit take 4096-byte chunks (128
+// KiB of buffers); larger grids take 1024-byte chunks, so that four
+// workgroups share a compute unit (measured at 4096 -> 4096 and 4096 ->
+// 14336: 8.0 -> 6.0 us and 17.4 -> 16.0 us for one and four tokens).  Inside a
+// row, 16-byte piece c sits at slot c ^ (row & 15), so the MFMA reads of 16
+// rows at one offset fall on distinct banks.  The 4 waves split a chunk's 64
+// steps of 64 bytes, one v_mfma_i32_16x16x64_i8 per step with A = the
+// (zero-padded) 16 rows of qx, and combine their int32 partials through LDS.
+// 16x16 accumulator layout: lane l, register r holds column l % 16 and row
+// 4 * (l / 16) + r.
+template <bool RAW, int CHUNK>
 __global__ __launch_bounds__(256) void skinny_fwd_kernel(const int8_t *__restrict__ qx,
                                                          const float *__restrict__ sx,
                                                          const int8_t *__restrict__ qw,
@@ -797,35 +807,77 @@ __global__ __launch_bounds__(256) void skinny_fwd_kernel(const int8_t *__restric
                                                          const float *__restrict__ bias, int M,
                                                          int N, int K, void *__restrict__ out)
 {
-    __shared__ i32x4 red[4][kWave];
+    constexpr int kBuf = 16 * CHUNK;            // one chunk of the 16 rows
+    constexpr int kSegs = CHUNK / 1024;         // 1 KiB segments per row
+    constexpr int kPer = CHUNK / 256;           // loads (and MFMA steps) per wave
+    // Two chunk buffers, then the partials of the 4 waves (one LDS object, so
+    // reads of one buffer do not wait for the loads filling the other).
+    __shared__ __attribute__((aligned(1024))) int8_t smem[2 * kBuf + 4 * kWave * 16];
     const int lane = __lane_id();
     const int w = threadIdx.x / kWave;
     const int n0 = blockIdx.x * 16;
     const int col = lane % 16, g = lane / 16;
-    const int8_t *xrow = qx + (int64_t)col * K;
-    const int8_t *wrow = qw + (int64_t)(n0 + col) * K;
     const bool xok = col < M;
-    i32x4 acc = {0, 0, 0, 0};
-    const int steps = (K + 63) / 64;
-    constexpr int U = 4;
-    for (int s0 = w; s0 < steps; s0 += 4 * U) {
-        i32x4 av[U], bv[U];
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(qx);
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(qw + (int64_t)n0 * K);
+    const int chunks = (K + CHUNK - 1) / CHUNK;
+
+    // Chunk kc into buffer b: wave w's instruction p fills 1 KiB of row
+    // (kPer w + p) / kSegs (its segment (kPer w + p) % kSegs); lane l's slot of
+    // that row is 64 segment + l and holds piece slot ^ (row & 15).
+    auto issue = [&](int kc, int b) {
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int k = (s0 + 4 * u) * 64 + g * 16;
-            const bool ok = (s0 + 4 * u) < steps && k < K;
-            bv[u] = ok ? *reinterpret_cast<const i32x4 *>(wrow + k) : i32x4{0, 0, 0, 0};
-            av[u] = (ok && xok) ? *reinterpret_cast<const i32x4 *>(xrow + k) : i32x4{0, 0, 0, 0};
+        for (int p = 0; p < kPer; p++) {
+            const int idx = w * kPer + p;
+            const int row = idx / kSegs, slot = (idx % kSegs) * 64 + lane;
+            const int k = kc * CHUNK + (slot ^ (row & 15)) * 16;
+            const uint32_t off = kc < chunks && k < K ? (uint32_t)(row * K + k) : kOob;
+            lds_i8 *dst = (lds_i8 *)smem + b * kBuf + row * CHUNK + (idx % kSegs) * 1024;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                wr, (__attribute__((address_space(3))) void *)dst, 16, off, 0, 0, 0);
         }
+    };
+
+    i32x4 acc = {0, 0, 0, 0};
+    issue(0, 0);
+    for (int kc = 0; kc < chunks; kc++) {
+        // This wave's steps of the chunk: x fragments from global memory
+        // (the same few rows for every workgroup, so L2-resident); rows past
+        // M and bytes past K read as zeros through the buffer range check.
+        i32x4 av[kPer];
 #pragma unroll
-        for (int u = 0; u < U; u++)
-            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[u], bv[u], acc, 0, 0, 0);
+        for (int t = 0; t < kPer; t++) {
+            const int k = kc * CHUNK + (w + 4 * t) * 64 + g * 16;
+            const uint32_t off = xok && k < K ? (uint32_t)(col * K + k) : kOob;
+            av[t] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+        }
+        // The next chunk's loads (past the last chunk they are all out of
+        // range: zero fills of the idle buffer), then wait until only they
+        // are outstanding.  The same instruction sequence every iteration
+        // keeps the compiler from adding waits of its own.
+        issue(kc + 1, (kc + 1) & 1);
+        wait_vmcnt<kPer>();
+        barrier_no_fence();
+        const int8_t *buf = smem + (kc & 1) * kBuf;
+#pragma unroll
+        for (int t = 0; t < kPer; t++) {
+            const int piece = (w + 4 * t) * 4 + g;
+            const i32x4 bv = *reinterpret_cast<const i32x4 *>(
+                buf + col * CHUNK + (piece ^ col) * 16);
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[t], bv, acc, 0, 0, 0);
+        }
+        // Every wave has read this buffer (its MFMAs consumed the reads)
+        // before the loads of chunk kc + 2 refill it; no fence, so the loads
+        // of chunk kc + 1 stay in flight.
+        barrier_no_fence();
     }
-    red[w][lane] = acc;
+    wait_vmcnt<0>();    // the zero fills issued by the last iteration
+    i32x4 *red = reinterpret_cast<i32x4 *>(smem + 2 * kBuf);
+    red[w * kWave + lane] = acc;
     __syncthreads();
     if (w != 0)
         return;
-    const i32x4 t = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+    const i32x4 t = (red[lane] + red[kWave + lane]) + (red[2 * kWave + lane] + red[3 * kWave + lane]);
     const int n = n0 + col;
     float cs = 0.0f, bn = 0.0f;
     if (!RAW) {
@@ -928,14 +980,15 @@ void launch_product(const ProductArgs &a, hipStream_t st)
     if (a.op == 0) {
         if (a.M <= 16 && a.ws_mode == 0) {
             const unsigned grid = (unsigned)(a.N / 16);
+            auto go = [&](auto kernel) {
+                hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, st, a.a, a.srow, a.b,
+                                   a.scol, a.bias, (int)a.M, (int)a.N, (int)a.K, a.out);
+            };
+            const bool wide = grid > (unsigned)kRound;
             if (a.raw)
-                hipLaunchKernelGGL(skinny_fwd_kernel<true>, dim3(grid), dim3(256), 0, st, a.a,
-                                   a.srow, a.b, a.scol, a.bias, (int)a.M, (int)a.N, (int)a.K,
-                                   a.out);
+                wide ? go(skinny_fwd_kernel<true, 1024>) : go(skinny_fwd_kernel<true, 4096>);
             else
-                hipLaunchKernelGGL(skinny_fwd_kernel<false>, dim3(grid), dim3(256), 0, st, a.a,
-                                   a.srow, a.b, a.scol, a.bias, (int)a.M, (int)a.N, (int)a.K,
-                                   a.out);
+                wide ? go(skinny_fwd_kernel<false, 1024>) : go(skinny_fwd_kernel<false, 4096>);
             return;
         }
         p.a = a.a; p.lda = a.K;
