@@ -108,12 +108,46 @@ def cpu_baseline(d, tokens):
                       f"(SGD requant over the whole weight), {t:.2f} s"}
 
 
+def replay_skinny(torch, nat, qx, sx, qws, sw, y, eager, reps, nbytes):
+    """The skinny calls replayed from a HIP graph, without the host's per-call
+    launch cost: one call per weight copy, in the order that ends on the copy
+    the eager loop ended on, so each replay must reproduce `eager` exactly
+    (checked after the first replay and after the timed ones)."""
+    copies = len(qws)
+    try:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(copies):
+                nat.qlin_fwd(qx, sx, qws[(reps + i) % copies], sw, y=y)
+        graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(y, eager):
+            return {"ms_graph": None, "graph_error": "replay differs from the eager output"}
+        n_rep = max(1, reps // copies)
+        b = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        b.record()
+        for _ in range(n_rep):
+            graph.replay()
+        e.record()
+        torch.cuda.synchronize()
+        if not torch.equal(y, eager):
+            return {"ms_graph": None, "graph_error": "replay differs from the eager output"}
+    except RuntimeError as err:      # capture not available: report, do not fail the bench
+        return {"ms_graph": None, "graph_error": str(err)[:200]}
+    ms_graph = b.elapsed_time(e) / (n_rep * copies)
+    return {"ms_graph": round(ms_graph, 5),
+            "gbs_graph": round(nbytes / (ms_graph * 1e-3) / 1e9, 1)}
+
+
 def skinny_forward(torch, reps=240, copies=24):
     """The weight-streaming forward for M <= 16 rows (4096 -> 4096, no rotation,
     seeded inputs of the skinny workload): HBM GB/s per call, where a call moves
     the weight once plus the small activation and output arrays.  Calls cycle
     through `copies` copies of the weight (403 MB, more than the 256 MB
-    infinity cache), so each call streams its weight from HBM."""
+    infinity cache), so each call streams its weight from HBM.  `ms` times the
+    calls as launched from Python; `ms_graph` times them replayed from a HIP
+    graph."""
     import numpy as np
 
     import workloads
@@ -140,10 +174,12 @@ def skinny_forward(torch, reps=240, copies=24):
         e.record()
         torch.cuda.synchronize()
         ms = b.elapsed_time(e) / reps
+        eager = y.clone()          # the last call used copy (reps - 1) % copies
         nbytes = nn * kk + m * kk + 4 * (m + nn) + 4 * m * nn
         gbs = nbytes / (ms * 1e-3) / 1e9
+        graph_res = replay_skinny(torch, nat, qx, sx, qws, sw, y, eager, reps, nbytes)
         res[f"skinny_fwd_m{m}"] = {"ms": round(ms, 5), "gbs": round(gbs, 1),
-                                   "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                                   "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), **graph_res,
                                    "shape": [m, kk, nn]}
     return res
 

@@ -179,3 +179,44 @@ def test_deterministic(orc):
     b = _step(T, d, 2048, 5376, 7168, 128, 1e-3, 9, 1)
     for k in a:
         assert_bitwise(a[k], b[k], k)
+
+
+def test_graph_replay_of_step(orc):
+    """One training step (2048 tokens, 5376 -> 7168, rotation 128: the dW
+    product splits its last round) captured in a HIP graph and replayed three
+    times from the same starting weight, with eager work between replays: each
+    replay reproduces the eager step bit for bit (the calls allocate nothing,
+    never synchronize, and the split counters return to zero)."""
+    import torch
+    from w8a8_integer_linear_amd import LinearW8A8Training
+    T = torch_cuda()
+    d = workloads.linear(2048, 5376, 7168, seed=4)
+    announce("graph replay", 2048)
+    layer = LinearW8A8Training(dev(d["w"]), had_block=128, max_tokens=2048)
+    x, dy = dev(d["x"]), dev(d["dy"])
+
+    def step():
+        y = layer.forward(x)
+        dx = layer.backward(dy)
+        layer.sgd_step(1e-3, 7, 3)
+        return y, dx
+
+    step()                                   # first call: buffers and workspace
+    q0, s0 = layer.qw.clone(), layer.sw.clone()
+    y, dx = step()
+    ref = [t.clone() for t in (y, dx, layer.qw, layer.sw)]
+    layer.qw.copy_(q0)
+    layer.sw.copy_(s0)
+    T.cuda.synchronize()
+    graph = T.cuda.CUDAGraph()
+    with T.cuda.graph(graph):
+        gy, gdx = step()
+    for rep in range(3):
+        layer.qw.copy_(q0)
+        layer.sw.copy_(s0)
+        junk = T.randn(1 << 20, device="cuda").sum()     # eager work between replays
+        graph.replay()
+        T.cuda.synchronize()
+        for name, got, want in zip(("y", "dx", "qw", "sw"), (gy, gdx, layer.qw, layer.sw), ref):
+            assert_bitwise(host(got), host(want), f"replay {rep}: {name}")
+        del junk
