@@ -243,7 +243,7 @@ int qlin_product_ws(int op, const int8_t *a, const float *srow, const int8_t *b,
 
 /* Workspace bytes qlin_product_ws needs for this shape: beyond the int32
  * bound 4096 + 8 per output element; within it 4096 + 256 KiB per balancing
- * piece (at most 160 pieces), or 0 when nothing is balanced.  Returns 0 for
+ * piece (at most 256 pieces), or 0 when nothing is balanced.  Returns 0 for
  * invalid arguments. */
 size_t qlin_product_ws_bytes(int op, int64_t M, int64_t N, int64_t K);
 

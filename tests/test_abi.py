@@ -187,7 +187,8 @@ def test_product_ws_validation(L):
     assert L.qlin_product_ws_bytes(0, 12000, 7168, 5376) == C + 36 * 3 * BLK  # 1316 tiles
     assert L.qlin_product_ws_bytes(1, 12000, 7168, 5376) == 0     # 987 tiles: 219 left, no split
     assert L.qlin_product_ws_bytes(2, 12000, 7168, 5376) == C + 76 * 2 * BLK  # 588 tiles
-    assert L.qlin_product_ws_bytes(2, 8192, 14336, 4096) == 0     # 896 tiles: 128 left, 2 x 128 > 160
+    assert L.qlin_product_ws_bytes(2, 8192, 14336, 4096) == C + 128 * 2 * BLK  # 896 tiles
+    assert L.qlin_product_ws_bytes(1, 8192, 14336, 4096) == 0     # 512 tiles: whole rounds
     assert L.qlin_product_ws_bytes(2, 1000, 16, 32) == C + 2 * BLK   # 8 stages in 2 pieces
     assert L.qlin_product_ws_bytes(2, 100, 16, 32) == 0           # one stage: nothing to split
     assert L.qlin_product_ws_bytes(0, 16, 7168, 5376) == 0        # weight-streaming kernel

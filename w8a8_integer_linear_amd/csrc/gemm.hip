@@ -917,15 +917,15 @@ void run_cfg(const GemmParams &p, hipStream_t st)
 // configuration at a time, so a grid runs in rounds of this many tiles.
 constexpr int kRound = 256;
 // Fewest contraction stages a piece of a split tile gets, most pieces per
-// tile, and most pieces in the balanced round.  The last round's pieces
-// share no operand data with one another, so a nearly full round of them runs
-// slower than a partly full one, and every piece past the first adds a 256 KiB
-// partial that the last one must read: on the 12000 x 5376 x 7168 products
-// three pieces (forward, 36 tiles left) and two (dW, 76 tiles left) measured
-// best.
+// tile, and most pieces in a round of three-way splits.  Every piece past the
+// first adds a 256 KiB partial that the last one must read, and a nearly full
+// round of three-way pieces ran slower than two-way ones: measured best were
+// three pieces for 36 tiles left (12000 x 5376 -> 7168 forward), two for 76
+// (its dW) and two for 128 (dW of 8192 tokens, 4096 <-> 14336: -3% and -8%
+// against no split).
 constexpr int kMinPieceStages = 4;
 constexpr int kMaxPieces = 3;
-constexpr int kMaxPieceUnits = 160;
+constexpr int kMaxThreeWayUnits = 128;
 
 SplitPlan split_plan(int op, int64_t M, int64_t N, int64_t K)
 {
@@ -941,10 +941,8 @@ SplitPlan split_plan(int op, int64_t M, int64_t N, int64_t K)
     const int64_t by_len = ((T + 127) / 128) / kMinPieceStages;
     split = split < by_len ? split : by_len;
     split = split < kMaxPieces ? split : kMaxPieces;
-    if (split > 2 && tail * split > kMaxPieceUnits)
-        split--;
-    if (split == 2 && tail * split > kMaxPieceUnits)
-        split = 1;
+    if (split == 3 && tail * split > kMaxThreeWayUnits)
+        split = 2;
     if (split < 2)
         return none;
     return SplitPlan{(int)full, (int)tail, (int)split};
