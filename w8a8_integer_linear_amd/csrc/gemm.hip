@@ -264,6 +264,20 @@ __device__ __forceinline__ void tile_at(int lin, int tiles_i, int tiles_j, int &
     tj = in / gsize;
 }
 
+// Compute units of the chip: each runs one workgroup of the 256 x 256 tile
+// configuration at a time, so a grid runs in rounds of this many tiles.
+constexpr int kRound = 256;
+// Fewest contraction stages a piece of a split tile gets, most pieces per
+// tile, and most pieces in a round of three-way splits.  Every piece past the
+// first adds a 256 KiB partial that the last one must read, and a nearly full
+// round of three-way pieces ran slower than two-way ones: measured best were
+// three pieces for 36 tiles left (12000 x 5376 -> 7168 forward), two for 76
+// (its dW) and two for 128 (dW of 8192 tokens, 4096 <-> 14336: -3% and -8%
+// against no split).
+constexpr int kMinPieceStages = 4;
+constexpr int kMaxPieces = 3;
+constexpr int kMaxThreeWayUnits = 128;
+
 // ------------------------------------------------------------------- kernel
 
 // Launch modes.  MODE_CHUNK: the launch is one chunk of a contraction longer
@@ -506,35 +520,37 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void gemm_kernel(GemmParams p)
             __syncthreads();
             if (!is_last)
                 return;
-            // The other units' sums, four units at a time: sixteen 16-byte
-            // loads per lane in flight per accumulator block.
+            // The other pieces' sums (at most two: kMaxPieces is 3), read for
+            // two accumulator blocks at a time: sixteen 16-byte loads per
+            // lane in flight, so the whole combine takes FM * FN / 2 round
+            // trips.  A missing second piece reads zeros through an empty
+            // buffer resource.
+            static_assert(kMaxPieces <= 3 && (FM * FN) % 2 == 0, "combine batch shape");
             const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<int32_t *>(p.part), (short)0, 0, kRsrcWord3);
-            for (int o0 = 0; o0 < p.split; o0 += 4) {
-                __amdgpu_buffer_rsrc_t rs[4];
+            const __amdgpu_buffer_rsrc_t rs[2] = {
+                part_rsrc((piece + 1) % p.split),
+                p.split > 2 ? part_rsrc((piece + 2) % p.split) : none};
 #pragma unroll
-                for (int u = 0; u < 4; u++)
-                    rs[u] = o0 + u < p.split && o0 + u != piece ? part_rsrc(o0 + u) : none;
+            for (int q = 0; q < FM * FN; q += 2) {
+                i32x4 t[2][2][4];
 #pragma unroll
-                for (int a = 0; a < FM; a++)
+                for (int h = 0; h < 2; h++)
 #pragma unroll
-                    for (int b = 0; b < FN; b++) {
-                        i32x4 t[4][4];
+                    for (int u = 0; u < 2; u++)
 #pragma unroll
-                        for (int u = 0; u < 4; u++)
+                        for (int g = 0; g < 4; g++)
+                            t[h][u][g] = __builtin_amdgcn_raw_buffer_load_b128(
+                                rs[u], lane_off, ((q + h) * 4 + g) * kWave * 16, kCoherent);
 #pragma unroll
-                            for (int g = 0; g < 4; g++)
-                                t[u][g] = __builtin_amdgcn_raw_buffer_load_b128(
-                                    rs[u], lane_off, ((a * FN + b) * 4 + g) * kWave * 16,
-                                    kCoherent);
+                for (int h = 0; h < 2; h++)
 #pragma unroll
-                        for (int u = 0; u < 4; u++)
+                    for (int u = 0; u < 2; u++)
 #pragma unroll
-                            for (int g = 0; g < 4; g++)
+                        for (int g = 0; g < 4; g++)
 #pragma unroll
-                                for (int e = 0; e < 4; e++)
-                                    acc[a][b][4 * g + e] += t[u][g][e];
-                    }
+                            for (int e = 0; e < 4; e++)
+                                acc[(q + h) / FN][(q + h) % FN][4 * g + e] += t[h][u][g][e];
             }
         }
     }
@@ -912,20 +928,6 @@ void run_cfg(const GemmParams &p, hipStream_t st)
 }
 
 } // namespace
-
-// Compute units of the chip: each runs one workgroup of the 256 x 256 tile
-// configuration at a time, so a grid runs in rounds of this many tiles.
-constexpr int kRound = 256;
-// Fewest contraction stages a piece of a split tile gets, most pieces per
-// tile, and most pieces in a round of three-way splits.  Every piece past the
-// first adds a 256 KiB partial that the last one must read, and a nearly full
-// round of three-way pieces ran slower than two-way ones: measured best were
-// three pieces for 36 tiles left (12000 x 5376 -> 7168 forward), two for 76
-// (its dW) and two for 128 (dW of 8192 tokens, 4096 <-> 14336: -3% and -8%
-// against no split).
-constexpr int kMinPieceStages = 4;
-constexpr int kMaxPieces = 3;
-constexpr int kMaxThreeWayUnits = 128;
 
 SplitPlan split_plan(int op, int64_t M, int64_t N, int64_t K)
 {
