@@ -220,3 +220,36 @@ def test_graph_replay_of_step(orc):
         for name, got, want in zip(("y", "dx", "qw", "sw"), (gy, gdx, layer.qw, layer.sw), ref):
             assert_bitwise(host(got), host(want), f"replay {rep}: {name}")
         del junk
+
+
+def test_split_products_equal_plain_at_full_size(orc):
+    """At 12000 x 5376 -> 7168 the forward (36 tiles in 3 pieces) and dW (76
+    tiles in 2 pieces) products split their last round; over the whole output
+    they equal the plain calls bit for bit, which the sampled oracle checks of
+    the step pin.  dX (no split at this shape) goes through the same call."""
+    import torch
+    T = torch_cuda()
+    from w8a8_integer_linear_amd import _native as Q
+    M, K, N = 12000, 5376, 7168
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    codes = lambda shape: torch.randint(-127, 128, shape, generator=g, device="cuda",
+                                        dtype=torch.int8)
+    qx, qw, qg = codes((M, K)), codes((N, K)), codes((M, N))
+    sx = torch.rand(M, generator=g, device="cuda") + 0.5
+    sw = torch.rand(N, generator=g, device="cuda") * 1e-2
+    s1 = torch.rand(M, generator=g, device="cuda") * 1e-3
+    s2 = torch.rand(N, generator=g, device="cuda") * 1e-3
+    bias = torch.randn(N, generator=g, device="cuda")
+    assert Q.qlin_product_ws_bytes(0, M, N, K) > 0 and Q.qlin_product_ws_bytes(2, M, N, K) > 0
+    announce("split vs plain at full size")
+    pairs = [
+        (Q.qlin_product_ws(0, qx, sx, qw, M, N, K, scol=sw, bias=bias),
+         Q.qlin_fwd(qx, sx, qw, sw, bias)),
+        (Q.qlin_product_ws(1, qg, s1, qw, M, N, K, had_block=128),
+         Q.qlin_bwd_dx(qg, s1, qw, had_block=128)),
+        (Q.qlin_product_ws(2, qg, s2, qx, M, N, K), Q.qlin_bwd_dw(qg, s2, qx)),
+    ]
+    T.cuda.synchronize()
+    for name, (a, b) in zip(("y", "dx", "dw"), pairs):
+        assert torch.equal(a, b), name
