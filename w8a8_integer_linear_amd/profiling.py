@@ -1,7 +1,7 @@
 """Turn rocprofv3 CSV output of bench.py runs into short text summaries.
 
-Usage (from the repository root, after the three profiler runs listed in
-the design doc have written their CSVs under OUT_DIR):
+Usage (from the repository root, after the profiler runs below have written
+their CSVs under OUT_DIR):
 
     python -m w8a8_integer_linear_amd.profiling OUT_DIR
 
