@@ -12,18 +12,17 @@
 //   dX       A = qg1 [M,N] row, B = qw [N,K] km (t = n)   C = dx [M,K]
 //   dW       A = qg2 [M,N] km,  B = qx [M,K] km (t = m)   C = dw [N,K]
 //
-// Tiles of BM x BN outputs (256 x 256) and kBK (128) contraction bytes per
-// stage are copied straight from global memory into LDS by 16-byte buffer
-// loads, in the layout they have in memory (XOR-swizzled at 16-byte
-// granularity), through a ring of stages (two at 128 bytes, as many as fit in
-// 160 KiB of LDS, at most four) so the next stage's loads are in flight while
-// one is multiplied.  Fragments for v_mfma_i32_32x32x32_i8 are read with
-// ds_read_b128 from a row operand and with two ds_read_b64_tr_b8 from a km
-// operand: in each 16-lane group the transpose read hands lane i byte i & 7
-// of the row addressed by lane 2e + (i >> 3) as its byte e, so pointing lane
-// s at contraction row k0 + (s >> 1), column c0 + 8 (s & 1) gives lane i the
-// eight contraction values of column c0 + i: the same lane -> (column, k)
-// map as a row operand's 16-byte read.
+// Tiles of 256 x 256 outputs and 128 contraction bytes per stage are copied
+// straight from global memory into LDS by 16-byte buffer loads, in the layout
+// they have in memory (XOR-swizzled at 16-byte granularity), through two LDS
+// stages so the next stage's loads are in flight while one is multiplied.
+// Fragments for v_mfma_i32_16x16x64_i8 are read with ds_read_b128 from a row
+// operand and with two ds_read_b64_tr_b8 from a km operand: in each 16-lane
+// group the transpose read hands lane i byte i & 7 of the row addressed by
+// lane 2e + (i >> 3) as its byte e, so pointing lane s at contraction row
+// k0 + (s >> 1), column c0 + 8 (s & 1) gives lane i the eight contraction
+// values of column c0 + i: the same lane -> (column, k) map as a row
+// operand's 16-byte read.
 //
 // The epilogue dequantizes (and for dX may rotate) in the accumulator layout,
 // then passes the values through the idle stage buffers so that global
@@ -37,6 +36,8 @@
 // workspace, the tiles of a grid's partial last round are split along the
 // contraction and their int32 partial sums added by the last piece to finish
 // (the MODE_SPLIT variant, split_plan); the sum is the same integer.
+#include <utility>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -92,44 +93,44 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const int8_t *base)
 
 typedef __attribute__((address_space(3))) int8_t lds_i8;
 
-// One operand tile of ROWS output rows (or columns) by kBK (64 or 128)
-// contraction bytes,
-// copied straight from global memory into LDS by buffer loads (each wave
-// instruction fills 1 KiB: lane l writes bytes 16 l .. 16 l + 15).
+// One operand tile of ROWS output rows (or columns) by kBK = 128 contraction
+// bytes, copied straight from global memory into LDS by buffer loads (each
+// wave instruction fills 1 KiB: lane l writes bytes 16 l .. 16 l + 15).
 //
-// Row operand: LDS [ROWS][kBK]; the 16-byte chunk holding contraction bytes
-// 16 c .. of row r sits at position c ^ ((r >> 2) & 3) for kBK = 64 and
-// c ^ ((r >> 1) & 7) for kBK = 128, so the 16 rows read together by a
-// fragment load fall on 16 distinct bank groups.
-// Km operand: LDS [kBK][ROWS]; chunk c (columns 16 c ..) of contraction row k
-// sits at position c ^ (2 (k & 7)) (for ROWS >= 256), so the 8 rows read
-// together by a transpose load (and the neighbouring chunk read by the next
-// 16 lanes) fall on distinct bank groups.
+// Row operand: LDS [ROWS][128]; the 16-byte chunk holding contraction bytes
+// 16 c .. of row r sits at position c ^ ((r >> 1) & 7), so the 16 rows read
+// together by a fragment load fall on 16 distinct bank groups.
+// Km operand: LDS [128][ROWS = 256]; chunk c (columns 16 c ..) of contraction
+// row k sits at position c ^ (2 (k & 7) | ((k >> 4) & 1)): the 8 rows read
+// together by one 16-lane group of a transpose load fall on distinct bank
+// groups, and so do those of the next group, which reads the same chunk 16
+// contraction rows further on.
 template <int ROWS, bool KM, int NT, int kBK>
 struct Operand {
     static constexpr int kBytes = ROWS * kBK;
     static constexpr int kLoads = kBytes / 16 / NT;      // 16-byte loads per lane per stage
     static_assert(kBytes % (16 * NT) == 0, "tile does not split evenly over the threads");
     static constexpr int kRowChunks = KM ? ROWS / 16 : kBK / 16;
+    static_assert(kBK == 128 && (!KM || ROWS == 256), "operand layout shape");
 
     __device__ static __forceinline__ int swz(int row)
     {
-        if constexpr (!KM)
-            return kBK == 64 ? (row >> 2) & 3 : (row >> 1) & 7;
-        else if constexpr (ROWS >= 256)
-            return 2 * (row & 7);
+        if constexpr (KM)
+            return 2 * (row & 7) | ((row >> 4) & 1);
         else
-            return row & (ROWS / 16 - 1) & 7;
+            return (row >> 1) & 7;
     }
 
-    // Enqueue the loads of stage k0 into 'dst' (this thread's share).
+    // Enqueue loads P0 .. P1 - 1 of this thread's share of the stage whose
+    // contraction starts at k0, into 'dst'.
+    template <int P0 = 0, int P1 = kLoads>
     __device__ static __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, int64_t ld, int i0,
                                                  int lim, int k0, int T, bool live, int8_t *dst)
     {
         const int lane = __lane_id();
         const int w = threadIdx.x / kWave;
 #pragma unroll
-        for (int p = 0; p < kLoads; p++) {
+        for (int p = P0; p < P1; p++) {
             const int slot = (p * (NT / kWave) + w) * kWave + lane;   // 16-byte LDS slot
             const int row = slot / kRowChunks;
             const int c = (slot % kRowChunks) ^ swz(row);
@@ -151,45 +152,62 @@ struct Operand {
         }
     }
 
-    // Raw registers of one MFMA fragment while its LDS reads are in flight.
+    // An MFMA fragment's registers while its LDS reads are in flight.
     struct Raw {
         i32x4 v;            // row operand: one 16-byte read
         i32x2v lo, hi;      // km operand: two transpose reads
     };
 
-    // Start loading the MFMA fragment of the 32 rows (columns) starting at
-    // 'r0' for contraction step kk (32 bytes): lane l gets row r0 + l % 32 and
-    // contraction bytes 16 (l / 32) .. +15 of the step.  Km fragments are read
-    // by inline asm so that the compiler does not order them behind the buffer
-    // loads still filling other stages; their registers are valid only after
-    // settle().
-    __device__ static __forceinline__ void frag(const int8_t *lds, int r0, int kk, Raw &f)
+    // Fragment of rows (columns) r0 .. r0 + 15 for one 64-byte contraction
+    // step of v_mfma_i32_16x16x64_i8: lane l holds row r0 + l % 16 and
+    // contraction bytes 16 (l / 16) .. +15 of the step.  off() gives the
+    // lane's LDS byte offset in a stage for step 0 (row operand: for step
+    // kk); the fragment of step kk of a km operand is at + kStep and, for a
+    // row operand, that of the 16-row block f rows further on at + f kBlock
+    // (neither moves the swizzle).  A km fragment's second transpose read is
+    // 8 contraction rows on.
+    __device__ static __forceinline__ uint32_t off(int r0, int kk)
     {
         const int lane = __lane_id();
         if constexpr (KM) {
             const int s = lane % 16;
-            const int krow = kk * 32 + (lane / 32) * 16 + (s >> 1);
-            const int chunk = (r0 + ((lane % 32) / 16) * 16) / 16;
-            const uint32_t base = (uint32_t)(uintptr_t)(const lds_i8 *)lds;
-            const uint32_t a0 = base + krow * ROWS + 16 * (chunk ^ swz(krow)) + 8 * (s & 1);
-            const uint32_t a1 =
-                base + (krow + 8) * ROWS + 16 * (chunk ^ swz(krow + 8)) + 8 * (s & 1);
-            asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(f.lo) : "v"(a0));
-            asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(f.hi) : "v"(a1));
+            const int krow = (lane / 16) * 16 + (s >> 1);
+            return krow * ROWS + 16 * ((r0 / 16) ^ swz(krow)) + 8 * (s & 1);
         } else {
-            const int row = r0 + lane % 32;
-            const int c = kk * 2 + lane / 32;
-            f.v = *reinterpret_cast<const i32x4 *>(lds + row * kBK + 16 * (c ^ swz(row)));
+            const int row = r0 + lane % 16, c = kk * 4 + lane / 16;
+            return row * kBK + 16 * (c ^ swz(row));
+        }
+    }
+    static constexpr int kStep = KM ? 64 * ROWS : 0;
+    static constexpr int kBlock = KM ? 0 : 16 * kBK;
+    static constexpr int kReads = KM ? 2 : 1;            // LDS instructions per fragment
+
+    // Issue the reads of one fragment at LDS address 'addr' plus the constant
+    // OFF.  Inline asm keeps the compiler from ordering them behind the buffer
+    // loads still filling the other stage; the registers are valid only after
+    // an lgkmcnt wait and settle().
+    template <int OFF>
+    __device__ static __forceinline__ void frag(uint32_t addr, Raw &f)
+    {
+        if constexpr (KM) {
+            asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(f.lo) : "v"(addr), "n"(OFF));
+            asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2"
+                         : "=v"(f.hi)
+                         : "v"(addr), "n"(OFF + 8 * ROWS));
+        } else {
+            asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(f.v) : "v"(addr), "n"(OFF));
         }
     }
 
-    // After an lgkmcnt(0) wait: ties the asm-loaded registers to the wait so no
+    // After the fragment's lgkmcnt wait: ties its registers to the wait so no
     // use (or copy) of them is scheduled before it.
     __device__ static __forceinline__ void settle(Raw &f)
     {
         if constexpr (KM) {
             asm volatile("" : "+v"(f.lo));
             asm volatile("" : "+v"(f.hi));
+        } else {
+            asm volatile("" : "+v"(f.v));
         }
     }
 
@@ -201,14 +219,6 @@ struct Operand {
             return f.v;
     }
 };
-
-// Pipeline depth: as many stages as fit in this workgroup's share of the
-// 160 KiB of LDS (OCC workgroups per CU), at most 4.
-template <int kStageBytes, int OCC>
-constexpr int kStagesFor()
-{
-    return (160 * 1024 / OCC / kStageBytes) < 4 ? (160 * 1024 / OCC / kStageBytes) : 4;
-}
 
 __device__ __forceinline__ void wait_lgkmcnt0()
 {
@@ -235,8 +245,7 @@ __device__ __forceinline__ void barrier_no_fence()
 
 // Epilogues: raw int32; dequant by the output row's scale; forward dequant by
 // row and column scales plus bias; row-scale dequant followed by the block
-// Hadamard rotation of each output row (blocks of up to 128 columns, which
-// needs a wave tile 128 columns wide).
+// Hadamard rotation of each output row (blocks of up to 128 columns).
 enum { EPI_RAW = 0, EPI_ROWSCALE = 1, EPI_FWD = 2, EPI_ROWSCALE_HAD = 3 };
 
 // Tile order: workgroups are dispatched round-robin over the 8 XCDs, so
@@ -286,337 +295,553 @@ constexpr int kMaxThreeWayUnits = 128;
 // split, part, count).  Ordinary launches carry neither's code.
 enum { MODE_PLAIN = 0, MODE_CHUNK = 1, MODE_SPLIT = 2 };
 
-template <int BM, int BN, int WM, int WN, int kBK, int OCC, bool AKM, bool BKM, int EPI,
-          int MODE>
-__global__ __launch_bounds__(WM *WN * 64, OCC) void gemm_kernel(GemmParams p)
-{
-    constexpr int NT = WM * WN * 64;
-    constexpr int FM = BM / WM / 32;   // 32x32 blocks per wave along rows
-    constexpr int FN = BN / WN / 32;
-    constexpr int NK = kBK / 32;       // MFMA contraction steps per stage
-    using OpA = Operand<BM, AKM, NT, kBK>;
-    using OpB = Operand<BN, BKM, NT, kBK>;
-    constexpr int kStage = OpA::kBytes + OpB::kBytes;
-    constexpr int kStages = kStagesFor<kStage, OCC>();
-    static_assert(kStages >= 2, "tile too large for the LDS share");
-    constexpr int kLoads = OpA::kLoads + OpB::kLoads;     // per lane per stage
-    __shared__ __attribute__((aligned(1024))) int8_t smem[kStages * kStage];
+// What this workgroup computes: output tile (ti, tj) over the contraction
+// stages [kb, kb + KT) of kBK bytes; tail >= 0 marks piece 'piece' of split
+// tail tile 'tail'.
+struct WorkUnit {
+    int ti, tj, kb, KT, tail, piece;
+};
 
-    // Work unit -> tile and range of contraction stages [kb, kb + KT).
+template <int MODE>
+__device__ __forceinline__ WorkUnit work_unit(const GemmParams &p, int kBK)
+{
     const int KT_all = (p.T + kBK - 1) / kBK;
-    int lin, kb = 0, KT = KT_all, tail = -1, piece = 0;
+    WorkUnit u{0, 0, 0, KT_all, -1, 0};
+    int lin;
     if (MODE == MODE_SPLIT && (int)blockIdx.x >= p.full) {
         const int q = (int)blockIdx.x - p.full;
-        tail = q / p.split;
-        piece = q % p.split;
-        lin = p.full + tail;
-        kb = piece * KT_all / p.split;
-        KT = (piece + 1) * KT_all / p.split - kb;
+        u.tail = q / p.split;
+        u.piece = q % p.split;
+        lin = p.full + u.tail;
+        u.kb = u.piece * KT_all / p.split;
+        u.KT = (u.piece + 1) * KT_all / p.split - u.kb;
     } else {
         lin = xcd_order(blockIdx.x, MODE == MODE_SPLIT ? p.full : p.tiles_i * p.tiles_j);
     }
-    int ti, tj;
-    tile_at(lin, p.tiles_i, p.tiles_j, ti, tj);
-    const int i0 = ti * BM, j0 = tj * BN;
+    tile_at(lin, p.tiles_i, p.tiles_j, u.ti, u.tj);
+    return u;
+}
+
+// Balanced last round: store this unit's int32 sums and count its arrival;
+// the last of the tile's units to arrive adds the others' sums (exact: int32
+// addition of bounded partials) and returns true, every other unit false.
+// Each lane holds kSlots 16-byte slots of sums: get(s) reads slot s,
+// add(s, v) adds v into it.
+//
+// The partial sums cross XCDs, whose L2s are not coherent with one another.
+// They are written and read with the device-scope coherence bit (sc1: the bit
+// a device-scope relaxed atomic access carries), so they never sit in an L2
+// as stale or dirty lines; each wave waits for its stores to complete before
+// the barrier that precedes the arrival count, and the reader's loads are
+// issued after it observes the count.  A device-scope fence would do the
+// same by writing back and invalidating whole L2s, which stalls the chip
+// while the rest of the grid is still storing outputs.
+//
+// The arrival flag lives in the stage buffers ('flag_lds'), free once every
+// wave has passed the main loop's last barrier: a second LDS object would make
+// the compiler wait for each stage's buffer-to-LDS loads before any LDS read.
+template <int kSlots, int kTile, int kBatch, typename Get, typename Add>
+__device__ __forceinline__ bool split_combine(const GemmParams &p, int tail, int piece,
+                                              int *flag_lds, Get get, Add add)
+{
+    // Unit o's sums: wave w's kSlots 16-byte slots per lane, the wave's slots
+    // contiguous.  Buffer resources start at this wave's run (so slot offsets
+    // are constants); an empty resource reads zeros.
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    auto part_rsrc = [&](int o) {
+        const int32_t *base = p.part + ((int64_t)tail * p.split + o) * kTile +
+                              (int64_t)wave * kSlots * kWave * 4;
+        return make_rsrc(reinterpret_cast<const int8_t *>(base));
+    };
+    const uint32_t lane_off = (uint32_t)__lane_id() * 16;
+    const __amdgpu_buffer_rsrc_t mine = part_rsrc(piece);
+#pragma unroll
+    for (int s = 0; s < kSlots; s++)
+        __builtin_amdgcn_raw_buffer_store_b128(get(s), mine, lane_off, s * kWave * 16, kCoherent);
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned arrived = atomicAdd(p.count + tail, 1u);
+        *flag_lds = arrived == (unsigned)(p.split - 1);
+        if (*flag_lds)
+            atomicExch(p.count + tail, 0u);
+    }
+    __syncthreads();
+    const bool is_last = *flag_lds;
+    // Every wave has read the flag before any reuses the stage buffers for
+    // the output.
+    __syncthreads();
+    if (!is_last)
+        return false;
+    // The other pieces' sums (at most two: kMaxPieces is 3), read kBatch
+    // slots at a time: 2 kBatch 16-byte loads per lane in flight, so the
+    // whole combine takes kSlots / kBatch round trips.  A missing second
+    // piece reads zeros through an empty buffer resource.
+    static_assert(kMaxPieces <= 3 && kSlots % kBatch == 0, "combine batch shape");
+    const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t *>(p.part), (short)0, 0, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rs[2] = {part_rsrc((piece + 1) % p.split),
+                                          p.split > 2 ? part_rsrc((piece + 2) % p.split) : none};
+#pragma unroll
+    for (int q = 0; q < kSlots; q += kBatch) {
+        i32x4 t[kBatch][2];
+#pragma unroll
+        for (int h = 0; h < kBatch; h++)
+#pragma unroll
+            for (int o = 0; o < 2; o++)
+                t[h][o] = __builtin_amdgcn_raw_buffer_load_b128(rs[o], lane_off,
+                                                                (q + h) * kWave * 16, kCoherent);
+#pragma unroll
+        for (int h = 0; h < kBatch; h++)
+            add(q + h, t[h][0] + t[h][1]);
+        // (Otherwise the scheduler hoists every batch's loads to the top.)
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    return true;
+}
+
+// Second half of a staged output pass: the wave's LDS slice 'stage' holds
+// 4096 words, kPassRows = 4096 / CW rows of CW columns whose 16-byte chunks
+// sit at stage_slot(row, chunk); each of 16 store instructions writes whole
+// row segments (16 lanes per 256 bytes) to the output from (i, j).
+template <int CW>
+__device__ __forceinline__ int stage_slot(int row, int chunk)
+{
+    constexpr int kChunks = CW / 4;
+    return row * CW + ((chunk ^ (row & (kChunks - 1))) * 4);
+}
+
+//
+// PAIR: the last stage of a rotation whose blocks span this wave's columns and
+// those of the wave whose slice is 'partner' (same rows, the other CW
+// columns of each 2 CW-column block): every value v and its partner value w
+// become fl(fl(v + w) * had_scale) in the lower wave of the pair and
+// fl(fl(w - v) * had_scale) in the upper one.
+template <int CW, bool PAIR = false>
+__device__ __forceinline__ void store_pass(const GemmParams &p, const lds_i8 *stage, int i, int j,
+                                           const lds_i8 *partner = nullptr, bool upper = false)
+{
+    constexpr int kChunks = CW / 4;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
+    const int lane = __lane_id();
+    wait_lgkmcnt0();
+#pragma unroll
+    for (int k0 = 0; k0 < 16; k0 += 8) {
+        // Eight slots' reads in flight together; the empty asm pins them
+        // here (otherwise each is sunk into its guarded store below and
+        // waited for alone).
+        u32x4 t[8], o[8];
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            const int s16 = (k0 + k) * kWave + lane;     // 16-byte slot of the pass
+            const int at = 4 * stage_slot<CW>(s16 / kChunks, s16 % kChunks);
+            t[k] = *reinterpret_cast<lds_u32x4 *>(stage + at);
+            if constexpr (PAIR)
+                o[k] = *reinterpret_cast<lds_u32x4 *>(partner + at);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            asm volatile("" : "+v"(t[k]));
+            if constexpr (PAIR)
+                asm volatile("" : "+v"(o[k]));
+        }
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            const int s16 = (k0 + k) * kWave + lane;
+            const int row = s16 / kChunks, chunk = s16 % kChunks;
+            if constexpr (PAIR) {
+                const float sign = upper ? -1.0f : 1.0f;
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    // lo + hi (lower wave) or lo - hi (upper wave), rounded
+                    // once.
+                    const float v = __uint_as_float(t[k][e]), x = __uint_as_float(o[k][e]);
+                    const float lo = upper ? x : v, hi = upper ? v : x;
+                    t[k][e] = __float_as_uint(__builtin_fmaf(sign, hi, lo) * p.had_scale);
+                }
+            }
+            if (i + row < p.R && j + chunk * 4 < p.S)
+                *reinterpret_cast<u32x4 *>(static_cast<uint32_t *>(p.out) +
+                                           (int64_t)(i + row) * p.ldc + j + chunk * 4) = t[k];
+        }
+    }
+    wait_lgkmcnt0();
+}
+
+// Enqueue the buffer-to-LDS loads of stage s of a work unit (contraction
+// stage kb + s) into 'dst'.  Row operands address rows from their tile start
+// (abase, bbase), km operands columns from their tile start and contraction
+// rows from the stage.  Stages past the unit's end (s >= KT) are issued as
+// all-out-of-range loads: zero fills of a buffer that is never read, so every
+// iteration waits for the same number of loads.
+// (Only loads G0 .. G1 - 1 of the stage's OpA::kLoads + OpB::kLoads per
+// lane, A's first.)
+template <typename OpA, typename OpB, bool AKM, bool BKM, int kBK, int G0 = 0,
+          int G1 = OpA::kLoads + OpB::kLoads>
+__device__ __forceinline__ void issue_stage(const GemmParams &p, const int8_t *abase,
+                                            const int8_t *bbase, int alim, int blim, int kb,
+                                            int KT, int s, int8_t *dst)
+{
+    constexpr int nA = OpA::kLoads;
+    const bool live = s < KT;
+    const int k0 = live ? (kb + s) * kBK : 0;
+    if constexpr (G0 < nA) {
+        const int8_t *ak = AKM ? abase + (int64_t)k0 * p.lda : abase;
+        OpA::template issue<G0, (G1 < nA ? G1 : nA)>(make_rsrc(ak), p.lda, 0, alim,
+                                                     AKM ? 0 : k0, AKM ? p.T - k0 : p.T, live,
+                                                     dst);
+    }
+    if constexpr (G1 > nA) {
+        const int8_t *bk = BKM ? bbase + (int64_t)k0 * p.ldb : bbase;
+        OpB::template issue<(G0 > nA ? G0 - nA : 0), G1 - nA>(
+            make_rsrc(bk), p.ldb, 0, blim, BKM ? 0 : k0, BKM ? p.T - k0 : p.T, live,
+            dst + OpA::kBytes);
+    }
+}
+
+// Write one 16-byte chunk of a staged pass.
+template <int CW>
+__device__ __forceinline__ void stage_put(lds_i8 *stage, int row, int chunk, uint32_t a, uint32_t b,
+                                          uint32_t c, uint32_t d)
+{
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    *reinterpret_cast<__attribute__((address_space(3))) u32x4 *>(
+        stage + 4 * stage_slot<CW>(row, chunk)) = u32x4{a, b, c, d};
+}
+
+// f(std::integral_constant<int, I>{}) for I = 0 .. N - 1, so that the index
+// can feed immediate operands.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_seq(F &f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
+
+template <int N>
+__device__ __forceinline__ void wait_lgkmcnt()
+{
+    static_assert(N >= 0 && N < 16, "lgkmcnt range");
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Order of the 16x16x64 main loop's LDS reads in a stage: the head (the FN
+// column blocks of step 0, then row-block fragments 0 .. D - 1), then for
+// each fragment s first column block s of step 1 (s < FN) and then fragment
+// s + D.
+
+// LDS read instructions issued after the last read that fragment t's MFMAs
+// need (fragment t itself and, at a step's first fragment, that step's
+// column blocks) and before fragment t's wait: its lgkmcnt, since LDS reads
+// complete in order.
+template <int D, int FM, int FN, int cA, int cB, int kSteps>
+constexpr int reads_after(int t)
+{
+    const bool need_b = t % FM == 0;
+    const int kk = t / FM;
+    int n = 0;
+    for (int b = 0; b < FN; b++)
+        n = need_b && kk == 0 ? 0 : n + cB;
+    for (int x = 0; x < D; x++)
+        n = x == t ? 0 : n + cA;
+    for (int s = 0; s < t; s++) {
+        if (s < FN)
+            n = need_b && kk == 1 ? 0 : n + cB;
+        if (s + D < kSteps)
+            n = s + D == t ? 0 : n + cA;
+    }
+    return n;
+}
+
+// Four consecutive int64 running sums of row i from column j when this is the
+// last chunk of a contraction past the int32 bound, otherwise zeros.
+template <int MODE>
+__device__ __forceinline__ void ws4(const GemmParams &p, bool ok, int i, int j, int64_t e[4])
+{
+    typedef long long i64x2 __attribute__((ext_vector_type(2)));
+    if (MODE == MODE_CHUNK && p.ws_mode == 3 && ok && j < p.S) {
+        const i64x2 *w = reinterpret_cast<const i64x2 *>(p.ws + (int64_t)i * p.ldc + j);
+        const i64x2 lo = w[0], hi = w[1];
+        e[0] = lo[0]; e[1] = lo[1]; e[2] = hi[0]; e[3] = hi[1];
+    } else {
+        e[0] = e[1] = e[2] = e[3] = 0;
+    }
+}
+
+// fl32 of an accumulator plus the running sum of earlier chunks.
+template <int MODE>
+__device__ __forceinline__ float tofloat(const GemmParams &p, int32_t c, int64_t e)
+{
+    if constexpr (MODE == MODE_CHUNK)
+        return p.ws_mode == 3 ? (float)((int64_t)c + e) : (float)c;
+    else
+        return (float)c;
+}
+
+// The product kernel: 256 x 256 tiles, 8 waves of RW x CW = 128 x 64 outputs
+// in FM x FN = 8 x 4 blocks of 16 x 16, 128 contraction bytes per stage in
+// two LDS stages (two MFMA steps of 64 bytes each).  Per lane the 128 int32
+// sums of the wave tile fill 128 registers.  A step's column-block fragments
+// are double-buffered (the next step's load behind the current one's MFMAs),
+// while the row-block fragments stream through registers: each one's reads
+// are issued kAhead fragments ahead of its four MFMAs (one per column block).
+// Double-buffering whole steps instead, as 32x32x32 blocks allow, would need
+// 96 fragment registers and spill.  Every fragment read is issued by inline
+// asm (constant offsets in the instruction) and waited for with an lgkmcnt
+// that counts the reads issued after it.
+//
+// The B operand is the MFMA's first operand, so block (a, b) holds C
+// transposed: lane l has output row 16 a + l % 16 and, in register e, output
+// column 16 b + 4 (l / 16) + e.
+template <int WM, int WN, bool AKM, bool BKM, int EPI, int MODE>
+__global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
+{
+    constexpr int BM = 256, BN = 256, kBK = 128;
+    constexpr int NT = WM * WN * kWave;
+    constexpr int RW = BM / WM, CW = BN / WN;
+    constexpr int FM = RW / 16, FN = CW / 16;
+    constexpr int NK = kBK / 64;                 // MFMA steps per stage
+    constexpr int kSteps = NK * FM;              // row-block fragments per stage
+    constexpr int kAhead = 4;                    // row-block fragments read ahead
+    constexpr int kSpread = 4;                   // fragments the stage loads spread over
+    static_assert(NK == 2 && kSteps % 8 == 0 && kAhead <= 4 && FN <= kSteps - kAhead,
+                  "fragment schedule shape");
+    using OpA = Operand<BM, AKM, NT, kBK>;
+    using OpB = Operand<BN, BKM, NT, kBK>;
+    constexpr int kStage = OpA::kBytes + OpB::kBytes;
+    constexpr int kLoads = OpA::kLoads + OpB::kLoads;
+    static_assert(kLoads % kSpread == 0, "stage loads per fragment");
+    constexpr int cA = OpA::kReads, cB = OpB::kReads;
+    __shared__ __attribute__((aligned(1024))) int8_t smem[2 * kStage];
+
+    const WorkUnit u = work_unit<MODE>(p, kBK);
+    const int kb = u.kb, KT = u.KT;
+    const int i0 = u.ti * BM, j0 = u.tj * BN;
     const int lane = __lane_id();
     const int w = threadIdx.x / kWave;
     const int wi = w / WN, wj = w % WN;
-
-    // Row operands address rows from their tile start; km operands address
-    // columns from their tile start and contraction rows from each stage.
     const int8_t *abase = AKM ? p.a + i0 : p.a + (int64_t)i0 * p.lda;
     const int8_t *bbase = BKM ? p.b + j0 : p.b + (int64_t)j0 * p.ldb;
     const int alim = p.R - i0, blim = p.S - j0;
-
-    // Stage s of the unit (stage kb + s of the contraction) goes to buffer
-    // s % kStages.  Stages past the end are issued as all-out-of-range loads
-    // (zero fills of a buffer that is never read) so every iteration waits
-    // for the same number of loads.
-    auto issue = [&](int s) {
-        const bool live = s < KT;
-        const int k0 = live ? (kb + s) * kBK : 0;
-        int8_t *dst = smem + (s % kStages) * kStage;
-        const int8_t *ak = AKM ? abase + (int64_t)k0 * p.lda : abase;
-        const int8_t *bk = BKM ? bbase + (int64_t)k0 * p.ldb : bbase;
-        OpA::issue(make_rsrc(ak), p.lda, 0, alim, AKM ? 0 : k0, AKM ? p.T - k0 : p.T, live, dst);
-        OpB::issue(make_rsrc(bk), p.ldb, 0, blim, BKM ? 0 : k0, BKM ? p.T - k0 : p.T, live,
-                   dst + OpA::kBytes);
+    // Part G of stage s's buffer-to-LDS loads, into buffer s % 2.
+    auto issue = [&](int s, auto G) {
+        constexpr int g = decltype(G)::value, per = kLoads / kSpread;
+        issue_stage<OpA, OpB, AKM, BKM, kBK, g * per, (g + 1) * per>(
+            p, abase, bbase, alim, blim, kb, KT, s, smem + (s & 1) * kStage);
     };
 
-    i32x16 acc[FM][FN];
+    // Lane offsets of this wave's fragments inside a stage: per step for a
+    // row operand (blocks at constant offsets), per block for a km operand
+    // (steps at constant offsets).
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_i8 *)smem;
+    uint32_t offA[AKM ? FM : NK], offB[BKM ? FN : NK];
+#pragma unroll
+    for (int x = 0; x < (AKM ? FM : NK); x++)
+        offA[x] = AKM ? OpA::off(wi * RW + 16 * x, 0) : OpA::off(wi * RW, x);
+#pragma unroll
+    for (int x = 0; x < (BKM ? FN : NK); x++)
+        offB[x] = OpA::kBytes + (BKM ? OpB::off(wj * CW + 16 * x, 0) : OpB::off(wj * CW, x));
+
+    i32x4 acc[FM][FN];
 #pragma unroll
     for (int a = 0; a < FM; a++)
 #pragma unroll
         for (int b = 0; b < FN; b++)
-            acc[a][b] = i32x16{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+            acc[a][b] = i32x4{0, 0, 0, 0};
 
-    // Fragment reads of contraction step kk of a stage (into fa, fb), their
-    // wait, and the MFMAs of one step.
-    auto load = [&](const int8_t *stage, int kk, typename OpA::Raw *fa, typename OpB::Raw *fb) {
-        const int8_t *lb = stage + OpA::kBytes;
-#pragma unroll
-        for (int a = 0; a < FM; a++)
-            OpA::frag(stage, wi * (BM / WM) + a * 32, kk, fa[a]);
-#pragma unroll
-        for (int b = 0; b < FN; b++)
-            OpB::frag(lb, wj * (BN / WN) + b * 32, kk, fb[b]);
+    typename OpA::Raw fa[8];          // row-block fragment t in fa[t % 8]
+    typename OpB::Raw fb[NK][FN];     // column-block fragments of each step
+    // Fragment t = FM kk + f (row block f, step kk) of the stage at sb.
+    auto read_a = [&](uint32_t sb, auto T) {
+        constexpr int t = decltype(T)::value, kk = t / FM, f = t % FM;
+        if constexpr (AKM)
+            OpA::template frag<kk * OpA::kStep>(sb + offA[f], fa[t % 8]);
+        else
+            OpA::template frag<f * OpA::kBlock>(sb + offA[kk], fa[t % 8]);
     };
-    auto settle = [&](typename OpA::Raw *fa, typename OpB::Raw *fb) {
-        wait_lgkmcnt0();
-#pragma unroll
-        for (int a = 0; a < FM; a++)
-            OpA::settle(fa[a]);
-#pragma unroll
-        for (int b = 0; b < FN; b++)
-            OpB::settle(fb[b]);
+    auto read_b = [&](uint32_t sb, auto KK, auto Bi) {
+        constexpr int kk = decltype(KK)::value, b = decltype(Bi)::value;
+        if constexpr (BKM)
+            OpB::template frag<kk * OpB::kStep>(sb + offB[b], fb[kk][b]);
+        else
+            OpB::template frag<b * OpB::kBlock>(sb + offB[kk], fb[kk][b]);
     };
-    auto mma = [&](const typename OpA::Raw *fa, const typename OpB::Raw *fb) {
-        i32x4 av[FM], bv[FN];
-#pragma unroll
-        for (int a = 0; a < FM; a++)
-            av[a] = OpA::value(fa[a]);
+    auto mfma = [&](auto T) {
+        constexpr int t = decltype(T)::value, kk = t / FM, f = t % FM;
+        const i32x4 av = OpA::value(fa[t % 8]);
 #pragma unroll
         for (int b = 0; b < FN; b++)
-            bv[b] = OpB::value(fb[b]);
-#pragma unroll
-        for (int a = 0; a < FM; a++)
-#pragma unroll
-            for (int b = 0; b < FN; b++)
-                acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bv[b], av[a], acc[a][b], 0, 0, 0);
+            acc[f][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(OpB::value(fb[kk][b]), av,
+                                                              acc[f][b], 0, 0, 0);
+    };
+    using Zero = std::integral_constant<int, 0>;
+    using One = std::integral_constant<int, 1>;
+    auto head = [&](uint32_t sb) {
+        static_for<FN>([&](auto Bi) { read_b(sb, Zero{}, Bi); });
+        static_for<kAhead>([&](auto T) { read_a(sb, T); });
     };
 
-    // Stage s lives in buffer s % kStages and is issued at the top of stage
-    // s - kStages + 1, into the buffer that the barrier closing the previous
-    // stage has freed (every wave had read that stage into registers).  The
-    // fragment sets alternate: the reads of step kk + 1 are in flight while
-    // the MFMAs of step kk run; the first step of the next stage is read right
-    // after the barrier that ends this one.  sched_barrier(0) pins this order
-    // and sched_group_barrier spreads the stage's buffer loads over the MFMAs
-    // of the first step.
-    typename OpA::Raw fa[2][FM];
-    typename OpB::Raw fb[2][FN];
-#pragma unroll
-    for (int s = 0; s < kStages - 1; s++)
-        issue(s);
-    wait_vmcnt<(kStages - 2) * kLoads>();
+    // Per stage: fragment t's MFMAs follow its wait; before them the reads of
+    // its share of step 1's column blocks and of fragment t + kAhead are
+    // issued.  After fragment kSteps - kAhead - 1 every read of the stage is
+    // waited for, the stage barrier passes, the next stage's head reads are
+    // issued and the last kAhead fragments' MFMAs cover their latency.  The
+    // next stage's buffer-to-LDS loads are issued among the MFMAs of the
+    // first kSpread fragments.
+    static_for<kSpread>([&](auto G) { issue(0, G); });
+    wait_vmcnt<0>();
     barrier_no_fence();
-    load(smem, 0, fa[0], fb[0]);
-
+    head(lds0);
     for (int kt = 0; kt < KT; kt++) {
-        const int8_t *cur = smem + (kt % kStages) * kStage;
+        const uint32_t sb = lds0 + (kt & 1) * kStage;
+        static_for<kSteps - kAhead>([&](auto T) {
+            constexpr int t = decltype(T)::value;
+            wait_lgkmcnt<reads_after<kAhead, FM, FN, cA, cB, kSteps>(t)>();
+            OpA::settle(fa[t % 8]);
+            if constexpr (t % FM == 0) {
 #pragma unroll
-        for (int kk = 0; kk + 1 < NK; kk++) {
-            settle(fa[kk & 1], fb[kk & 1]);
-            load(cur, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
-            if (kk == 0)
-                issue(kt + kStages - 1);
-            mma(fa[kk & 1], fb[kk & 1]);
-            if (kk == 0) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 2 * (FM + FN), 0);
+                for (int b = 0; b < FN; b++)
+                    OpB::settle(fb[t / FM][b]);
+            }
+            if constexpr (t < FN)
+                read_b(sb, One{}, T);
+            read_a(sb, std::integral_constant<int, t + kAhead>{});
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (t < kSpread) {
+                issue(kt + 1, T);
+                mfma(T);
 #pragma unroll
-                for (int g = 0; g < kLoads; g++) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, (FM * FN + kLoads - 1) / kLoads, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                for (int g = 0; g < FN; g++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, (kLoads / kSpread + FN - 1) / FN, 0);
                 }
+            } else {
+                mfma(T);
             }
             __builtin_amdgcn_sched_barrier(0);
-        }
-        // Stage kt + 1 has landed once at most the loads of stages kt + 2 ..
-        // kt + kStages - 1 are outstanding.
-        wait_vmcnt<(kStages - 2) * kLoads>();
-        settle(fa[(NK - 1) & 1], fb[(NK - 1) & 1]);
+        });
+        // Stage kt + 1 has landed (its loads were the only ones in flight).
+        wait_vmcnt<0>();
+        wait_lgkmcnt<0>();
+        static_for<kAhead>(
+            [&](auto T) { OpA::settle(fa[(kSteps - kAhead + decltype(T)::value) % 8]); });
         barrier_no_fence();
         if (kt + 1 < KT)
-            load(smem + ((kt + 1) % kStages) * kStage, 0, fa[0], fb[0]);
+            head(lds0 + ((kt + 1) & 1) * kStage);
         __builtin_amdgcn_sched_barrier(0);
-        mma(fa[(NK - 1) & 1], fb[(NK - 1) & 1]);
+        static_for<kAhead>([&](auto T) {
+            mfma(std::integral_constant<int, kSteps - kAhead + decltype(T)::value>{});
+        });
         __builtin_amdgcn_sched_barrier(0);
     }
     wait_vmcnt<0>();
 
-    // Epilogue.  The MFMA ran with B as its first operand, so each 32x32
-    // block holds C transposed: lane l has output row l % 32 and, in register
-    // 4 g + e, output column 8 g + 4 (l / 32) + e.
-    typedef long long i64x2 __attribute__((ext_vector_type(2)));
-    auto ws_at = [&](int i, int j) { return p.ws + (int64_t)i * p.ldc + j; };
-    // Four consecutive int64 running sums of row i from column j, or zeros
-    // when this is not the last chunk of a split contraction.
-    auto ws4 = [&](bool ok, int i, int j, int64_t e[4]) {
-        if (MODE == MODE_CHUNK && p.ws_mode == 3 && ok && j < p.S) {
-            const i64x2 *w = reinterpret_cast<const i64x2 *>(ws_at(i, j));
-            const i64x2 lo = w[0], hi = w[1];
-            e[0] = lo[0]; e[1] = lo[1]; e[2] = hi[0]; e[3] = hi[1];
-        } else {
-            e[0] = e[1] = e[2] = e[3] = 0;
-        }
-    };
-    // fl32 of the accumulator (plus the running sum of earlier chunks).
-    auto tofloat = [&](int32_t c, int64_t e) {
-        if constexpr (MODE == MODE_CHUNK)
-            return p.ws_mode == 3 ? (float)((int64_t)c + e) : (float)c;
-        else
-            return (float)c;
-    };
     if constexpr (MODE == MODE_SPLIT) {
-        if (tail >= 0) {
-            // Store this unit's int32 sums in register order (coalesced
-            // 16-byte runs) and count its arrival; the last of the tile's
-            // units to arrive adds the others' sums (exact: int32 addition of
-            // bounded partials) and runs the epilogue.
-            //
-            // The partial sums cross XCDs, whose L2s are not coherent with
-            // one another.  They are written and read with the device-scope
-            // coherence bit (sc1: the bit a device-scope relaxed atomic access
-            // carries), so they never sit in an L2 as stale or dirty lines;
-            // each wave waits for its stores to complete before the barrier
-            // that precedes the arrival count, and the reader's loads are
-            // issued after it observes the count.  A device-scope fence would
-            // do the same by writing back and invalidating whole L2s, which
-            // stalls the chip while the rest of the grid is still storing
-            // outputs.
-            //
-            // The arrival flag lives in the stage buffers, free once every
-            // wave has passed the main loop's last barrier: a second LDS
-            // object would make the compiler wait for each stage's
-            // buffer-to-LDS loads before any LDS read.
-            int *last_unit = reinterpret_cast<int *>(smem);
-            // Unit o's sums: wave w's FM x FN x 4 16-byte slots per lane, the
-            // wave's slots contiguous.  Buffer resources start at this wave's
-            // run (so slot offsets are constants); an empty resource reads
-            // zeros.
-            constexpr int kSlots = FM * FN * 4;
-            const int wave = __builtin_amdgcn_readfirstlane(w);
-            auto part_rsrc = [&](int o) {
-                const int32_t *base = p.part + ((int64_t)tail * p.split + o) * (BM * BN) +
-                                      (int64_t)wave * kSlots * kWave * 4;
-                return make_rsrc(reinterpret_cast<const int8_t *>(base));
-            };
-            const uint32_t lane_off = (uint32_t)lane * 16;
-            const __amdgpu_buffer_rsrc_t mine = part_rsrc(piece);
-#pragma unroll
-            for (int a = 0; a < FM; a++)
-#pragma unroll
-                for (int b = 0; b < FN; b++)
-#pragma unroll
-                    for (int g = 0; g < 4; g++) {
-                        const int slot = (a * FN + b) * 4 + g;
-                        const i32x16 &c = acc[a][b];
-                        __builtin_amdgcn_raw_buffer_store_b128(
-                            i32x4{c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]}, mine,
-                            lane_off, slot * kWave * 16, kCoherent);
-                    }
-            wait_vmcnt<0>();
-            __syncthreads();
-            if (threadIdx.x == 0) {
-                const unsigned arrived = atomicAdd(p.count + tail, 1u);
-                *last_unit = arrived == (unsigned)(p.split - 1);
-                if (*last_unit)
-                    atomicExch(p.count + tail, 0u);
-            }
-            __syncthreads();
-            const bool is_last = *last_unit;
-            // Every wave has read the flag before any reuses the stage
-            // buffers for the output.
-            __syncthreads();
-            if (!is_last)
-                return;
-            // The other pieces' sums (at most two: kMaxPieces is 3), read for
-            // two accumulator blocks at a time: sixteen 16-byte loads per
-            // lane in flight, so the whole combine takes FM * FN / 2 round
-            // trips.  A missing second piece reads zeros through an empty
-            // buffer resource.
-            static_assert(kMaxPieces <= 3 && (FM * FN) % 2 == 0, "combine batch shape");
-            const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<int32_t *>(p.part), (short)0, 0, kRsrcWord3);
-            const __amdgpu_buffer_rsrc_t rs[2] = {
-                part_rsrc((piece + 1) % p.split),
-                p.split > 2 ? part_rsrc((piece + 2) % p.split) : none};
-#pragma unroll
-            for (int q = 0; q < FM * FN; q += 2) {
-                i32x4 t[2][2][4];
-#pragma unroll
-                for (int h = 0; h < 2; h++)
-#pragma unroll
-                    for (int u = 0; u < 2; u++)
-#pragma unroll
-                        for (int g = 0; g < 4; g++)
-                            t[h][u][g] = __builtin_amdgcn_raw_buffer_load_b128(
-                                rs[u], lane_off, ((q + h) * 4 + g) * kWave * 16, kCoherent);
-#pragma unroll
-                for (int h = 0; h < 2; h++)
-#pragma unroll
-                    for (int u = 0; u < 2; u++)
-#pragma unroll
-                        for (int g = 0; g < 4; g++)
-#pragma unroll
-                            for (int e = 0; e < 4; e++)
-                                acc[(q + h) / FN][(q + h) % FN][4 * g + e] += t[h][u][g][e];
-            }
-        }
+        // Slot b + FN a of a lane holds block (a, b).
+        if (u.tail >= 0 &&
+            !split_combine<FM * FN, BM * BN, 8>(
+                p, u.tail, u.piece, reinterpret_cast<int *>(smem),
+                [&](int s) { return acc[s / FN][s % FN]; },
+                [&](int s, i32x4 v) { acc[s / FN][s % FN] += v; }))
+            return;
     }
-    if constexpr (MODE == MODE_CHUNK && EPI != EPI_RAW) {
+    if constexpr (MODE == MODE_CHUNK) {
+        // Not the last chunk: store (ws_mode 1) or add (2) the int32 sums
+        // into the int64 running sums.
         if (p.ws_mode == 1 || p.ws_mode == 2) {
+            typedef long long i64x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
             for (int a = 0; a < FM; a++) {
-                const int i = i0 + wi * (BM / WM) + a * 32 + lane % 32;
-                if (i >= p.R)
-                    continue;
+                const int i = i0 + wi * RW + 16 * a + lane % 16;
 #pragma unroll
                 for (int b = 0; b < FN; b++) {
-#pragma unroll
-                    for (int g = 0; g < 4; g++) {
-                        const int j = j0 + wj * (BN / WN) + b * 32 + 8 * g + 4 * (lane / 32);
-                        if (j >= p.S)
-                            continue;
-                        i64x2 *w = reinterpret_cast<i64x2 *>(ws_at(i, j));
-                        i64x2 lo = {acc[a][b][4 * g], acc[a][b][4 * g + 1]};
-                        i64x2 hi = {acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]};
-                        if (p.ws_mode == 2) {
-                            lo = lo + w[0];
-                            hi = hi + w[1];
-                        }
-                        w[0] = lo;
-                        w[1] = hi;
+                    const int j = j0 + wj * CW + 16 * b + 4 * (lane / 16);
+                    if (i >= p.R || j >= p.S)
+                        continue;
+                    i64x2 *ws = reinterpret_cast<i64x2 *>(p.ws + (int64_t)i * p.ldc + j);
+                    i64x2 lo = {acc[a][b][0], acc[a][b][1]};
+                    i64x2 hi = {acc[a][b][2], acc[a][b][3]};
+                    if (p.ws_mode == 2) {
+                        lo = lo + ws[0];
+                        hi = hi + ws[1];
                     }
+                    ws[0] = lo;
+                    ws[1] = hi;
                 }
+                // (Otherwise every block's running sums are loaded at once.)
+                __builtin_amdgcn_sched_barrier(0);
             }
             return;
         }
     }
-    // Output values of row block a of this wave, as 32-bit patterns in the
-    // accumulator layout: v[b][4 g + e] belongs to row i0 + wi RW + 32 a +
-    // lane % 32 and column j0 + wj CW + 32 b + 8 g + 4 (lane / 32) + e.  Rows
-    // and columns past the output give zeros (they are never stored).
-    constexpr int RW = BM / WM, CW = BN / WN;
-    auto row_values = [&](int a, uint32_t (&out)[FN][16]) {
-        const int i = i0 + wi * RW + a * 32 + lane % 32;
+
+    // Output values of row block a as 32-bit patterns, in the accumulator
+    // layout: o[b][e] belongs to row i0 + wi RW + 16 a + l % 16 and column
+    // j0 + wj CW + 16 b + 4 (l / 16) + e.  Rows and columns past the output
+    // give zeros (they are never stored).  The forward product's column
+    // scales and bias are the same for every row block.
+    f32x4 cs[FN], bj[FN];
+    if constexpr (EPI == EPI_FWD) {
+#pragma unroll
+        for (int b = 0; b < FN; b++) {
+            const int j = j0 + wj * CW + 16 * b + 4 * (lane / 16);
+            const bool ok = j < p.S;
+            cs[b] = ok ? *reinterpret_cast<const f32x4 *>(p.scol + j) : f32x4{0, 0, 0, 0};
+            bj[b] = ok && p.bias ? *reinterpret_cast<const f32x4 *>(p.bias + j)
+                                 : f32x4{0, 0, 0, 0};
+        }
+    }
+    // Row scales of every row block, loaded before the first store: on
+    // gfx950 a load's vmcnt wait also waits for the stores issued before it.
+    float rsv[FM];
+#pragma unroll
+    for (int a = 0; a < FM; a++) {
+        const int i = i0 + wi * RW + 16 * a + lane % 16;
+        rsv[a] = EPI != EPI_RAW && i < p.R ? p.srow[i] : 0.0f;
+    }
+    auto block_values = [&](int a, uint32_t (&o)[FN][4]) {
+        const int i = i0 + wi * RW + 16 * a + lane % 16;
         const bool row_ok = i < p.R;
-        float rs = 0.0f;
-        if constexpr (EPI != EPI_RAW)
-            rs = row_ok ? p.srow[i] : 0.0f;
+        const float rs = rsv[a];
+        float v[FN][4];
+#pragma unroll
+        for (int b = 0; b < FN; b++) {
+            if constexpr (EPI == EPI_RAW) {
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    o[b][e] = (uint32_t)acc[a][b][e];
+            } else {
+                int64_t ext[4];
+                ws4<MODE>(p, row_ok, i, j0 + wj * CW + 16 * b + 4 * (lane / 16), ext);
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    v[b][e] = tofloat<MODE>(p, acc[a][b][e], ext[e]) * rs;
+                    if constexpr (EPI == EPI_FWD) {
+                        v[b][e] = v[b][e] * cs[b][e];
+                        if (p.bias)
+                            v[b][e] = v[b][e] + bj[b][e];
+                    }
+                }
+            }
+        }
         if constexpr (EPI == EPI_ROWSCALE_HAD) {
-            static_assert(FN == 4, "the rotating epilogue needs 128-column wave tiles");
-            // Within the wave's 128 columns, column c = 32 b + 8 g + 4 h + e
-            // with h = lane / 32: butterfly strides 1 and 2 pair registers e,
-            // stride 4 pairs lane l with lane l ^ 32, strides 8 and 16 pair
-            // registers g and strides 32 and 64 pair blocks b.  Stages run in
+            static_assert(CW == 64, "the rotating epilogue is laid out for 64-column wave tiles");
+            // Within a rotation block, column c = 64 (wj & 1) + 16 b + 4 h + e
+            // with h = lane / 16: butterfly strides 1 and 2 pair registers e,
+            // strides 4 and 8 pair lane l with lanes l ^ 16 and l ^ 32,
+            // strides 16 and 32 pair blocks b, and stride 64 pairs the two
+            // waves wj and wj ^ 1 (done in the store pass).  Stages run in
             // ascending stride, the lower element becoming lo + hi and the
             // upper lo - hi, then every element is scaled once: the same
             // operations, in the same order, as the separate rotation of the
-            // dequantized row.  (Lanes l and l ^ 32 share the row, so a row
-            // past the output is all zeros on both.)
-            const bool upper = lane >= 32;
-            float v[FN][16];
-#pragma unroll
-            for (int b = 0; b < FN; b++)
-#pragma unroll
-                for (int g = 0; g < 4; g++) {
-                    int64_t e[4];
-                    ws4(row_ok, i, j0 + wj * CW + b * 32 + 8 * g + 4 * (lane / 32), e);
-#pragma unroll
-                    for (int r = 0; r < 4; r++)
-                        v[b][4 * g + r] = tofloat(acc[a][b][4 * g + r], e[r]) * rs;
-                }
+            // dequantized row.  (The four lanes holding a row agree on
+            // whether it is past the output, where all values are zero.)
             auto pair = [](float &lo, float &hi) {
                 const float x = lo, y = hi;
                 lo = x + y;
@@ -624,178 +849,110 @@ __global__ __launch_bounds__(WM *WN * 64, OCC) void gemm_kernel(GemmParams p)
             };
             if (p.had > 1)
 #pragma unroll
-                for (int b = 0; b < FN; b++)
-#pragma unroll
-                    for (int g = 0; g < 4; g++) {
-                        pair(v[b][4 * g], v[b][4 * g + 1]);
-                        pair(v[b][4 * g + 2], v[b][4 * g + 3]);
-                    }
+                for (int b = 0; b < FN; b++) {
+                    pair(v[b][0], v[b][1]);
+                    pair(v[b][2], v[b][3]);
+                }
             if (p.had > 2)
 #pragma unroll
-                for (int b = 0; b < FN; b++)
-#pragma unroll
-                    for (int g = 0; g < 4; g++) {
-                        pair(v[b][4 * g], v[b][4 * g + 2]);
-                        pair(v[b][4 * g + 1], v[b][4 * g + 3]);
-                    }
-            if (p.had > 4)
-#pragma unroll
-                for (int b = 0; b < FN; b++)
-#pragma unroll
-                    for (int r = 0; r < 16; r++) {
-                        // v_permlane32_swap exchanges the upper half of its
-                        // first operand with the lower half of its second:
-                        // with both the same value, lane l finds lane
-                        // l ^ 32's value in the second result (l < 32) or
-                        // the first (l >= 32).
-                        const uint32_t u = __float_as_uint(v[b][r]);
-                        const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-                        const float o = __uint_as_float(upper ? sw[0] : sw[1]);
-                        v[b][r] = upper ? o - v[b][r] : v[b][r] + o;
-                    }
-            if (p.had > 8)
+                for (int b = 0; b < FN; b++) {
+                    pair(v[b][0], v[b][2]);
+                    pair(v[b][1], v[b][3]);
+                }
+            // v_permlane16_swap exchanges the odd 16-lane rows of its first
+            // operand with the even rows of its second, v_permlane32_swap the
+            // upper half of its first with the lower half of its second: with
+            // both operands the same value, every lane finds the lower
+            // element of its pair (lo) in the first result and the upper
+            // (hi) in the second.  lo + sign hi, with sign -1 in the upper
+            // lanes, is computed as one fused multiply-add: sign hi is exact,
+            // so it rounds once, exactly as lo + hi or lo - hi.
+            if (p.had > 4) {
+                const float sign = (lane / 16) & 1 ? -1.0f : 1.0f;
 #pragma unroll
                 for (int b = 0; b < FN; b++)
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
-                        pair(v[b][e], v[b][4 + e]);
-                        pair(v[b][8 + e], v[b][12 + e]);
+                        const uint32_t x = __float_as_uint(v[b][e]);
+                        const auto sw = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+                        v[b][e] = __builtin_fmaf(sign, __uint_as_float(sw[1]),
+                                                 __uint_as_float(sw[0]));
                     }
+            }
+            if (p.had > 8) {
+                const float sign = lane >= 32 ? -1.0f : 1.0f;
+#pragma unroll
+                for (int b = 0; b < FN; b++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const uint32_t x = __float_as_uint(v[b][e]);
+                        const auto sw = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+                        v[b][e] = __builtin_fmaf(sign, __uint_as_float(sw[1]),
+                                                 __uint_as_float(sw[0]));
+                    }
+            }
             if (p.had > 16)
 #pragma unroll
-                for (int b = 0; b < FN; b++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        pair(v[b][e], v[b][8 + e]);
-                        pair(v[b][4 + e], v[b][12 + e]);
-                    }
+                for (int e = 0; e < 4; e++) {
+                    pair(v[0][e], v[1][e]);
+                    pair(v[2][e], v[3][e]);
+                }
             if (p.had > 32)
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    pair(v[0][r], v[1][r]);
-                    pair(v[2][r], v[3][r]);
+                for (int e = 0; e < 4; e++) {
+                    pair(v[0][e], v[2][e]);
+                    pair(v[1][e], v[3][e]);
                 }
-            if (p.had > 64)
+            if (p.had <= 64)
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    pair(v[0][r], v[2][r]);
-                    pair(v[1][r], v[3][r]);
-                }
+                for (int b = 0; b < FN; b++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        v[b][e] = v[b][e] * p.had_scale;
+        }
+        if constexpr (EPI != EPI_RAW) {
 #pragma unroll
             for (int b = 0; b < FN; b++)
 #pragma unroll
-                for (int r = 0; r < 16; r++)
-                    out[b][r] = __float_as_uint(v[b][r] * p.had_scale);
-        } else {
-#pragma unroll
-            for (int b = 0; b < FN; b++)
-#pragma unroll
-                for (int g = 0; g < 4; g++) {
-                    const int j = j0 + wj * CW + b * 32 + 8 * g + 4 * (lane / 32);
-                    const i32x16 &c = acc[a][b];
-                    if constexpr (EPI == EPI_RAW) {
-#pragma unroll
-                        for (int e = 0; e < 4; e++)
-                            out[b][4 * g + e] = (uint32_t)c[4 * g + e];
-                    } else {
-                        const bool ok = row_ok && j < p.S;
-                        int64_t w[4];
-                        ws4(ok, i, j, w);
-                        f32x4 v;
-#pragma unroll
-                        for (int e = 0; e < 4; e++)
-                            v[e] = tofloat(c[4 * g + e], w[e]) * rs;
-                        if constexpr (EPI == EPI_FWD) {
-                            const f32x4 cs = ok ? *reinterpret_cast<const f32x4 *>(p.scol + j)
-                                                : f32x4{0, 0, 0, 0};
-#pragma unroll
-                            for (int e = 0; e < 4; e++)
-                                v[e] = v[e] * cs[e];
-                            if (p.bias) {
-                                const f32x4 bj = ok ? *reinterpret_cast<const f32x4 *>(p.bias + j)
-                                                    : f32x4{0, 0, 0, 0};
-#pragma unroll
-                                for (int e = 0; e < 4; e++)
-                                    v[e] = v[e] + bj[e];
-                            }
-                        }
-#pragma unroll
-                        for (int e = 0; e < 4; e++)
-                            out[b][4 * g + e] = __float_as_uint(v[e]);
-                    }
-                }
+                for (int e = 0; e < 4; e++)
+                    o[b][e] = __float_as_uint(v[b][e]);
         }
     };
 
-    // Stores go through LDS so that each store instruction writes whole row
-    // segments (16 lanes per 256 bytes) instead of 32 bytes of 32 rows: each
-    // wave owns a 16 KiB slice of the (now idle) stage buffers and passes its
-    // RW x CW values through it in passes of 4096 words.  Within a row the
-    // 16-byte chunks are XOR-swizzled by the row, so both the column-wise
-    // writes and the row-wise reads spread over the banks.
-    constexpr int kChunks = CW / 4;                  // 16-byte chunks per row
-    constexpr int kPassRows = 4096 / CW;             // rows per pass
-    constexpr int kPassBlocks = kPassRows / 32;      // 32-row blocks per pass
-    static_assert(kPassBlocks >= 1 && FM % kPassBlocks == 0, "staging pass shape");
-    static_assert(kStages * kStage >= NT / kWave * 4096 * 4, "staging needs 16 KiB per wave");
+    // Stores pass through the wave's 16 KiB slice of the idle stage buffers
+    // (see store_pass), kPassRows rows at a time.
+    constexpr int kPassRows = 4096 / CW;
+    constexpr int kPassBlocks = kPassRows / 16;
+    static_assert(FM % kPassBlocks == 0 && 2 * kStage >= NT / kWave * 4096 * 4, "staging shape");
     lds_i8 *stage_base = (lds_i8 *)smem + w * 4096 * 4;
-    auto slot = [&](int row, int chunk) { return row * CW + ((chunk ^ (row & (kChunks - 1))) * 4); };
 #pragma unroll
     for (int pass = 0; pass < FM / kPassBlocks; pass++) {
 #pragma unroll
         for (int q = 0; q < kPassBlocks; q++) {
-            const int a = pass * kPassBlocks + q;
-            uint32_t v[FN][16];
-            row_values(a, v);
-            const int row = q * 32 + lane % 32;
+            uint32_t o[FN][4];
+            block_values(pass * kPassBlocks + q, o);
 #pragma unroll
             for (int b = 0; b < FN; b++)
-#pragma unroll
-                for (int g = 0; g < 4; g++) {
-                    const int chunk = b * 8 + 2 * g + lane / 32;
-                    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-                    *reinterpret_cast<__attribute__((address_space(3))) u32x4 *>(
-                        stage_base + 4 * slot(row, chunk)) =
-                        u32x4{v[b][4 * g], v[b][4 * g + 1], v[b][4 * g + 2], v[b][4 * g + 3]};
-                }
+                stage_put<CW>(stage_base, 16 * q + lane % 16, 4 * b + lane / 16, o[b][0], o[b][1],
+                              o[b][2], o[b][3]);
+            // (The int64 sums of later blocks would be loaded here too, all
+            // at once.)
+            if constexpr (MODE == MODE_CHUNK)
+                __builtin_amdgcn_sched_barrier(0);
         }
-        wait_lgkmcnt0();
-#pragma unroll
-        for (int k = 0; k < 16; k++) {
-            const int s16 = k * kWave + lane;            // 16-byte slot of the pass
-            const int row = s16 / kChunks, chunk = s16 % kChunks;
-            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-            const u32x4 t = *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(
-                stage_base + 4 * slot(row, chunk));
-            const int i = i0 + wi * RW + pass * kPassRows + row;
-            const int j = j0 + wj * CW + chunk * 4;
-            if (i < p.R && j < p.S)
-                *reinterpret_cast<u32x4 *>(static_cast<uint32_t *>(p.out) + (int64_t)i * p.ldc +
-                                           j) = t;
+        const int i = i0 + wi * RW + pass * kPassRows, j = j0 + wj * CW;
+        if (EPI == EPI_ROWSCALE_HAD && p.had > 64) {
+            // Rotation blocks of 128 columns: wave pairs (wj, wj ^ 1) finish
+            // the last stage through each other's slices, once both have
+            // written them and before either overwrites its own.  The
+            // barriers carry no fence, so the output stores stay in flight.
+            wait_lgkmcnt0();
+            barrier_no_fence();
+            store_pass<CW, true>(p, stage_base, i, j, (lds_i8 *)smem + (w ^ 1) * 4096 * 4, wj & 1);
+            barrier_no_fence();
+        } else {
+            store_pass<CW>(p, stage_base, i, j);
         }
-        wait_lgkmcnt0();
-    }
-}
-
-template <int BM, int BN, int WM, int WN, int BK, int OCC, bool AKM, bool BKM, int EPI>
-void run_gemm(const GemmParams &p0, hipStream_t st)
-{
-    GemmParams p = p0;
-    p.tiles_i = (p.R + BM - 1) / BM;
-    p.tiles_j = (p.S + BN - 1) / BN;
-    const int tiles = p.tiles_i * p.tiles_j;
-    if (p.ws_mode != 0) {
-        if constexpr (EPI != EPI_RAW)
-            hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, OCC, AKM, BKM, EPI, MODE_CHUNK>),
-                               dim3(tiles), dim3(WM * WN * 64), 0, st, p);
-    } else if (p.split >= 2) {
-        const unsigned grid = (unsigned)(p.full + (tiles - p.full) * p.split);
-        if constexpr (EPI != EPI_RAW)
-            hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, OCC, AKM, BKM, EPI, MODE_SPLIT>),
-                               dim3(grid), dim3(WM * WN * 64), 0, st, p);
-    } else {
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, OCC, AKM, BKM, EPI, MODE_PLAIN>),
-                           dim3(tiles), dim3(WM * WN * 64), 0, st, p);
     }
 }
 
@@ -918,13 +1075,36 @@ __global__ __launch_bounds__(256) void skinny_fwd_kernel(const int8_t *__restric
     }
 }
 
+template <int WM, int WN, bool AKM, bool BKM, int EPI>
+void run_gemm(const GemmParams &p0, hipStream_t st)
+{
+    GemmParams p = p0;
+    p.tiles_i = (p.R + 255) / 256;
+    p.tiles_j = (p.S + 255) / 256;
+    const int tiles = p.tiles_i * p.tiles_j;
+    const dim3 block(WM * WN * kWave);
+    if (p.ws_mode != 0) {
+        if constexpr (EPI != EPI_RAW)
+            hipLaunchKernelGGL((gemm_kernel<WM, WN, AKM, BKM, EPI, MODE_CHUNK>), dim3(tiles), block,
+                               0, st, p);
+    } else if (p.split >= 2) {
+        const unsigned grid = (unsigned)(p.full + (tiles - p.full) * p.split);
+        if constexpr (EPI != EPI_RAW)
+            hipLaunchKernelGGL((gemm_kernel<WM, WN, AKM, BKM, EPI, MODE_SPLIT>), dim3(grid), block,
+                               0, st, p);
+    } else {
+        hipLaunchKernelGGL((gemm_kernel<WM, WN, AKM, BKM, EPI, MODE_PLAIN>), dim3(tiles), block, 0,
+                           st, p);
+    }
+}
+
 // Tile configuration of the three products: 256 x 256 outputs per
 // workgroup, 8 waves each owning 128 x 64, 128 contraction bytes per stage
 // (two stages in flight in 128 KiB of LDS).
 template <bool AKM, bool BKM, int EPI>
 void run_cfg(const GemmParams &p, hipStream_t st)
 {
-    run_gemm<256, 256, 2, 4, 128, 1, AKM, BKM, EPI>(p, st);
+    run_gemm<2, 4, AKM, BKM, EPI>(p, st);
 }
 
 } // namespace
@@ -1005,10 +1185,10 @@ void launch_product(const ProductArgs &a, hipStream_t st)
         if (a.raw) {
             run_cfg<false, true, EPI_RAW>(p, st);
         } else if (a.had >= 2 && a.had <= 128) {
-            // dX with the un-rotation in the epilogue: 64 x 128 wave tiles.
+            // dX with the un-rotation in the epilogue.
             p.had = a.had;
             p.had_scale = a.had_scale;
-            run_gemm<256, 256, 4, 2, 128, 1, false, true, EPI_ROWSCALE_HAD>(p, st);
+            run_cfg<false, true, EPI_ROWSCALE_HAD>(p, st);
         } else {
             run_cfg<false, true, EPI_ROWSCALE>(p, st);
         }
