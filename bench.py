@@ -48,9 +48,9 @@ GEMMS = ("fwd", "bwd_dx", "bwd_dw")
 COPY_BYTES = 512 << 20        # calibration copy: reads and writes this many bytes
 # Kernel symbols behind each call, as rocprofv3 names them (a call's traffic
 # is the sum over its kernels).
-KERNEL_OF = {"fwd": ["gemm_kernel<256, 256, 2, 4, 128, 1, false, false, 2, 2>"],
-             "bwd_dx": ["gemm_kernel<256, 256, 4, 2, 128, 1, false, true, 3, 0>"],
-             "bwd_dw": ["gemm_kernel<256, 256, 2, 4, 128, 1, true, true, 1, 2>"],
+KERNEL_OF = {"fwd": ["gemm_kernel<2, 4, false, false, 2, 2>"],
+             "bwd_dx": ["gemm_kernel<2, 4, false, true, 3, 0>"],
+             "bwd_dw": ["gemm_kernel<2, 4, true, true, 1, 2>"],
              "quantize_x": ["quant_rows_kernel<true, 256, 3, 128, false>"],
              "quantize_dy": ["quant_rows_kernel<true, 512, 2, 0, true>", "grad_cols_reduce_kernel",
                              "colquant_kernel<true>"],
