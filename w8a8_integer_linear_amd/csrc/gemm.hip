@@ -533,14 +533,20 @@ __device__ __forceinline__ void wait_lgkmcnt()
 
 // Order of the 16x16x64 main loop's LDS reads in a stage: the head (the FN
 // column blocks of step 0, then row-block fragments 0 .. D - 1), then for
-// each fragment s first column block s of step 1 (s < FN) and then fragment
-// s + D.
+// each fragment s first column block s / E of step 1 (when s is a multiple
+// of E and s / E < FN) and then fragment s + D.
+template <int E, int FN>
+constexpr int b_at(int s)
+{
+    return s % E == 0 && s / E < FN ? s / E : -1;
+}
+
 
 // LDS read instructions issued after the last read that fragment t's MFMAs
 // need (fragment t itself and, at a step's first fragment, that step's
 // column blocks) and before fragment t's wait: its lgkmcnt, since LDS reads
 // complete in order.
-template <int D, int FM, int FN, int cA, int cB, int kSteps>
+template <int D, int E, int FM, int FN, int cA, int cB, int kSteps>
 constexpr int reads_after(int t)
 {
     const bool need_b = t % FM == 0;
@@ -551,7 +557,7 @@ constexpr int reads_after(int t)
     for (int x = 0; x < D; x++)
         n = x == t ? 0 : n + cA;
     for (int s = 0; s < t; s++) {
-        if (s < FN)
+        if (b_at<E, FN>(s) >= 0)
             n = need_b && kk == 1 ? 0 : n + cB;
         if (s + D < kSteps)
             n = s + D == t ? 0 : n + cA;
@@ -608,9 +614,10 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
     constexpr int FM = RW / 16, FN = CW / 16;
     constexpr int NK = kBK / 64;                 // MFMA steps per stage
     constexpr int kSteps = NK * FM;              // row-block fragments per stage
-    constexpr int kAhead = 4;                    // row-block fragments read ahead
+    constexpr int kAhead = 3;                    // row-block fragments read ahead
     constexpr int kSpread = 4;                   // fragments the stage loads spread over
-    static_assert(NK == 2 && kSteps % 8 == 0 && kAhead <= 4 && FN <= kSteps - kAhead,
+    constexpr int kBEvery = 1;                   // fragments between step 1's column blocks
+    static_assert(NK == 2 && kSteps % 8 == 0 && kAhead <= 4 && FN * kBEvery <= FM,
                   "fragment schedule shape");
     using OpA = Operand<BM, AKM, NT, kBK>;
     using OpB = Operand<BN, BKM, NT, kBK>;
@@ -688,12 +695,12 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
     };
 
     // Per stage: fragment t's MFMAs follow its wait; before them the reads of
-    // its share of step 1's column blocks and of fragment t + kAhead are
-    // issued.  After fragment kSteps - kAhead - 1 every read of the stage is
-    // waited for, the stage barrier passes, the next stage's head reads are
-    // issued and the last kAhead fragments' MFMAs cover their latency.  The
-    // next stage's buffer-to-LDS loads are issued among the MFMAs of the
-    // first kSpread fragments.
+    // one of step 1's column blocks (every kBEvery fragments) and of fragment
+    // t + kAhead are issued.  After fragment kSteps - kAhead - 1 every read
+    // of the stage is waited for, the stage barrier passes, the next stage's
+    // head reads are issued and the last kAhead fragments' MFMAs cover their
+    // latency.  The next stage's buffer-to-LDS loads are issued among the
+    // MFMAs of the first kSpread fragments.
     static_for<kSpread>([&](auto G) { issue(0, G); });
     wait_vmcnt<0>();
     barrier_no_fence();
@@ -702,15 +709,15 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
         const uint32_t sb = lds0 + (kt & 1) * kStage;
         static_for<kSteps - kAhead>([&](auto T) {
             constexpr int t = decltype(T)::value;
-            wait_lgkmcnt<reads_after<kAhead, FM, FN, cA, cB, kSteps>(t)>();
+            wait_lgkmcnt<reads_after<kAhead, kBEvery, FM, FN, cA, cB, kSteps>(t)>();
             OpA::settle(fa[t % 8]);
             if constexpr (t % FM == 0) {
 #pragma unroll
                 for (int b = 0; b < FN; b++)
                     OpB::settle(fb[t / FM][b]);
             }
-            if constexpr (t < FN)
-                read_b(sb, One{}, T);
+            if constexpr (b_at<kBEvery, FN>(t) >= 0)
+                read_b(sb, One{}, std::integral_constant<int, b_at<kBEvery, FN>(t)>{});
             read_a(sb, std::integral_constant<int, t + kAhead>{});
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (t < kSpread) {
