@@ -422,9 +422,17 @@ __device__ __forceinline__ void store_pass(const GemmParams &p, const lds_i8 *st
                                            const lds_i8 *partner = nullptr, bool upper = false)
 {
     constexpr int kChunks = CW / 4;
+    constexpr int kRowsPer = kWave / kChunks;      // rows per store instruction
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
     const int lane = __lane_id();
+    // Store k writes row k kRowsPer + r0, 16-byte chunk 'chunk' (the same for
+    // every k): one column test, and the row address advances by a constant.
+    const int r0 = lane / kChunks, chunk = lane % kChunks;
+    const bool col_ok = j + chunk * 4 < p.S;
+    uint32_t *dst = static_cast<uint32_t *>(p.out) + (int64_t)(i + r0) * p.ldc + j + chunk * 4;
+    const int64_t step = (int64_t)kRowsPer * p.ldc;
+    const float sign = upper ? -1.0f : 1.0f;
     wait_lgkmcnt0();
 #pragma unroll
     for (int k0 = 0; k0 < 16; k0 += 8) {
@@ -434,8 +442,7 @@ __device__ __forceinline__ void store_pass(const GemmParams &p, const lds_i8 *st
         u32x4 t[8], o[8];
 #pragma unroll
         for (int k = 0; k < 8; k++) {
-            const int s16 = (k0 + k) * kWave + lane;     // 16-byte slot of the pass
-            const int at = 4 * stage_slot<CW>(s16 / kChunks, s16 % kChunks);
+            const int at = 4 * stage_slot<CW>((k0 + k) * kRowsPer + r0, chunk);
             t[k] = *reinterpret_cast<lds_u32x4 *>(stage + at);
             if constexpr (PAIR)
                 o[k] = *reinterpret_cast<lds_u32x4 *>(partner + at);
@@ -448,22 +455,18 @@ __device__ __forceinline__ void store_pass(const GemmParams &p, const lds_i8 *st
         }
 #pragma unroll
         for (int k = 0; k < 8; k++) {
-            const int s16 = (k0 + k) * kWave + lane;
-            const int row = s16 / kChunks, chunk = s16 % kChunks;
             if constexpr (PAIR) {
-                const float sign = upper ? -1.0f : 1.0f;
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    // lo + hi (lower wave) or lo - hi (upper wave), rounded
-                    // once.
+                    // own + partner (lower wave) or partner - own (upper),
+                    // rounded once: sign * own is exact.
                     const float v = __uint_as_float(t[k][e]), x = __uint_as_float(o[k][e]);
-                    const float lo = upper ? x : v, hi = upper ? v : x;
-                    t[k][e] = __float_as_uint(__builtin_fmaf(sign, hi, lo) * p.had_scale);
+                    t[k][e] = __float_as_uint(__builtin_fmaf(sign, v, x) * p.had_scale);
                 }
             }
-            if (i + row < p.R && j + chunk * 4 < p.S)
-                *reinterpret_cast<u32x4 *>(static_cast<uint32_t *>(p.out) +
-                                           (int64_t)(i + row) * p.ldc + j + chunk * 4) = t[k];
+            if (col_ok && i + (k0 + k) * kRowsPer + r0 < p.R)
+                *reinterpret_cast<u32x4 *>(dst) = t[k];
+            dst += step;
         }
     }
     wait_lgkmcnt0();
