@@ -317,6 +317,60 @@ def test_skinny_forward(T, Q, orc, M):
     assert_bitwise(host(y2), orc.fwd(qx, sx, qw, sw, bias), "y+bias")
 
 
+def _random_product_cases(n=10, seed=20261203):
+    """Seeded random shapes: any token count, feature counts multiples of 16,
+    contractions long enough (>= 8 stages of 128) for some tiles to be split
+    along the contraction, and a rotation block that divides K."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        M = int(rng.integers(1, 1500))
+        N = 16 * int(rng.integers(1, 100))
+        K = 16 * int(rng.integers(1, 100))
+        if i % 3 == 1:
+            K = 128 * (K // 128 + 1)            # the widest fused rotation
+            had = 128
+        elif i % 3 == 2:
+            hads = [h for h in (64, 32, 16, 8, 4, 2) if K % h == 0]
+            had = hads[int(rng.integers(0, len(hads)))]
+        else:
+            had = 0
+        cases.append((i, M, N, K, had, bool(rng.integers(0, 2))))
+    return cases
+
+
+@pytest.mark.parametrize("i,M,N,K,had,with_bias", _random_product_cases())
+def test_products_random_shapes(T, Q, orc, i, M, N, K, had, with_bias):
+    """The three products through qlin_product_ws (tiles split along the
+    contraction where the shape allows) and the plain entry points, bit for
+    bit against the oracle, on seeded random shapes."""
+    rng = np.random.default_rng(1000 + i)
+    qx, qw, qg = _codes(rng, (M, K)), _codes(rng, (N, K)), _codes(rng, (M, N))
+    sx = rng.uniform(1e-3, 1e-1, M).astype(np.float32)
+    sw = rng.uniform(1e-4, 1e-2, N).astype(np.float32)
+    sg1 = rng.uniform(1e-6, 1e-4, M).astype(np.float32)
+    sg2 = rng.uniform(1e-6, 1e-4, N).astype(np.float32)
+    b = rng.standard_normal(N).astype(np.float32) if with_bias else None
+    y_ref = orc.fwd(qx, sx, qw, sw, b)
+    dx_ref = orc.bwd_dx(qg, sg1, qw)
+    if had:
+        dx_ref = orc.hadamard(dx_ref, had)
+    dw_ref = orc.bwd_dw(qg, sg2, qx)
+    announce("random products", i, M, N, K, had, with_bias)
+    y = Q.qlin_product_ws(Q.QLIN_OP_FWD, dev(qx), dev(sx), dev(qw), M, N, K, scol=dev(sw),
+                          bias=None if b is None else dev(b))
+    dx = Q.qlin_product_ws(Q.QLIN_OP_DX, dev(qg), dev(sg1), dev(qw), M, N, K, had_block=had)
+    dw = Q.qlin_product_ws(Q.QLIN_OP_DW, dev(qg), dev(sg2), dev(qx), M, N, K)
+    y2 = Q.qlin_fwd(dev(qx), dev(sx), dev(qw), dev(sw), None if b is None else dev(b))
+    dx2 = Q.qlin_bwd_dx(dev(qg), dev(sg1), dev(qw), had_block=had)
+    dw2 = Q.qlin_bwd_dw(dev(qg), dev(sg2), dev(qx))
+    T.cuda.synchronize()
+    for got, ref, what in ((y, y_ref, "y"), (dx, dx_ref, "dx"), (dw, dw_ref, "dw"),
+                           (y2, y_ref, "y plain"), (dx2, dx_ref, "dx plain"),
+                           (dw2, dw_ref, "dw plain")):
+        assert_bitwise(host(got), ref, what)
+
+
 @pytest.mark.parametrize("M,N,K,had", [(64, 128, 256, 128), (130, 272, 384, 128), (17, 48, 512, 64),
                                        (33, 64, 256, 2), (40, 32, 64, 16), (5, 16, 1024, 256),
                                        (3, 16, 512, 512), (257, 144, 5376, 128)])
