@@ -83,6 +83,10 @@ def lib():
         L.orc_dequantize_weight.argtypes = [vp, vp, i64, i64, i32, vp]
         L.orc_gemm_s64_at.argtypes = [i32, vp, vp, i64, i64, i64, vp, vp, i64, vp]
         L.orc_op_at_long.argtypes = [i32, vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, i64, vp]
+        L.orc_wn_init.argtypes = [vp, vp, i64, i64, vp, vp]
+        L.orc_wn_grads.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp]
+        L.orc_wn_sgd_requant.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, u64, u64, vp, vp,
+                                         vp]
         L.orc_adamw_constants.argtypes = [f32, f32, f32, f32, u64, vp]
         L.orc_adamw_constants.restype = None
         L.orc_adamw_update.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, f32, f32, f32, f32,
@@ -93,7 +97,8 @@ def lib():
                      "orc_gemm_s32", "orc_gemm_s32_at", "orc_fwd", "orc_bwd_dx",
                      "orc_bwd_dw", "orc_bwd_dw_rows", "orc_op_at", "orc_sgd_requant",
                      "orc_adamw_update", "orc_adamw_requant", "orc_dequantize_weight",
-                     "orc_gemm_s64_at", "orc_op_at_long"):
+                     "orc_gemm_s64_at", "orc_op_at_long", "orc_wn_init", "orc_wn_grads",
+                     "orc_wn_sgd_requant"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -361,6 +366,44 @@ def adamw_requant(qw, sw, dw, m, v, lr, beta1, beta2, eps, weight_decay, seed, s
                                  ctypes.c_uint64(seed), ctypes.c_uint64(step), _ptr(b),
                                  _ptr(_f32(db)), _ptr(bm), _ptr(bv), _ptr(ids)))
     return qw, sw, m, v, b, bm, bv
+
+
+def wn_init(q, s):
+    """Row weight normalization at preparation: (g, sw) from the direction
+    codes q [N, K] and row scales s [N]; rejects all-zero directions."""
+    q = np.ascontiguousarray(q, np.int8)
+    N, K = q.shape
+    g = np.empty(N, np.float32)
+    sw = np.empty(N, np.float32)
+    _chk(lib().orc_wn_init(_ptr(q), _ptr(_f32(s)), N, K, _ptr(g), _ptr(sw)))
+    return g, sw
+
+
+def wn_grads(q, s, g, dw):
+    """(dg [N], dv [N, K]): gradients of the magnitude and the direction."""
+    q = np.ascontiguousarray(q, np.int8)
+    N, K = q.shape
+    dg = np.empty(N, np.float32)
+    dv = np.empty((N, K), np.float32)
+    _chk(lib().orc_wn_grads(_ptr(q), _ptr(_f32(s)), _ptr(_f32(g)), _ptr(_f32(dw)), N, K,
+                            _ptr(dg), _ptr(dv)))
+    return dg, dv
+
+
+def wn_sgd_requant(q, s, g, dw, lr, seed, step, bias=None, db=None, row_ids=None):
+    """One SGD step of the weight-normalized row state; returns updated copies
+    (q, s, g, sw, bias)."""
+    q = np.array(q, np.int8, copy=True, order="C")
+    s = np.array(s, np.float32, copy=True)
+    g = np.array(g, np.float32, copy=True)
+    N, K = q.shape
+    sw = np.empty(N, np.float32)
+    b = None if bias is None else np.array(bias, np.float32, copy=True)
+    ids = None if row_ids is None else np.ascontiguousarray(row_ids, np.int64)
+    _chk(lib().orc_wn_sgd_requant(_ptr(q), _ptr(s), _ptr(g), _ptr(sw), _ptr(_f32(dw)), N, K,
+                                  ctypes.c_float(lr), ctypes.c_uint64(seed),
+                                  ctypes.c_uint64(step), _ptr(b), _ptr(_f32(db)), _ptr(ids)))
+    return q, s, g, sw, b
 
 
 def prepare_weight(w, had_block=0):

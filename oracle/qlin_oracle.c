@@ -40,6 +40,18 @@
  *      d = fl(fl(sqrt(v')*c2) + eps), w = fl(fl(fl(s*q)*decay) - fl(c1*fl(m'/d)))
  *    with a1 = 1-b1, a2 = 1-b2, c1 = lr/(1-b1^t), c2 = 1/sqrt(1-b2^t),
  *    decay = 1-lr*wd, then the same row requant as SGD with Philox step t.
+ *  - Row weight normalization (the guide's feature table: an INT8 direction
+ *    and a floating magnitude per output row): W[n, :] = g[n] v[n, :] /
+ *    ||v[n, :]|| with the direction v = s q held as INT8 codes q and a row
+ *    scale s, and g trained as its own parameter.  ||q|| = fl32(sqrt(sum q^2))
+ *    with the integer sum exact and the square root in double.  The products'
+ *    column scale is fl(g / ||q||).  Backward from dW (the gradient of the
+ *    represented weight): dot = fl32 of the pairwise (zero-padded to a power
+ *    of two, adjacent pairs first) double sum of dW_k q_k; dg = fl(dot /
+ *    ||q||); dv_k = fl(fl(g / fl(s ||q||)) * fl(dW_k - fl(fl(dg / ||q||) *
+ *    q_k))).  SGD: g' = fl(g - fl(lr dg)), w_k = fl(fl(s q_k) - fl(lr dv_k)),
+ *    then the row requant of SGD.  At preparation g = fl(s ||q||), so the
+ *    represented weight starts as the absmax one.
  *  - fp32 arithmetic: IEEE binary32, round to nearest even, no FMA
  *    contraction (built with -ffp-contract=off), IEEE division.
  *
@@ -574,6 +586,134 @@ int orc_sgd_requant(int8_t *qw, float *sw, const float *dw, int64_t N, int64_t K
             }
             sw[n] = requant_row(w, K, row_ids ? row_ids[n] : n, seed, step, qw + n * K);
         }
+        free(w);
+    }
+    if (bias && db)
+        for (int64_t n = 0; n < N; n++)
+            bias[n] = bias[n] - lr * db[n];
+    return ORC_OK;
+}
+
+/* ------------------------------------------ row weight normalization */
+
+/* ||q|| of one row of codes: the exact integer sum of squares, square root
+ * in double, rounded once to fp32. */
+static float code_norm(const int8_t *q, int64_t K)
+{
+    int64_t n2 = 0;
+    for (int64_t k = 0; k < K; k++)
+        n2 += (int64_t)q[k] * q[k];
+    return (float)sqrt((double)n2);
+}
+
+/* Pairwise sum of x[lo .. lo + len) (len a power of two) where positions at
+ * or past n read as zero: the two halves are summed first, then added. */
+static double pairwise(const double *x, int64_t n, int64_t lo, int64_t len)
+{
+    if (len == 1)
+        return lo < n ? x[lo] : 0.0;
+    return pairwise(x, n, lo, len / 2) + pairwise(x, n, lo + len / 2, len / 2);
+}
+
+/* Gradients of one row for the magnitude (dg) and the direction (dv [K]),
+ * from dW [K] (the gradient of the represented weight g v / ||v||, v = s q):
+ *   dL/dg = <dW, v> / ||v|| = <dW, q> / ||q||,
+ *   dL/dv = (g / ||v||) (dW - (dL/dg) v / ||v||)
+ *         = (g / (s ||q||)) (dW - (dL/dg / ||q||) q).
+ * A row whose codes are all zero has no direction: both gradients are zero. */
+static void wn_row_grads(const int8_t *q, float s, float g, const float *dw, int64_t K,
+                         double *tmp, float *dg, float *dv)
+{
+    const float nrm = code_norm(q, K);
+    if (nrm == 0.0f) {
+        *dg = 0.0f;
+        for (int64_t k = 0; k < K; k++)
+            dv[k] = 0.0f;
+        return;
+    }
+    for (int64_t k = 0; k < K; k++)
+        tmp[k] = (double)dw[k] * (double)q[k];     /* exact */
+    int64_t len = 1;
+    while (len < K)
+        len *= 2;
+    const float dot = (float)pairwise(tmp, K, 0, len);
+    const float d = dot / nrm;
+    const float a = g / (s * nrm);
+    const float b = d / nrm;
+    for (int64_t k = 0; k < K; k++)
+        dv[k] = a * (dw[k] - b * (float)q[k]);
+    *dg = d;
+}
+
+/* Magnitude and column scale of a weight-normalized layer at preparation,
+ * from its direction codes and row scales: g = fl(s ||q||), sw = fl(g /
+ * ||q||).  An all-zero direction is rejected (mini_trainer guide: initial zero
+ * directions are rejected). */
+int orc_wn_init(const int8_t *q, const float *s, int64_t N, int64_t K, float *g, float *sw)
+{
+    if (N < 0 || K < 1)
+        return ORC_EINVAL;
+    for (int64_t n = 0; n < N; n++)
+        if (code_norm(q + n * K, K) == 0.0f)
+            return ORC_EINVAL;
+    for (int64_t n = 0; n < N; n++) {
+        const float nrm = code_norm(q + n * K, K);
+        g[n] = s[n] * nrm;
+        sw[n] = g[n] / nrm;
+    }
+    return ORC_OK;
+}
+
+/* The float gradients of every row (dg [N], dv [N, K]), without an update. */
+int orc_wn_grads(const int8_t *q, const float *s, const float *g, const float *dw, int64_t N,
+                 int64_t K, float *dg, float *dv)
+{
+    if (N < 0 || K < 1)
+        return ORC_EINVAL;
+#pragma omp parallel
+    {
+        double *tmp = (double *)malloc((size_t)K * sizeof(double));
+#pragma omp for schedule(static)
+        for (int64_t n = 0; n < N; n++)
+            wn_row_grads(q + n * K, s[n], g[n], dw + n * K, K, tmp, dg + n, dv + n * K);
+        free(tmp);
+    }
+    return ORC_OK;
+}
+
+/* One SGD step of a weight-normalized layer, in place on q [N, K], s, g and
+ * sw [N]: g' = fl(g - fl(lr dg)); the direction w = fl(fl(s q) - fl(lr dv))
+ * is requantized exactly as in SGD (new absmax scale, Philox stochastic
+ * rounding keyed by the element index); sw' = fl(g' / ||q'||), or 0 when the
+ * new codes are all zero.  bias -= lr * db when both are given. */
+int orc_wn_sgd_requant(int8_t *q, float *s, float *g, float *sw, const float *dw, int64_t N,
+                       int64_t K, float lr, uint64_t seed, uint64_t step, float *bias,
+                       const float *db, const int64_t *row_ids)
+{
+    if (N < 0 || K < 1)
+        return ORC_EINVAL;
+#pragma omp parallel
+    {
+        double *tmp = (double *)malloc((size_t)K * sizeof(double));
+        float *dv = (float *)malloc((size_t)K * sizeof(float));
+        float *w = (float *)malloc((size_t)K * sizeof(float));
+#pragma omp for schedule(static)
+        for (int64_t n = 0; n < N; n++) {
+            int8_t *qn = q + n * K;
+            float dg;
+            wn_row_grads(qn, s[n], g[n], dw + n * K, K, tmp, &dg, dv);
+            for (int64_t k = 0; k < K; k++) {
+                float cur = s[n] * (float)qn[k];
+                float upd = lr * dv[k];
+                w[k] = cur - upd;
+            }
+            g[n] = g[n] - lr * dg;
+            s[n] = requant_row(w, K, row_ids ? row_ids[n] : n, seed, step, qn);
+            const float nrm = code_norm(qn, K);
+            sw[n] = nrm == 0.0f ? 0.0f : g[n] / nrm;
+        }
+        free(tmp);
+        free(dv);
         free(w);
     }
     if (bias && db)
