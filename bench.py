@@ -43,6 +43,8 @@ ALG_BYTES = {
     "sgd_requant": N * K * (1 + 4 + 1) + 8 * N,
     # AdamW: codes in and out, gradient in, both fp32 moments in and out.
     "adamw_requant": N * K * (1 + 4 + 8 + 8 + 1) + 8 * N,
+    # Weight-normalized SGD: codes in and out, gradient in.
+    "wn_sgd_requant": N * K * (1 + 4 + 1) + 16 * N,
 }
 GEMMS = ("fwd", "bwd_dx", "bwd_dw")
 COPY_BYTES = 512 << 20        # calibration copy: reads and writes this many bytes
@@ -324,11 +326,33 @@ def main():
     out["extras"] = {"adamw_requant": {"ms": round(a_ms, 4), "gbs": round(a_gbs, 1),
                                        "frac_hbm": round(a_gbs / PEAK_HBM_GBS, 4),
                                        "shape": [N, K]}}
+    out["extras"].update(wn_update(torch, layer))
     out["extras"].update(skinny_forward(torch))
     if args.cpu_tokens > 0:
         print(f"[bench] cpu baseline on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(d, args.cpu_tokens)
     print(json.dumps(out), flush=True)
+
+
+def wn_update(torch, layer):
+    """The weight-normalized SGD step (trained magnitude, INT8 direction) on
+    a copy of the headline weight's state, timed over ten calls."""
+    from w8a8_integer_linear_amd import _native as nat
+    q, s = layer.qw.clone(), layer.sw.clone()
+    g, sw = nat.qlin_wn_init(q, s)
+    nat.qlin_wn_sgd_requant(q, s, g, sw, layer.dw, LR, SEED, 1)
+    torch.cuda.synchronize()
+    b = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    b.record()
+    for t in range(2, 12):
+        nat.qlin_wn_sgd_requant(q, s, g, sw, layer.dw, LR, SEED, t)
+    e.record()
+    torch.cuda.synchronize()
+    ms = b.elapsed_time(e) / 10
+    gbs = ALG_BYTES["wn_sgd_requant"] / (ms * 1e-3) / 1e9
+    return {"wn_sgd_requant": {"ms": round(ms, 4), "gbs": round(gbs, 1),
+                               "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "shape": [N, K]}}
 
 
 if __name__ == "__main__":

@@ -269,6 +269,49 @@ int qlin_sgd_requant(int8_t *qw, float *sw, const float *dw, int64_t N, int64_t 
                      void *stream);
 
 /*
+ * Row weight normalization (mini_trainer guide, feature table: an INT8
+ * direction and a floating magnitude per output row; initial zero directions
+ * are rejected).  A weight-normalized layer keeps per output row n the
+ * direction codes q[n, :] with their scale s[n] (the direction v = s q, the
+ * same storage as the absmax weight) and a magnitude g[n] trained as its own
+ * parameter.  The represented weight is g q / ||q||, so the products take
+ * qw = q with the column scale sw = fl(g / ||q||).  ||q|| = fl32(sqrt(sum
+ * q^2)): the integer sum exact, the square root in double, rounded once.
+ *
+ * qlin_wn_init: g = fl(s ||q||) and sw = fl(g / ||q||), so the represented
+ * weight starts as the absmax weight s q (within the rounding of sw).  An
+ * all-zero row gives g = sw = 0: callers reject it (a zero direction).
+ *   q [N, K] int8, s [N] fp32 inputs; g, sw [N] fp32 outputs.
+ *   N >= 0; K in [16, QLIN_WN_MAX_ROW], a multiple of 16.
+ */
+#define QLIN_WN_MAX_ROW 32768
+int qlin_wn_init(const int8_t *q, const float *s, int64_t N, int64_t K, float *g, float *sw,
+                 void *stream);
+
+/*
+ * SGD step of a weight-normalized layer, in place, with dw the gradient of
+ * the represented weight (the dW product's output).  Per row:
+ *   dot = fl32(pairwise double sum of dw_k q_k)   (the products are exact;
+ *         pairwise: the row zero-padded to a power of two, adjacent pairs
+ *         added level by level)
+ *   dg  = fl(dot / ||q||)                          (dL/dg)
+ *   dv_k = fl(fl(g / fl(s ||q||)) * fl(dw_k - fl(fl(dg / ||q||) * q_k)))
+ *                                                  (dL/dv, v = s q)
+ *   w_k = fl(fl(s q_k) - fl(lr dv_k)), requantized exactly as by
+ *         qlin_sgd_requant (new absmax scale s', Philox stochastic rounding
+ *         keyed by seed, step and the element index)
+ *   g'  = fl(g - fl(lr dg)),  sw' = fl(g' / ||q'||) (0 for all-zero codes).
+ * A row whose codes are all zero has zero gradients.
+ *   q [N, K] int8, s, g, sw [N] fp32: read and overwritten (sw is only
+ *   written).  dw [N, K] fp32.  bias, db [N] (both or neither): bias =
+ *   fl(bias - fl(lr db)).
+ *   N >= 0; K in [16, QLIN_WN_MAX_ROW], a multiple of 16; lr finite.
+ */
+int qlin_wn_sgd_requant(int8_t *q, float *s, float *g, float *sw, const float *dw, int64_t N,
+                        int64_t K, float lr, uint64_t seed, uint64_t step, float *bias,
+                        const float *db, void *stream);
+
+/*
  * AdamW step on the represented weight followed by the same stochastic
  * requantization of each row (mini_trainer guide, feature table: AdamW is
  * among the update paths covered on INT8 weights; update paragraph: updates

@@ -99,6 +99,22 @@ def test_product_validation(L):
     assert L.qlin_gemm_s32(0, ODD, Q, 4, 16, 16, R, None) == 1        # misaligned
 
 
+def test_weight_norm_validation(L):
+    _cpu_only()
+    T = 0x50000
+    assert L.qlin_wn_init(P, Q, 4, 24, R, S, None) == 1              # K % 16
+    assert L.qlin_wn_init(P, Q, 4, 16, R, R, None) == 1              # g aliases sw
+    assert L.qlin_wn_init(P, None, 4, 16, R, S, None) == 1           # no row scales
+    assert L.qlin_wn_init(P, Q, 4, 32784, R, S, None) == 2           # row too long
+    assert L.qlin_wn_init(P, Q, 0, 16, R, S, None) == 0
+    assert L.qlin_wn_sgd_requant(P, Q, R, S, T, 4, 16, 1e-3, 0, 0, Q, None, None) == 1  # bias w/o db
+    assert L.qlin_wn_sgd_requant(P, Q, R, S, T, 4, 16, float("inf"), 0, 0, None, None, None) == 1
+    assert L.qlin_wn_sgd_requant(P, Q, Q, S, T, 4, 16, 1e-3, 0, 0, None, None, None) == 1  # s = g
+    assert L.qlin_wn_sgd_requant(ODD, Q, R, S, T, 4, 16, 1e-3, 0, 0, None, None, None) == 1
+    assert L.qlin_wn_sgd_requant(P, Q, R, S, T, 4, 32784, 1e-3, 0, 0, None, None, None) == 2
+    assert L.qlin_wn_sgd_requant(P, Q, R, S, T, 0, 16, 1e-3, 0, 0, None, None, None) == 0
+
+
 def test_sgd_and_hadamard_validation(L):
     _cpu_only()
     assert L.qlin_sgd_requant(P, Q, R, 4, 16, 1e-3, 0, 0, S, None, None) == 1    # bias w/o db

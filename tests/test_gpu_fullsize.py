@@ -253,3 +253,59 @@ def test_split_products_equal_plain_at_full_size(orc):
     T.cuda.synchronize()
     for name, (a, b) in zip(("y", "dx", "dw"), pairs):
         assert torch.equal(a, b), name
+
+
+def test_weight_norm_step_at_full_size(orc):
+    """Weight-normalized 5376 -> 7168 weight: preparation and two SGD steps on
+    the whole weight; sampled rows against the oracle (rows key their own
+    random streams)."""
+    from w8a8_integer_linear_amd import _native as Q
+    T = torch_cuda()
+    N, K = 7168, 5376
+    rng = np.random.default_rng(21)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    announce("wn full size", N, K)
+    qd, sd = Q.qlin_quantize_rows(dev(w), had_block=128)
+    gd, swd = Q.qlin_wn_init(qd, sd)
+    rows = np.sort(rng.choice(N, 6, replace=False))
+    q, s = host(qd)[rows], host(sd)[rows]
+    g, sw = orc.wn_init(q, s)
+    T.cuda.synchronize()
+    assert_bitwise(host(gd)[rows], g, "g")
+    assert_bitwise(host(swd)[rows], sw, "sw")
+    for step in (1, 2):
+        dw = (rng.standard_normal((N, K)) * 1e-3).astype(np.float32)
+        Q.qlin_wn_sgd_requant(qd, sd, gd, swd, dev(dw), 0.05, seed=5, step=step)
+        T.cuda.synchronize()
+        q, s, g, sw, _ = orc.wn_sgd_requant(q, s, g, dw[rows], 0.05, 5, step, row_ids=rows)
+        for got, ref, what in ((qd, q, "q"), (sd, s, "s"), (gd, g, "g"), (swd, sw, "sw")):
+            assert_bitwise(host(got)[rows], ref, f"{what} after step {step}")
+
+
+def test_weight_norm_layer_step(orc):
+    """A layer built with weight_norm=True (tiny workload, no bias): forward,
+    backward and the weight-normalized SGD step, every tensor bit for bit
+    against the oracle's chain."""
+    from w8a8_integer_linear_amd import LinearW8A8Training
+    T = torch_cuda()
+    d = workloads.tiny()
+    M, K, N = 64, 256, 128
+    announce("wn layer step")
+    layer = LinearW8A8Training(dev(d["w"]), had_block=0, max_tokens=M, weight_norm=True)
+    y = layer.forward(dev(d["x"]))
+    dx = layer.backward(dev(d["dy"]))
+    layer.sgd_step(0.05, 3, 1)
+    T.cuda.synchronize()
+    q, s = orc.quantize_rows(d["w"])
+    g, sw = orc.wn_init(q, s)
+    qx, sx = orc.quantize_rows(d["x"])
+    assert_bitwise(host(y), orc.fwd(qx, sx, q, sw), "y")
+    qg1, sg1 = orc.quantize_rows(d["dy"], prescale=sw)
+    assert_bitwise(host(dx), orc.bwd_dx(qg1, sg1, q), "dx")
+    qg2, sg2 = orc.quantize_cols(d["dy"], prescale=sx)[:2]
+    dw = orc.bwd_dw(qg2, sg2, qx)
+    assert_bitwise(host(layer.dw), dw, "dw")
+    q1, s1, g1, sw1, _ = orc.wn_sgd_requant(q, s, g, dw, 0.05, 3, 1)
+    for got, ref, what in ((layer.qw, q1, "q"), (layer.s, s1, "s"), (layer.g, g1, "g"),
+                           (layer.sw, sw1, "sw")):
+        assert_bitwise(host(got), ref, what)

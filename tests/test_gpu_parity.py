@@ -542,6 +542,44 @@ def test_sgd_requant(T, Q, orc, N, K, with_bias):
             assert_bitwise(host(bd), br, "bias")
 
 
+WN_CASES = [(4, 16, False), (33, 272, True), (16, 2064, False), (64, 5376, True),
+            (8, 14336, False), (4, 20480, True), (2, 32768, False)]
+
+
+@pytest.mark.parametrize("N,K,with_bias", WN_CASES)
+def test_weight_norm_steps(T, Q, orc, N, K, with_bias):
+    """Weight-normalized layer: preparation, then three chained SGD steps
+    (each step's oracle inputs are the oracle's own previous outputs); one row
+    has all-zero codes (no direction: zero gradients).  Bit for bit."""
+    rng = np.random.default_rng(N * K + 5)
+    q = _codes(rng, (N, K))
+    q[:, 0] = 127
+    s = rng.uniform(1e-3, 1e-2, N).astype(np.float32)
+    announce("wn_init", N, K)
+    gd, swd = Q.qlin_wn_init(dev(q), dev(s))
+    T.cuda.synchronize()
+    g, sw = orc.wn_init(q, s)
+    assert_bitwise(host(gd), g, "g")
+    assert_bitwise(host(swd), sw, "sw")
+    q[N // 2] = 0                       # a row without a direction from here on
+    s[N // 2] = 0.0
+    g[N // 2] = np.float32(1.5)
+    bias = rng.standard_normal(N).astype(np.float32) if with_bias else None
+    d = {k: (None if a is None else dev(a)) for k, a in
+         dict(q=q, s=s, g=g, sw=sw, bias=bias).items()}
+    for step, lr in ((1, 1e-2), (2, 0.3), (3, 0.0)):
+        dw = (rng.standard_normal((N, K)) * 10.0 ** rng.uniform(-4, -1)).astype(np.float32)
+        db = rng.standard_normal(N).astype(np.float32) if with_bias else None
+        announce("wn_sgd_requant", N, K, step, lr)
+        Q.qlin_wn_sgd_requant(d["q"], d["s"], d["g"], d["sw"], dev(dw), lr, seed=77, step=step,
+                              bias=d["bias"], db=None if db is None else dev(db))
+        T.cuda.synchronize()
+        q, s, g, sw, bias = orc.wn_sgd_requant(q, s, g, dw, lr, 77, step, bias=bias, db=db)
+        for key, ref in (("q", q), ("s", s), ("g", g), ("sw", sw), ("bias", bias)):
+            if ref is not None:
+                assert_bitwise(host(d[key]), ref, f"{key} after step {step}")
+
+
 ADAMW_CASES = [(128, 256, True), (64, 5376, False), (7, 16, True), (3, 20480, False),
                (5, 14336, True)]
 

@@ -7,5 +7,6 @@ from ._native import (  # noqa: F401
     MAX_CONTRACTION, QLIN_BF16, QLIN_F32, QLIN_OP_DW, QLIN_OP_DX, QLIN_OP_FWD, QlinError,
     SIGNATURES, lib, qlin_adamw_requant, qlin_bwd_dw, qlin_bwd_dx, qlin_dequantize_weight,
     qlin_fwd, qlin_gemm_s32, qlin_hadamard, qlin_product_ws, qlin_product_ws_bytes,
-    qlin_quantize_cols, qlin_quantize_grad, qlin_quantize_rows, qlin_sgd_requant)
+    qlin_quantize_cols, qlin_quantize_grad, qlin_quantize_rows, qlin_sgd_requant, qlin_wn_init,
+    qlin_wn_sgd_requant)
 from .layer import LinearW8A8Training  # noqa: F401

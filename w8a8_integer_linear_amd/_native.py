@@ -34,6 +34,9 @@ SIGNATURES = {
     "qlin_bwd_dx": ([_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp], _i32),
     "qlin_bwd_dw": ([_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp], _i32),
     "qlin_sgd_requant": ([_vp, _vp, _vp, _i64, _i64, _f32, _u64, _u64, _vp, _vp, _vp], _i32),
+    "qlin_wn_init": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp], _i32),
+    "qlin_wn_sgd_requant": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _u64, _u64, _vp, _vp,
+                             _vp], _i32),
     "qlin_adamw_requant": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _f32, _f32, _f32, _f32,
                             _u64, _u64, _vp, _vp, _vp, _vp, _vp], _i32),
     "qlin_gemm_s32": ([_i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp], _i32),
@@ -244,6 +247,34 @@ def qlin_sgd_requant(qw, sw, dw, lr, seed, step, bias=None, db=None, stream=None
         _ptr(qw), _ptr(sw), _ptr(dw), N, K, float(lr), int(seed), int(step), _ptr(bias),
         _ptr(db), _stream(stream)))
     return qw, sw
+
+
+def qlin_wn_init(q, s, g=None, sw=None, stream=None):
+    """Magnitudes g and column scales sw of a weight-normalized layer from its
+    direction codes q and row scales s.  Returns (g, sw)."""
+    N, K = q.shape
+    _need(q, "q", torch.int8)
+    _need(s, "s", torch.float32, (N,))
+    g = _empty((N,), torch.float32, q) if g is None else _need(g, "g", torch.float32, (N,))
+    sw = _empty((N,), torch.float32, q) if sw is None else _need(sw, "sw", torch.float32, (N,))
+    _check("qlin_wn_init", lib().qlin_wn_init(_ptr(q), _ptr(s), N, K, _ptr(g), _ptr(sw),
+                                              _stream(stream)))
+    return g, sw
+
+
+def qlin_wn_sgd_requant(q, s, g, sw, dw, lr, seed, step, bias=None, db=None, stream=None):
+    """In place on q, s, g, sw (and bias)."""
+    N, K = q.shape
+    _need(q, "q", torch.int8)
+    for t, name in ((s, "s"), (g, "g"), (sw, "sw")):
+        _need(t, name, torch.float32, (N,))
+    _need(dw, "dw", torch.float32, (N, K))
+    _opt(bias, "bias", torch.float32, (N,))
+    _opt(db, "db", torch.float32, (N,))
+    _check("qlin_wn_sgd_requant", lib().qlin_wn_sgd_requant(
+        _ptr(q), _ptr(s), _ptr(g), _ptr(sw), _ptr(dw), N, K, float(lr), int(seed), int(step),
+        _ptr(bias), _ptr(db), _stream(stream)))
+    return q, s, g, sw
 
 
 def qlin_adamw_requant(qw, sw, dw, m, v, lr, beta1, beta2, eps, weight_decay, seed, step,

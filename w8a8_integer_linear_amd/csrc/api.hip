@@ -356,6 +356,50 @@ int qlin_sgd_requant(int8_t *qw, float *sw, const float *dw, int64_t N, int64_t 
     return finish();
 }
 
+int qlin_wn_init(const int8_t *q, const float *s, int64_t N, int64_t K, float *g, float *sw,
+                 void *stream)
+{
+    if (N < 0 || !dim16(K))
+        return QLIN_EINVAL;
+    const bool any = N > 0;
+    if (!array_ok(q, any) || (any && (!s || !g || !sw)))
+        return QLIN_EINVAL;
+    if (any && (overlap(g, N * 4, sw, N * 4) || overlap(g, N * 4, s, N * 4) ||
+                overlap(sw, N * 4, s, N * 4)))
+        return QLIN_EINVAL;
+    if (K > QLIN_WN_MAX_ROW || N > kMaxRows)
+        return QLIN_EUNSUPPORTED;
+    if (N == 0)
+        return QLIN_OK;
+    qlin::launch_wn_init(q, s, N, K, g, sw, as_stream(stream));
+    return finish();
+}
+
+int qlin_wn_sgd_requant(int8_t *q, float *s, float *g, float *sw, const float *dw, int64_t N,
+                        int64_t K, float lr, uint64_t seed, uint64_t step, float *bias,
+                        const float *db, void *stream)
+{
+    if (N < 0 || !dim16(K))
+        return QLIN_EINVAL;
+    const bool any = N > 0;
+    if (!array_ok(q, any) || !array_ok(dw, any) || (any && (!s || !g || !sw)))
+        return QLIN_EINVAL;
+    if ((bias == nullptr) != (db == nullptr))
+        return QLIN_EINVAL;
+    if (!isfinite(lr))
+        return QLIN_EINVAL;
+    if (any && (overlap(g, N * 4, sw, N * 4) || overlap(g, N * 4, s, N * 4) ||
+                overlap(sw, N * 4, s, N * 4)))
+        return QLIN_EINVAL;
+    if (K > QLIN_WN_MAX_ROW || N > kMaxRows)
+        return QLIN_EUNSUPPORTED;
+    if (N == 0)
+        return QLIN_OK;
+    qlin::launch_wn_sgd_requant(q, s, g, sw, dw, N, K, lr, seed, step, bias, db,
+                                as_stream(stream));
+    return finish();
+}
+
 int qlin_adamw_requant(int8_t *qw, float *sw, const float *dw, float *m, float *v, int64_t N,
                        int64_t K, float lr, float beta1, float beta2, float eps,
                        float weight_decay, uint64_t seed, uint64_t step, float *bias,

@@ -76,6 +76,12 @@ struct AdamConsts {
     float b1, b2, eps, a1, a2, c1, c2, decay;
 };
 
+// Row weight normalization: preparation and the SGD step (sgd.hip).
+void launch_wn_init(const int8_t *q, const float *s, int64_t N, int64_t K, float *g, float *sw,
+                    hipStream_t st);
+void launch_wn_sgd_requant(int8_t *q, float *s, float *g, float *sw, const float *dw, int64_t N,
+                           int64_t K, float lr, uint64_t seed, uint64_t step, float *bias,
+                           const float *db, hipStream_t st);
 void launch_adamw_requant(int8_t *qw, float *sw, const float *dw, float *m, float *v, int64_t N,
                           int64_t K, const AdamConsts &k, uint64_t seed, uint64_t step,
                           float *bias, const float *db, float *bm, float *bv, hipStream_t st);

@@ -27,8 +27,14 @@ from . import _native as nat
 
 
 class LinearW8A8Training:
-    def __init__(self, weight, bias=None, had_block=128, max_tokens=0):
-        """weight: [N, K] float GPU tensor in the original basis (rotated here)."""
+    def __init__(self, weight, bias=None, had_block=128, max_tokens=0, weight_norm=False):
+        """weight: [N, K] float GPU tensor in the original basis (rotated here).
+
+        weight_norm: row weight normalization (the guide's INT8 direction with a
+        floating magnitude per output row, trained as its own parameter): the
+        represented weight is g q / ||q||, the direction s q (s in self.s),
+        and the products take the column scale sw = g / ||q||.  It starts as
+        the absmax weight.  Updates go through wn_sgd_step."""
         self.timer = None    # optional callable(label) invoked after each call
         N, K = weight.shape
         self.N, self.K, self.had = N, K, int(had_block)
@@ -37,6 +43,10 @@ class LinearW8A8Training:
         self.qw, self.sw = nat.qlin_quantize_rows(w, had_block=self.had)
         if bool((self.sw == 0).any()):
             raise ValueError("weight has an all-zero row (zero direction)")
+        self.weight_norm = bool(weight_norm)
+        if self.weight_norm:
+            self.s = self.sw
+            self.g, self.sw = nat.qlin_wn_init(self.qw, self.s)
         self.bias = None if bias is None else bias.to(torch.float32).contiguous().clone()
         self.max_tokens = 0
         self.dw = torch.empty((N, K), dtype=torch.float32, device=dev)
@@ -100,12 +110,25 @@ class LinearW8A8Training:
         return dx
 
     def sgd_step(self, lr, seed, step):
+        if self.weight_norm:
+            return self.wn_sgd_step(lr, seed, step)
         nat.qlin_sgd_requant(self.qw, self.sw, self.dw, lr, seed, step, bias=self.bias, db=self.db)
         self._tick("sgd_requant")
+
+    def wn_sgd_step(self, lr, seed, step):
+        """SGD on the magnitude g and the direction s q of a weight-normalized
+        layer, with the direction's stochastic requant; refreshes sw."""
+        if not self.weight_norm:
+            raise ValueError("the layer was not built with weight_norm=True")
+        nat.qlin_wn_sgd_requant(self.qw, self.s, self.g, self.sw, self.dw, lr, seed, step,
+                                bias=self.bias, db=self.db)
+        self._tick("wn_sgd_requant")
 
     def adamw_step(self, lr, seed, step, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0):
         """AdamW update + stochastic requant (step >= 1).  The fp32 moments (and
         the bias moments) are allocated, zeroed, on the first call."""
+        if self.weight_norm:
+            raise ValueError("AdamW is built for the absmax weight only")
         if getattr(self, "_m", None) is None:
             self._m = torch.zeros_like(self.dw)
             self._v = torch.zeros_like(self.dw)
@@ -121,8 +144,9 @@ class LinearW8A8Training:
         self._tick("adamw_requant")
 
     def unquantized_weight(self):
-        """The represented weight fl(s_w * Q_w), rotated back to the original
-        basis (a new [N, K] fp32 tensor)."""
+        """The represented weight fl(s_w * Q_w) (with weight normalization
+        sw = g / ||q||), rotated back to the original basis (a new [N, K] fp32
+        tensor)."""
         return nat.qlin_dequantize_weight(self.qw, self.sw, had_block=self.had)
 
     def _tick(self, label):
