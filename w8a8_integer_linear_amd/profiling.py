@@ -15,7 +15,8 @@ Writes profiles/kernels_headline_step.txt (per-kernel durations),
        launch, scaled by the reading of the calibration copy of 512 MiB) and
        profiles/mfma_busy_clock.txt (per kernel: the shader clock it ran at,
        SQ busy cycles per shader engine over the dispatch's duration, and the
-       fraction of those cycles the SIMDs' matrix pipes were busy).
+       fraction of those cycles the SIMDs' matrix pipes were busy) and
+       profiles/lds_bank_conflicts.txt (from OUT_DIR/lds, if present).
 """
 import csv
 import glob
@@ -176,6 +177,34 @@ def main(out_dir, digest=None):
                 f.write(f"  {k[:70]:<70} {clk:>9.3f} {busy:>9.3f} {busy * clk / 2.4:>8.3f} "
                         f"{dur:>8.1f} {n:>3}\n")
         print(open(os.path.join(PROFILES, "mfma_busy_clock.txt")).read())
+    if glob.glob(os.path.join(out_dir, "lds", "*counter_collection.csv")):
+        lds_summary(out_dir)
+
+
+def lds_summary(out_dir):
+    """profiles/lds_bank_conflicts.txt: per kernel, LDS instructions and
+    bank-conflict cycles per dispatch (OUT/lds from the command below)."""
+    path = _one(os.path.join(out_dir, "lds", "*counter_collection.csv"))
+    vals = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            k = _short(r["Kernel_Name"])
+            vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+    with open(os.path.join(PROFILES, "lds_bank_conflicts.txt"), "w") as f:
+        f.write("# LDS activity per dispatch of the headline step's kernels.\n")
+        f.write("#   rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS SQ_WAVES "
+                "-d OUT/lds -o lds --output-format csv -- python bench.py --steps 2 --warmup 1 "
+                "--cpu-tokens 0\n")
+        f.write(f"# {'kernel':<70} {'lds_insts':>12} {'conflict_cyc':>12} {'waves':>7}\n")
+        for k, d in sorted(vals.items(), key=lambda kv: -statistics.mean(
+                kv[1].get("SQ_INSTS_LDS", [0]))):
+            m = {c: statistics.mean(v) for c, v in d.items()}
+            if m.get("SQ_INSTS_LDS", 0) == 0:
+                continue
+            f.write(f"  {k[:70]:<70} {m['SQ_INSTS_LDS']:>12.0f} "
+                    f"{m['SQ_LDS_BANK_CONFLICT']:>12.0f} {m['SQ_WAVES']:>7.0f}\n")
+    print(open(os.path.join(PROFILES, "lds_bank_conflicts.txt")).read())
 
 
 if __name__ == "__main__":
