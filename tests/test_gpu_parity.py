@@ -66,6 +66,34 @@ def test_quantize_rows(T, Q, orc, rows, cols, had, bf16, pre):
     assert_bitwise(host(q), qr, "codes")
 
 
+def _random_row_cases(n=12, seed=7101):
+    """Seeded random quantizer shapes: 1..3000 rows, 16..40960 columns (a
+    multiple of 16, of the block when rotating), any rotation block, fp32 or
+    bf16 input, with or without a prescale."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        rows = int(rng.integers(1, 3000)) if i % 4 else int(rng.integers(1, 40))
+        had = [0, 0, 2, 16, 32, 64, 128, 256, 512][int(rng.integers(0, 9))]
+        unit = max(16, had)
+        cols = unit * int(rng.integers(1, max(2, 40960 // unit // (8 if i % 4 else 1))))
+        cases.append((i, rows, cols, had, bool(rng.integers(0, 2)), bool(rng.integers(0, 2))))
+    return cases
+
+
+@pytest.mark.parametrize("i,rows,cols,had,bf16,pre", _random_row_cases())
+def test_quantize_rows_random(T, Q, orc, i, rows, cols, had, bf16, pre):
+    rng = np.random.default_rng(500 + i)
+    x = _x(rng, rows, cols, bf16, 10.0 ** rng.uniform(-3, 3))
+    p = rng.uniform(0.25, 4.0, cols).astype(np.float32) if pre else None
+    announce("quantize_rows random", i, rows, cols, had, bf16, pre)
+    q, s = Q.qlin_quantize_rows(dev(x), prescale=None if p is None else dev(p), had_block=had)
+    T.cuda.synchronize()
+    qr, sr = orc.quantize_rows(x, prescale=p, had_block=had)
+    assert_bitwise(host(s), sr, "scales")
+    assert_bitwise(host(q), qr, "codes")
+
+
 def test_quantize_rows_edge_values(T, Q, orc):
     """Zero rows, subnormal scales, huge values, exact ties."""
     rows, cols = 6, 64
@@ -280,6 +308,30 @@ def test_products_dequant(T, Q, orc, M, N, K, with_bias):
     dw = Q.qlin_bwd_dw(dev(qg), dev(sg2), dev(qx))
     T.cuda.synchronize()
     assert_bitwise(host(dw), orc.bwd_dw(qg, sg2, qx), "dw")
+
+
+def _random_skinny_cases(n=8, seed=7202):
+    """Seeded random shapes for the weight-streaming forward: 1..16 tokens,
+    up to 8192 output features (grids past one workgroup per compute unit take
+    the 1024-byte chunks), contractions of 16..12288."""
+    rng = np.random.default_rng(seed)
+    return [(i, int(rng.integers(1, 17)), 16 * int(rng.integers(1, 513)),
+             16 * int(rng.integers(1, 769)), bool(rng.integers(0, 2))) for i in range(n)]
+
+
+@pytest.mark.parametrize("i,M,N,K,with_bias", _random_skinny_cases())
+def test_skinny_forward_random(T, Q, orc, i, M, N, K, with_bias):
+    rng = np.random.default_rng(900 + i)
+    qx, qw = _codes(rng, (M, K)), _codes(rng, (N, K))
+    sx = rng.uniform(1e-3, 1e-1, M).astype(np.float32)
+    sw = rng.uniform(1e-4, 1e-2, N).astype(np.float32)
+    bias = rng.standard_normal(N).astype(np.float32) if with_bias else None
+    announce("skinny random", i, M, N, K, with_bias)
+    c = Q.qlin_gemm_s32(Q.QLIN_OP_FWD, dev(qx), dev(qw), M, N, K)
+    y = Q.qlin_fwd(dev(qx), dev(sx), dev(qw), dev(sw), None if bias is None else dev(bias))
+    T.cuda.synchronize()
+    assert_bitwise(host(c), orc.gemm_s32(0, qx, qw, M, N, K), "acc")
+    assert_bitwise(host(y), orc.fwd(qx, sx, qw, sw, bias), "y")
 
 
 @pytest.mark.parametrize("M,N,K", [(2, 48, 4112), (16, 32, 8192), (1, 16, 12352), (7, 64, 16)])
