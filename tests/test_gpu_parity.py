@@ -168,6 +168,38 @@ def test_quantize_grad(T, Q, orc, rows, cols, bf16):
     assert np.all(np.abs(host(db).astype(np.float64) - dbr) <= bound)
 
 
+def _random_grad_cases(n=8, seed=7303):
+    """Seeded random dY shapes for both quantizations: mostly the fused pass
+    (>= 512 rows, <= 8192 columns), some of the separate passes."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        rows = int(rng.integers(512, 5000)) if i % 4 else int(rng.integers(1, 512))
+        cols = 16 * int(rng.integers(1, 513 if i % 3 else 1024))
+        cases.append((i, rows, cols, bool(rng.integers(0, 2))))
+    return cases
+
+
+@pytest.mark.parametrize("i,rows,cols,bf16", _random_grad_cases())
+def test_quantize_grad_random(T, Q, orc, i, rows, cols, bf16):
+    rng = np.random.default_rng(1300 + i)
+    x = _x(rng, rows, cols, bf16, scale=10.0 ** rng.uniform(-4, 1))
+    sw = rng.uniform(1e-3, 1e-2, cols).astype(np.float32)
+    sx = rng.uniform(1e-3, 1e-1, rows).astype(np.float32)
+    announce("quantize_grad random", i, rows, cols, bf16)
+    q1, s1, q2, s2, db = Q.qlin_quantize_grad(dev(x), dev(sw), dev(sx), want_sum=True)
+    T.cuda.synchronize()
+    q1r, s1r = orc.quantize_rows(x, prescale=sw)
+    assert_bitwise(host(s1), s1r, "row scales")
+    assert_bitwise(host(q1), q1r, "row codes")
+    q2r, s2r, dbr = orc.quantize_cols(x, prescale=sx, want_sum=True)
+    assert_bitwise(host(s2), s2r, "column scales")
+    assert_bitwise(host(q2), q2r, "column codes")
+    xf = workloads.bf16_bits_to_f32(x) if bf16 else x
+    bound = 1e-5 * np.abs(xf.astype(np.float64)).sum(axis=0) + 1e-30
+    assert np.all(np.abs(host(db).astype(np.float64) - dbr) <= bound)
+
+
 def test_quantize_grad_no_tokens(T, Q, orc):
     cols = 64
     announce("quantize_grad rows=0")
@@ -630,6 +662,54 @@ def test_weight_norm_steps(T, Q, orc, N, K, with_bias):
         for key, ref in (("q", q), ("s", s), ("g", g), ("sw", sw), ("bias", bias)):
             if ref is not None:
                 assert_bitwise(host(d[key]), ref, f"{key} after step {step}")
+
+
+def _random_update_cases(n=8, seed=7404):
+    rng = np.random.default_rng(seed)
+    return [(i, int(rng.integers(1, 600)), 16 * int(rng.integers(1, 2048 if i % 2 else 256)),
+             bool(rng.integers(0, 2))) for i in range(n)]
+
+
+@pytest.mark.parametrize("i,N,K,with_bias", _random_update_cases())
+def test_updates_random(T, Q, orc, i, N, K, with_bias):
+    """SGD, AdamW and weight-normalized SGD on seeded random shapes, one step
+    each from the same state, bit for bit."""
+    rng = np.random.default_rng(1400 + i)
+    qw = _codes(rng, (N, K))
+    sw = rng.uniform(1e-4, 1e-2, N).astype(np.float32)
+    dw = (rng.standard_normal((N, K)) * 10.0 ** rng.uniform(-4, 0)).astype(np.float32)
+    bias = rng.standard_normal(N).astype(np.float32) if with_bias else None
+    db = rng.standard_normal(N).astype(np.float32) if with_bias else None
+    lr, seed, step = 0.05, 99 + i, 1 + i
+    announce("updates random", i, N, K, with_bias)
+    q, s, b = dev(qw), dev(sw), None if bias is None else dev(bias)
+    Q.qlin_sgd_requant(q, s, dev(dw), lr, seed, step, bias=b, db=None if db is None else dev(db))
+    T.cuda.synchronize()
+    qr, sr, br = orc.sgd_requant(qw, sw, dw, lr, seed, step, bias=bias, db=db)
+    assert_bitwise(host(q), qr, "sgd codes")
+    assert_bitwise(host(s), sr, "sgd scales")
+    if bias is not None:
+        assert_bitwise(host(b), br, "sgd bias")
+    q, s = dev(qw), dev(sw)
+    m, v = dev(np.zeros((N, K), np.float32)), dev(np.zeros((N, K), np.float32))
+    Q.qlin_adamw_requant(q, s, dev(dw), m, v, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
+                         weight_decay=0.01, seed=seed, step=step)
+    T.cuda.synchronize()
+    qa, sa, ma, va = orc.adamw_requant(qw, sw, dw, np.zeros((N, K), np.float32),
+                                       np.zeros((N, K), np.float32), 1e-3, 0.9, 0.999, 1e-8,
+                                       0.01, seed, step)[:4]
+    for got, ref, what in ((q, qa, "adamw codes"), (s, sa, "adamw scales"), (m, ma, "m"),
+                           (v, va, "v")):
+        assert_bitwise(host(got), ref, what)
+    qw[:, 0] = 127
+    g0, sw0 = orc.wn_init(qw, sw)
+    q, s, g, swd = dev(qw), dev(sw), dev(g0), dev(sw0)
+    Q.qlin_wn_sgd_requant(q, s, g, swd, dev(dw), lr, seed, step)
+    T.cuda.synchronize()
+    qn, sn, gn, swn, _ = orc.wn_sgd_requant(qw, sw, g0, dw, lr, seed, step)
+    for got, ref, what in ((q, qn, "wn codes"), (s, sn, "wn scales"), (g, gn, "wn g"),
+                           (swd, swn, "wn sw")):
+        assert_bitwise(host(got), ref, what)
 
 
 ADAMW_CASES = [(128, 256, True), (64, 5376, False), (7, 16, True), (3, 20480, False),
