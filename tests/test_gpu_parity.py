@@ -753,6 +753,42 @@ def test_adamw_requant(T, Q, orc, N, K, with_bias):
             assert_bitwise(host(d["bv"]), bv, f"bias v step {t}")
 
 
+def test_sgd_extreme_scales(T, Q, orc):
+    """Rows whose requant scale lies outside [2^-40, 2^40] and elements whose
+    quotient w / s' is below 2^-40 in magnitude (normal and subnormal w) take
+    the kernel's division path; the rest of each row its reciprocal path.
+    Both must give the oracle's codes."""
+    rng = np.random.default_rng(404)
+    N, K = 12, 1024
+    qw = _codes(rng, (N, K))
+    qw[:, 0] = 127
+    sw = np.full(N, 1e-3, np.float32)
+    sw[0], sw[1] = 1e-20, 2e-14           # scales below 2^-40
+    sw[2], sw[3] = 3e13, 1e18             # scales above 2^40
+    sw[4] = np.float32(2.0 ** -40)        # the bounds themselves
+    sw[5] = np.float32(2.0 ** 40)
+    dw = rng.standard_normal((N, K)).astype(np.float32)
+    dw[:6] *= sw[:6, None]
+    # rows 6-11: zero codes with tiny or zero gradients beside full-size ones
+    for r, mag in ((6, 1e-30), (7, 1e-36), (8, 1e-41), (9, 0.0)):
+        qw[r, 1::2] = 0
+        dw[r, 1::2] = mag * rng.choice([-1.0, 1.0], K // 2).astype(np.float32)
+    qw[10, 8:] = 0                         # whole chunks of tiny quotients
+    dw[10, 8:] = 1e-33
+    qw[11] = 0                             # one normal element, the rest subnormal w
+    qw[11, 0] = 127
+    dw[11, 1:] = rng.choice([-1.0, 1.0], K - 1).astype(np.float32) * np.float32(1e-36)
+    lr = 1e-3
+    for seed, step in ((0, 0), (5, 2 ** 31 + 3)):
+        announce("sgd_requant extreme scales", seed, step)
+        qd, sd = dev(qw), dev(sw)
+        Q.qlin_sgd_requant(qd, sd, dev(dw), lr, seed, step)
+        T.cuda.synchronize()
+        qr, sr, _ = orc.sgd_requant(qw, sw, dw, lr, seed, step)
+        assert_bitwise(host(sd), sr, "scales")
+        assert_bitwise(host(qd), qr, "codes")
+
+
 def test_sgd_zero_rows(T, Q, orc):
     N, K = 4, 64
     qw = np.zeros((N, K), np.int8)

@@ -25,8 +25,9 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32
         }
         const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
         const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
-        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
-        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+        // Three-input exclusive or in one instruction (truth table 0x96).
+        const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c[1], k0, 0x96);
+        const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c[3], k1, 0x96);
         c[1] = (uint32_t)p1;
         c[3] = (uint32_t)p0;
         c[0] = n0;
@@ -53,32 +54,83 @@ __device__ __forceinline__ float adamw_elem(const AdamParams &a, float w0, float
     return w0 * a.decay - a.c1 * (m / d);
 }
 
-// Stochastic codes of one 8-element chunk w[8] for the row scale s2 > 0: one
-// Philox block per 8 consecutive elements of the row-major weight, counter
-// (blk, step), key (seed); element e takes 16-bit half (e & 1) of word e >> 1
-// as u = r * 2^-16, and q = floor(y) + (u < y - floor(y)), y = fl(w / s2),
-// clamped to [-127, 127].
-__device__ __forceinline__ i32x2 sr_codes8(const float w[8], float s2, uint64_t blk,
+// A row's requant scale s2 > 0 with inv = fl(1 / s2); 'fast' when s2 lies in
+// [2^-40, 2^40], the range in which row_quotient is exact.
+struct RowScale {
+    float s, inv;
+    bool fast;
+};
+
+__device__ __forceinline__ RowScale row_scale(float s2)
+{
+    return RowScale{s2, 1.0f / s2, s2 >= 0x1p-40f && s2 <= 0x1p40f};
+}
+
+// fl(w / s) from the row's reciprocal inv = fl(1 / s), without a division:
+// q = fl(w inv), then twice q = fl(q + r inv) with the remainder r = w - q s
+// (exact by FMA).  The first correction leaves q within half an ulp plus
+// about 2^-45 relative of w / s, i.e. faithful; from a faithful q and a
+// correctly rounded reciprocal, one more correction yields the correctly
+// rounded quotient (Markstein's theorem, IBM J. Res. Dev. 34(1), 1990),
+// provided nothing underflows.  With s in [2^-40, 2^40] that holds whenever
+// the result is 0 or at least 2^-40 in magnitude; smaller quotients must be
+// recomputed by division.
+__device__ __forceinline__ float row_quotient(float w, float s, float inv)
+{
+    float q = w * inv;
+    float r = __builtin_fmaf(-q, s, w);
+    q = __builtin_fmaf(r, inv, q);
+    r = __builtin_fmaf(-q, s, w);
+    return __builtin_fmaf(r, inv, q);
+}
+
+// Stochastic codes of one 8-element chunk w[8] for the row scale rs.s > 0:
+// one Philox block per 8 consecutive elements of the row-major weight,
+// counter (blk, step), key (seed); element e takes 16-bit half (e & 1) of
+// word e >> 1 as u = r * 2^-16, and q = floor(y) + (u < y - floor(y)),
+// y = fl(w / rs.s), clamped to [-127, 127].  Clamping y to [-127, 127] first
+// gives the same codes (a y beyond 127 in magnitude has codes at the clamp
+// either way) and keeps every code within reach of the packing below: the
+// floor plus 1.5 * 2^23 is exact, its low byte is the floor's two's
+// complement byte, and adding the stochastic carry to the bit pattern adds
+// it to that byte.
+__device__ __forceinline__ i32x2 sr_codes8(const float w[8], const RowScale &rs, uint64_t blk,
                                            uint32_t seed_lo, uint32_t seed_hi, uint32_t step_lo,
                                            uint32_t step_hi)
 {
+    constexpr float kMagic = 0x1.8p23f;
     uint32_t x[4] = {(uint32_t)blk, (uint32_t)(blk >> 32), step_lo, step_hi};
     philox4x32_10(x, seed_lo, seed_hi);
-    float out[8];
+    float y[8];
+    bool slow = !rs.fast;
+    if (rs.fast) {
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            y[e] = row_quotient(w[e], rs.s, rs.inv);
+            slow |= w[e] != 0.0f && __builtin_fabsf(y[e]) < 0x1p-40f;
+        }
+    }
+    if (slow) {
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            y[e] = w[e] / rs.s;
+    }
+    uint32_t b[8];
 #pragma unroll
     for (int e = 0; e < 8; e++) {
         const uint32_t r16 = (x[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-        const float y = w[e] / s2;
-        const float f = floorf(y);
-        const float frac = y - f;
+        const float yc = fminf(fmaxf(y[e], -127.0f), 127.0f);
+        const float f = floorf(yc);
+        const float frac = yc - f;
         const float u = (float)r16 * 0x1p-16f;
-        const float v = f + (u < frac ? 1.0f : 0.0f);
-        out[e] = fminf(fmaxf(v, -127.0f), 127.0f);
+        b[e] = __float_as_uint(f + kMagic) + (u < frac ? 1u : 0u);
     }
-    i32x2 o;
-    o[0] = (int)pack4(out[0], out[1], out[2], out[3]);
-    o[1] = (int)pack4(out[4], out[5], out[6], out[7]);
-    return o;
+    auto pack = [&](int o) {
+        const uint32_t lo = __builtin_amdgcn_perm(b[o + 1], b[o], 0x0C0C0400u);
+        const uint32_t hi = __builtin_amdgcn_perm(b[o + 3], b[o + 2], 0x04000C0Cu);
+        return (int)(lo | hi);
+    };
+    return i32x2{pack(0), pack(4)};
 }
 
 template <int THREADS, int J, bool ADAM>
@@ -131,7 +183,7 @@ __global__ __launch_bounds__(THREADS) void sgd_requant_kernel(
     // block_max ends with a barrier, so every lane has read sw[row] before
     // lane 0 overwrites it below.
     const float a = block_max<THREADS>(amax, red);
-    const float s2 = a / 127.0f;
+    const RowScale rs = row_scale(a / 127.0f);
 #pragma unroll
     for (int j = 0; j < J; j++) {
         const int64_t c = t + (int64_t)j * THREADS;
@@ -141,12 +193,12 @@ __global__ __launch_bounds__(THREADS) void sgd_requant_kernel(
         // 8c + e has i >> 3 = base / 8 + c and i & 7 = e (K is a multiple of
         // 16).
         const i32x2 o = a == 0.0f ? i32x2{0, 0}
-                                  : sr_codes8(w[j], s2, (uint64_t)(base / 8 + c), seed_lo,
+                                  : sr_codes8(w[j], rs, (uint64_t)(base / 8 + c), seed_lo,
                                               seed_hi, step_lo, step_hi);
         *reinterpret_cast<i32x2 *>(qw + base + c * 8) = o;
     }
     if (t == 0) {
-        sw[row] = s2;
+        sw[row] = rs.s;
         if constexpr (ADAM) {
             if (bias && db && ap.bm && ap.bv) {
                 float m = ap.bm[row], v = ap.bv[row];
@@ -352,7 +404,7 @@ __global__ __launch_bounds__(THREADS) void wn_sgd_kernel(
         }
     }
     const float am = block_max<THREADS>(amax, red);
-    const float s2 = am / 127.0f;
+    const RowScale rs = row_scale(am / 127.0f);
     int m2 = 0;
 #pragma unroll
     for (int j = 0; j < J; j++) {
@@ -360,7 +412,7 @@ __global__ __launch_bounds__(THREADS) void wn_sgd_kernel(
         if (c >= nch)
             continue;
         const i32x2 o = am == 0.0f ? i32x2{0, 0}
-                                   : sr_codes8(d[j], s2, (uint64_t)(base / 8 + c), seed_lo,
+                                   : sr_codes8(d[j], rs, (uint64_t)(base / 8 + c), seed_lo,
                                                seed_hi, step_lo, step_hi);
         *reinterpret_cast<i32x2 *>(q + base + c * 8) = o;
 #pragma unroll
@@ -370,7 +422,7 @@ __global__ __launch_bounds__(THREADS) void wn_sgd_kernel(
     const float nrm2 = code_norm(block_sum_i64<THREADS>(m2, isum));
     if (t == 0) {
         const float g2 = gr - lr * dg;
-        s[row] = s2;
+        s[row] = rs.s;
         g[row] = g2;
         sw[row] = nrm2 == 0.0f ? 0.0f : g2 / nrm2;
         if (bias && db)
