@@ -186,6 +186,60 @@ def skinny_forward(torch, reps=240, copies=24):
     return res
 
 
+def mlp_products(torch, reps=10):
+    """The six products of the transformer MLP workload (8192 tokens, fc1
+    4096 -> 14336, fc2 14336 -> 4096, dX rotated back with blocks of 128),
+    each timed over `reps` calls through the same entry point as the step,
+    with its workspace for split tails.  Operands are seeded codes in
+    [-127, 127] and positive scales: a product's time does not depend on
+    the values.  TOPS count 2 M N K per call."""
+    from w8a8_integer_linear_amd import _native as nat
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    M = 8192
+
+    def codes(r, c):
+        return torch.randint(-127, 128, (r, c), dtype=torch.int8, device="cuda", generator=g)
+
+    def scales(n):
+        return torch.rand(n, device="cuda", generator=g) * 1e-2 + 1e-3
+
+    res = {}
+    for name, K, N in (("fc1", 4096, 14336), ("fc2", 14336, 4096)):
+        qx, sx, qw, sw = codes(M, K), scales(M), codes(N, K), scales(N)
+        qg1, sg1, qg2, sg2 = codes(M, N), scales(M), codes(N, M), scales(N)
+        out = {0: torch.empty(M, N, device="cuda"), 1: torch.empty(M, K, device="cuda"),
+               2: torch.empty(N, K, device="cuda")}
+        ws = torch.zeros(max(nat.qlin_product_ws_bytes(op, M, N, K) for op in range(3)) + 16,
+                         dtype=torch.uint8, device="cuda")
+        calls = {
+            "fwd": lambda: nat.qlin_product_ws(nat.QLIN_OP_FWD, qx, sx, qw, M, N, K, scol=sw,
+                                               out=out[0], workspace=ws),
+            "dx": lambda: nat.qlin_product_ws(nat.QLIN_OP_DX, qg1, sg1, qw, M, N, K,
+                                              had_block=HAD, out=out[1], workspace=ws),
+            "dw": lambda: nat.qlin_product_ws(nat.QLIN_OP_DW, qg2, sg2, qx, M, N, K,
+                                              out=out[2], workspace=ws),
+        }
+        for op, fn in calls.items():
+            fn()
+            fn()
+            torch.cuda.synchronize()
+            b = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            b.record()
+            for _ in range(reps):
+                fn()
+            e.record()
+            torch.cuda.synchronize()
+            ms = b.elapsed_time(e) / reps
+            tops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+            res[f"mlp_{name}_{op}"] = {"ms": round(ms, 4), "tops": round(tops, 1),
+                                       "frac_mfma": round(tops / PEAK_INT8_TOPS, 4),
+                                       "shape": [M, K, N]}
+        del out, ws
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -328,6 +382,7 @@ def main():
                                        "shape": [N, K]}}
     out["extras"].update(wn_update(torch, layer))
     out["extras"].update(skinny_forward(torch))
+    out["extras"].update(mlp_products(torch))
     if args.cpu_tokens > 0:
         print(f"[bench] cpu baseline on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(d, args.cpu_tokens)
