@@ -247,6 +247,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="token sample of the oracle CPU baseline (0 skips it)")
+    ap.add_argument("--no-mlp", action="store_true",
+                    help="skip the MLP workload's products, whose kernels share names with "
+                         "the step's (for per-kernel profiler summaries of the step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before the steps, run a plain device copy of 512 MiB (three times) "
                          "whose counter readings calibrate HBM byte counters")
@@ -382,7 +385,8 @@ def main():
                                        "shape": [N, K]}}
     out["extras"].update(wn_update(torch, layer))
     out["extras"].update(skinny_forward(torch))
-    out["extras"].update(mlp_products(torch))
+    if not args.no_mlp:
+        out["extras"].update(mlp_products(torch))
     if args.cpu_tokens > 0:
         print(f"[bench] cpu baseline on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(d, args.cpu_tokens)

@@ -104,7 +104,7 @@ def main(out_dir, digest=None):
         f.write("# rocprofv3 --kernel-trace --stats of the headline training step\n")
         f.write("# (12000 tokens, 5376 -> 7168, Hadamard block 128).  Command:\n")
         f.write("#   rocprofv3 --kernel-trace --stats -d OUT/kt -o kt --output-format csv -- "
-                "python bench.py --cpu-tokens 0\n")
+                "python bench.py --cpu-tokens 0 --no-mlp\n")
         f.write(f"# {'kernel':<70} {'calls':>5} {'avg_us':>9} {'pct':>6}\n")
         for s in sorted(stats, key=lambda r: -r["total_ns"]):
             f.write(f"  {s['kernel'][:70]:<70} {s['calls']:>5} {s['avg_ns'] / 1e3:>9.2f} "
@@ -145,9 +145,9 @@ def main(out_dir, digest=None):
     rec = {"source_digest": digest, "calibration_dispatches": cal, "fetch_scale": f_fac,
            "write_scale": w_fac, "kernels": kernels,
            "commands": ["rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o fetch --output-format csv -- "
-                        "python bench.py --steps 2 --warmup 1 --cpu-tokens 0 --copy-calibration",
+                        "python bench.py --steps 2 --warmup 1 --cpu-tokens 0 --no-mlp --copy-calibration",
                         "rocprofv3 --pmc WRITE_SIZE -d OUT/write -o write --output-format csv -- "
-                        "python bench.py --steps 2 --warmup 1 --cpu-tokens 0 --copy-calibration"]}
+                        "python bench.py --steps 2 --warmup 1 --cpu-tokens 0 --no-mlp --copy-calibration"]}
     with open(os.path.join(PROFILES, "pmc_traffic.json"), "w") as f:
         json.dump(rec, f, indent=1)
     with open(os.path.join(PROFILES, "pmc_traffic.txt"), "w") as f:
@@ -167,7 +167,7 @@ def main(out_dir, digest=None):
         with open(os.path.join(PROFILES, "mfma_busy_clock.txt"), "w") as f:
             f.write("# Shader clock and matrix-pipe occupancy per kernel of the headline step.\n")
             f.write("#   rocprofv3 --pmc SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES -d OUT/busy -o busy "
-                    "--output-format csv -- python bench.py --steps 2 --warmup 1 --cpu-tokens 0\n")
+                    "--output-format csv -- python bench.py --steps 2 --warmup 1 --cpu-tokens 0 --no-mlp\n")
             f.write(f"# clock = SQ_BUSY_CYCLES / {n_se} shader engines / dispatch duration; "
                     f"mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / {n_simd} SIMDs / busy cycles.\n")
             f.write("# Fraction of the 2.4 GHz dense INT8 peak = mfma_busy x clock / 2.4.\n")
@@ -195,7 +195,7 @@ def lds_summary(out_dir):
         f.write("# LDS activity per dispatch of the headline step's kernels.\n")
         f.write("#   rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS SQ_WAVES "
                 "-d OUT/lds -o lds --output-format csv -- python bench.py --steps 2 --warmup 1 "
-                "--cpu-tokens 0\n")
+                "--cpu-tokens 0 --no-mlp\n")
         f.write(f"# {'kernel':<70} {'lds_insts':>12} {'conflict_cyc':>12} {'waves':>7}\n")
         for k, d in sorted(vals.items(), key=lambda kv: -statistics.mean(
                 kv[1].get("SQ_INSTS_LDS", [0]))):
