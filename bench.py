@@ -14,6 +14,9 @@ Per-call durations come from HIP events recorded on the launch stream between
 the calls inside the timed steps; the dominant call is reported against its
 roofline.  The CPU baseline runs the oracle on a bounded token sample.
 
+The default warmup is 50 steps (about 75 ms): after 5, the clocks have not
+settled, and the same GPU timed its steps about 4% slower.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 import argparse
@@ -244,7 +247,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="token sample of the oracle CPU baseline (0 skips it)")
     ap.add_argument("--no-mlp", action="store_true",
