@@ -301,18 +301,19 @@ def main():
         marks.append((label, ev))
 
     def step(i):
-        tick("start")
+        if layer.timer is not None:
+            tick("start")
         layer.forward(x)
         layer.backward(dy)
         layer.sgd_step(LR, SEED, i)
 
-    layer.timer = tick
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    marks.clear()
 
+    # The timed steps carry no per-call events; the per-call breakdown comes
+    # from as many steps again, run after them with an event between calls.
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -323,6 +324,18 @@ def main():
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t_begin.elapsed_time(t_end) / args.steps
+
+    print(f"[bench] per-call events over {args.steps} more steps", file=sys.stderr, flush=True)
+    layer.timer = tick
+    e_begin = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
+    e_begin.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i)
+    e_end.record(stream)
+    torch.cuda.synchronize()
+    print(f"[bench] {ms_per_step:.4f} ms per step; with per-call events "
+          f"{e_begin.elapsed_time(e_end) / args.steps:.4f}", file=sys.stderr, flush=True)
 
     per = {}
     for (_, a), (label, b) in zip(marks[:-1], marks[1:]):
