@@ -10,8 +10,9 @@ SGD stochastic requant.
 Metric: int8 TOPS counting the three products (3 * 2 * M * N * K ops) over
 the wall time of the full step, and its fraction of the dense INT8 MFMA peak.
 
-Per-call durations come from HIP events recorded on the launch stream between
-the calls inside the timed steps; the dominant call is reported against its
+The timed steps carry no events between calls.  Per-call durations come from
+HIP events recorded on the launch stream between the calls of as many steps
+again, run after the timed ones; the dominant call is reported against its
 roofline.  The CPU baseline runs the oracle on a bounded token sample.
 
 The default warmup is 50 steps (about 75 ms): after 5, the clocks have not
