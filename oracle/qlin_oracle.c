@@ -57,7 +57,11 @@
  *
  * Parity is pinned by tests against scipy's Hadamard matrix, brute-force
  * integer and float64 matrix products, exactly quantizable inputs, numpy's
- * Philox4x64-10, and statistical properties of the stochastic rounding.
+ * Philox4x64-10, Triton's Philox4x32-10 (run by its CPU interpreter),
+ * statistical properties of the stochastic rounding, and numpy float32
+ * replicas of every fp32 step above (rotation stage order, the quantizer's
+ * division, the epilogue order, the SGD update and its rounding comparison),
+ * compared bit for bit.
  */
 #include <math.h>
 #include <omp.h>
