@@ -28,6 +28,21 @@
  *    features) and K (in features) are multiples of 16.  A contraction longer
  *    than QLIN_MAX_CONTRACTION is rejected with QLIN_EUNSUPPORTED, except by
  *    qlin_product_ws, which combines int32 chunks in int64.
+ *  - Operand reach: the product kernels address each int8 operand with 32-bit
+ *    byte offsets from a base that moves with the tile and the contraction,
+ *    and must reach no further than 2,147,483,632 bytes from it.  The product
+ *    calls (qlin_fwd, qlin_bwd_dx, qlin_bwd_dw, qlin_product_ws and
+ *    qlin_gemm_s32) return QLIN_EUNSUPPORTED, before launching anything, for
+ *    the shapes whose offsets would go past that:
+ *      an operand strided along the contraction (dX: qw, whose rows hold K
+ *      bytes; dW: qg2 and qx, rows of N and K bytes) needs
+ *      (min(T, 128) - 1) * row_bytes + 256 <= 2,147,483,632, with T the
+ *      contraction: row_bytes <= 16,909,312 once T >= 128;
+ *      an operand contiguous along the contraction (forward: qx and qw, dX:
+ *      qg1) needs (min(rows, 256) - 1) * T + t <= 2,147,483,632, with t = T
+ *      within the int32 bound and t = 130,944 (one chunk) beyond it: only
+ *      qlin_product_ws's long forward and dX contractions reach this, at
+ *      T > 8,420,976 when the operand has 256 rows or more.
  *  - Arithmetic: IEEE binary32, round to nearest even, no fused multiply-add,
  *    IEEE division.  Results are deterministic and do not depend on the
  *    launch configuration, except col_sum of qlin_quantize_cols (fp32 sums
@@ -60,8 +75,8 @@ extern "C" {
 
 /* Longest contraction for which an int32 sum of int8 x int8 products cannot
  * overflow: 131071 * 128 * 128 < 2^31 (mini_trainer guide, arithmetic
- * paragraph: longer contractions need an int64 combination of bounded int32
- * partial products, which this library does not provide). */
+ * paragraph).  The plain product calls reject longer ones; qlin_product_ws
+ * takes them, adding exact int32 chunk sums in int64. */
 #define QLIN_MAX_CONTRACTION 131071
 /* Largest Hadamard block and longest row the row kernels accept. */
 #define QLIN_MAX_HAD_BLOCK 512
@@ -99,9 +114,11 @@ int qlin_quantize_rows(const void *x, int dtype, int64_t rows, int64_t cols,
 
 /*
  * Per-column dynamic INT8 quantization of x * prescale[:, None], the operand
- * of the weight-gradient product: scales sit on the output axis of that
- * product, never on its contraction (token) axis.  q keeps the [rows, cols]
- * layout of x.
+ * of the weight-gradient product (mini_trainer guide, opening paragraph: the
+ * backward matrix products are integer products on INT8 operands, the weight
+ * gradient's on the saved INT8 input).  Scales sit on the output axis of that
+ * product, never on its contraction (token) axis, so they factor out of the
+ * token sum exactly.  q keeps the [rows, cols] layout of x.
  *
  *   x         [rows, cols] fp32 or bf16 input (dY, rows = tokens).
  *   prescale  [rows] fp32 or NULL (the activation row scales s_x).
@@ -209,11 +226,11 @@ int qlin_bwd_dw(const int8_t *qg2, const float *sg2, const int8_t *qx, int64_t M
  * Any of the three products with a caller workspace: the same results, bit
  * for bit, as qlin_fwd / qlin_bwd_dx / qlin_bwd_dw, for a contraction of any
  * length up to 2^31 - 1.
- *  - Beyond QLIN_MAX_CONTRACTION (mini_trainer guide, arithmetic paragraph:
- *    contractions above 131,071 combine bounded int32 dot products in int64
- *    before scaling) the contraction runs in chunks of at most 131,071 terms
- *    whose exact int32 sums are combined in int64 in the workspace; fl32 of
- *    the int64 total then goes through the product's usual epilogue.
+ *  - Beyond QLIN_MAX_CONTRACTION (mini_trainer guide, arithmetic paragraph,
+ *    on contractions too long for an exact int32 sum) the contraction runs
+ *    in chunks of at most 130,944 terms, each summed exactly in int32; the
+ *    workspace adds the chunk sums in int64, and the int64 total, converted
+ *    once to fp32, goes through the product's usual epilogue.
  *  - Within the bound the workspace balances the grid: the 256 x 256 output
  *    tiles left over after the last whole round of the chip's 256 compute
  *    units are each computed in two or three pieces along the contraction,
@@ -342,7 +359,9 @@ int qlin_adamw_requant(int8_t *qw, float *sw, const float *dw, float *m, float *
 
 /*
  * Raw int32 accumulators of one of the three products (same kernels as the
- * fused calls, no dequant), for exact verification.  op is QLIN_OP_FWD,
+ * fused calls, no dequant), for exact verification of the integer forward
+ * and backward products (mini_trainer guide, opening paragraph; OneTrainer
+ * PR #1681, commit note 1: an int8 x int8 -> int32 product).  op is QLIN_OP_FWD,
  * QLIN_OP_DX or QLIN_OP_DW; a, b and the shape arguments mean what they mean
  * in qlin_fwd / qlin_bwd_dx / qlin_bwd_dw; c is [M,N], [M,K] or [N,K].
  */

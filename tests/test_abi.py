@@ -99,6 +99,50 @@ def test_product_validation(L):
     assert L.qlin_gemm_s32(0, ODD, Q, 4, 16, 16, R, None) == 1        # misaligned
 
 
+# Operand reach of the product kernels (32-bit buffer offsets, at most
+# 2,147,483,632 bytes from a base at the tile's first row or the stage's first
+# contraction row).
+KM_ROW_MAX = 16909312        # (128 - 1) * row + 256 <= 2,147,483,632
+LONG_T_MAX = 8420976         # (256 - 1) * T + 130,944 <= 2,147,483,632
+
+
+def test_operand_reach_bounds():
+    lim = 2147483632
+    assert 127 * KM_ROW_MAX + 256 <= lim < 127 * (KM_ROW_MAX + 16) + 256
+    assert 255 * LONG_T_MAX + 130944 <= lim < 255 * (LONG_T_MAX + 16) + 130944
+
+
+def test_product_operand_reach(L):
+    _cpu_only()
+    F = lambda i: (i + 1) << 40     # widely spaced fake addresses
+    past = KM_ROW_MAX + 16
+    # dX: qw is read down its columns, rows of K bytes
+    assert L.qlin_bwd_dx(F(0), F(1), F(2), 4, 128, past, 0, F(3), None) == 2
+    assert L.qlin_gemm_s32(1, F(0), F(2), 4, 128, past, F(3), None) == 2
+    assert L.qlin_bwd_dx(F(0), F(1), F(2), 0, 128, KM_ROW_MAX, 0, F(3), None) == 0
+    # dW: qg2 (rows of N bytes) and qx (rows of K bytes), both down their columns
+    assert L.qlin_bwd_dw(F(0), F(1), F(2), 128, past, 16, F(3), None) == 2
+    assert L.qlin_bwd_dw(F(0), F(1), F(2), 128, 16, past, F(3), None) == 2
+    assert L.qlin_gemm_s32(2, F(0), F(2), 128, 16, past, F(3), None) == 2
+    # a contraction of 127 rows reaches less far: accepted up to the row count
+    # bound (the call then fails to launch here, where no GPU exists)
+    assert L.qlin_bwd_dw(F(0), F(1), F(2), 127, 16, past, F(3), None) != 2
+    # qlin_product_ws past the int32 bound: the forward and dX contraction is
+    # also the row stride of their contiguous operand
+    C = 4096
+    def ws_call(op, M, N, K, ws):
+        return L.qlin_product_ws(op, F(0), F(1), F(2), F(4) if op == 0 else None, None, M, N, K,
+                                 0, F(3), ws, C + 8 * 256 * 256 * 16, None)
+    assert ws_call(0, 256, 16, LONG_T_MAX + 16, F(5)) == 2
+    assert ws_call(1, 256, LONG_T_MAX + 16, 16, F(5)) == 2
+    assert ws_call(0, 256, 16, LONG_T_MAX, None) == 1      # within reach: the workspace is next
+    assert ws_call(1, 256, LONG_T_MAX, 16, None) == 1
+    assert ws_call(0, 255, 16, LONG_T_MAX + 16, None) == 1  # 255 rows reach less far
+    # a long dW contraction only moves the base: its reach is that of N and K
+    assert ws_call(2, 1 << 24, 16, past, F(5)) == 2
+    assert ws_call(2, 1 << 24, 16, 16, None) == 1
+
+
 def test_weight_norm_validation(L):
     _cpu_only()
     T = 0x50000

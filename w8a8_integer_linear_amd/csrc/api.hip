@@ -197,6 +197,8 @@ static int check_product(int op, const void *a, const void *b, void *out, int64_
     const int64_t contraction = op == QLIN_OP_FWD ? K : (op == QLIN_OP_DX ? N : M);
     if (contraction > max_contraction || M > kMaxRows || N > kMaxRows || K > kMaxRows)
         return QLIN_EUNSUPPORTED;
+    if (!qlin::product_addressable(op, M, N, K))
+        return QLIN_EUNSUPPORTED;
     return QLIN_OK;
 }
 

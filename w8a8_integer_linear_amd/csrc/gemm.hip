@@ -76,9 +76,12 @@ struct GemmParams {
 
 // ------------------------------------------------------------------ staging
 
-// Buffer resource over a whole operand: every lane offset used below is
-// either a valid byte offset (< 2^31 - 16 by the shape limits) or kOob, which
-// the buffer range check turns into a zero fill of the lane's 16 LDS bytes.
+// Buffer resource over an operand from a base at the tile's first row (row
+// operand) or the stage's first contraction row (km operand): every lane
+// offset used below is either a byte offset whose 16 bytes end at or below
+// kOob, which product_addressable checks for each shape before a launch, or
+// kOob itself, which the buffer range check turns into a zero fill of the
+// lane's 16 LDS bytes.
 constexpr uint32_t kOob = 0x7FFFFFF0u;
 constexpr int kRsrcWord3 = 0x00020000;   // raw 32-bit buffer format
 // Cache policy of buffer accesses that must be coherent across the XCDs'
@@ -1140,6 +1143,30 @@ SplitPlan split_plan(int op, int64_t M, int64_t N, int64_t K)
     return SplitPlan{(int)full, (int)tail, (int)split};
 }
 
+// Contraction terms per launch of a chunked product (1023 stages of 128):
+// within the int32-exact bound of 131,071.
+constexpr int64_t kChunkLen = 1023 * 128;
+
+bool product_addressable(int op, int64_t M, int64_t N, int64_t K)
+{
+    const int64_t T = op == 0 ? K : (op == 1 ? N : M);
+    const int64_t t = T > 131071 ? kChunkLen : T;       // contraction of one launch
+    auto lo = [](int64_t a, int64_t b) { return a < b ? a : b; };
+    // Row operand of 'rows' rows with stride ld: a tile's loads reach
+    // (rows in the tile - 1) * ld + t bytes past its base.  Km operand with
+    // stride ld: a stage's loads reach (contraction rows in the stage - 1) *
+    // ld + 256 (one tile's columns).
+    auto row_ok = [&](int64_t rows, int64_t ld) {
+        return rows < 1 || (lo(rows, 256) - 1) * ld + t <= (int64_t)kOob;
+    };
+    auto km_ok = [&](int64_t ld) { return t < 1 || (lo(t, 128) - 1) * ld + 256 <= (int64_t)kOob; };
+    if (op == 0)
+        return row_ok(M, K) && row_ok(N, K);
+    if (op == 1)
+        return row_ok(M, N) && km_ok(K);
+    return km_ok(N) && km_ok(K);
+}
+
 size_t split_ws_bytes(const SplitPlan &sp)
 {
     if (sp.split < 2)
@@ -1220,11 +1247,10 @@ void launch_product(const ProductArgs &a, hipStream_t st)
 // acc + workspace through the usual dequant (and rotation) arithmetic.
 void launch_product_long(const ProductArgs &a, int64_t *ws, hipStream_t st)
 {
-    constexpr int64_t kChunk = 1023 * 128;
     const int64_t T = a.op == 0 ? a.K : (a.op == 1 ? a.N : a.M);
-    for (int64_t k0 = 0; k0 < T; k0 += kChunk) {
+    for (int64_t k0 = 0; k0 < T; k0 += kChunkLen) {
         ProductArgs c = a;
-        const int64_t len = T - k0 < kChunk ? T - k0 : kChunk;
+        const int64_t len = T - k0 < kChunkLen ? T - k0 : kChunkLen;
         c.t_len = len;
         c.ws = ws;
         c.ws_mode = k0 == 0 ? 1 : (k0 + len >= T ? 3 : 2);

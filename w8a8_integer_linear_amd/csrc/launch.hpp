@@ -52,6 +52,11 @@ struct ProductArgs {
 
 void launch_product(const ProductArgs &p, hipStream_t st);
 
+// Whether the product kernels can address every operand byte of this shape
+// with their 32-bit buffer offsets (for contractions past the int32 bound,
+// those of one chunk's launch).
+bool product_addressable(int op, int64_t M, int64_t N, int64_t K);
+
 // How a product balances its last round of 256 x 256 tiles over the chip:
 // 'full' whole tiles, then each of the 'tail' remaining tiles in 'split'
 // pieces along the contraction (split 1: no balancing).
