@@ -10,10 +10,17 @@ SGD stochastic requant.
 Metric: int8 TOPS counting the three products (3 * 2 * M * N * K ops) over
 the wall time of the full step, and its fraction of the dense INT8 MFMA peak.
 
-The timed steps carry no events between calls.  Per-call durations come from
-HIP events recorded on the launch stream between the calls of as many steps
-again, run after the timed ones; the dominant call is reported against its
-roofline.  The CPU baseline runs the oracle on a bounded token sample.
+The timed steps carry one event per step boundary and none between calls;
+ms_per_step is the median step, and the mean over the bracketed K steps is
+reported beside it.  Per-call durations come from HIP events recorded on the
+launch stream between the calls of as many steps again, run after the timed
+ones; the dominant call is reported against its roofline.  The memory-bound
+calls are also timed on their own, cycling through more than 512 MB of
+buffer copies so the 256 MB infinity cache cannot serve them, next to the
+library's streaming copy (the device's practical read+write ceiling).  The
+forward of 2048 tokens (rotate, quantize, forward product) is timed on its
+own as well.  The CPU baseline runs the oracle, compiled for the host CPU,
+on a bounded token sample.
 
 The default warmup is 50 steps (about 75 ms): after 5, the clocks have not
 settled, and the same GPU timed its steps about 4% slower.
@@ -92,9 +99,25 @@ def traffic_for(call):
     return total or None
 
 
+def host_cpu():
+    """(logical CPUs, CPU model name) of the host."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return os.cpu_count(), model
+
+
 def cpu_baseline(d, tokens):
-    """The oracle's full step on the first `tokens` rows (weight prep untimed)."""
+    """The oracle's full step on the first `tokens` rows (weight prep untimed),
+    with the oracle compiled -O3 -march=native for this host."""
     import oracle
+    flags = oracle.use_host_build()
     qw, sw = oracle.prepare_weight(d["w"], had_block=HAD)
     x, dy = d["x"][:tokens], d["dy"][:tokens]
     t0 = time.perf_counter()
@@ -108,10 +131,111 @@ def cpu_baseline(d, tokens):
     oracle.sgd_requant(qw, sw, dw, LR, SEED, 0)
     t = time.perf_counter() - t0
     ops = 3 * 2.0 * tokens * N * K
+    ncpu, model = host_cpu()
     return {"value": round(ops / t / 1e12, 6), "unit": "TOPS", "cores": oracle.threads(),
             "kind": "oracle",
             "sample": f"{tokens} of {M} tokens at full 5376->7168 width, all eight steps "
-                      f"(SGD requant over the whole weight), {t:.2f} s"}
+                      f"(SGD requant over the whole weight), {t:.2f} s",
+            "host_cpus": ncpu, "cpu_model": model, "build": " ".join(flags)}
+
+
+def median(v):
+    s = sorted(v)
+    n = len(s)
+    return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+
+
+def timed_calls(torch, fns, reps):
+    """Median device time (ms) of calls fns[i % len(fns)], each bracketed by
+    events on the current stream, after one untimed pass over fns."""
+    for fn in fns:
+        fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        fns[i % len(fns)]()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    return median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])
+
+
+def memory_bound_rotating(torch, layer, d, reps=24):
+    """The memory-bound calls of the step on their own, each cycling through
+    enough copies of its operands (more than 512 MB in all) that the 256 MB
+    infinity cache cannot hold the next call's data, against the library's
+    streaming copy of 512 MiB (the same cycling), the device's practical
+    read+write ceiling.  GB/s count algorithmic bytes."""
+    import numpy as np
+    from w8a8_integer_linear_amd import _native as nat
+    x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).cuda()
+    dy = torch.from_numpy(d["dy"].view(np.int16)).view(torch.bfloat16).cuda()
+    res = {}
+
+    copy_n = 512 << 20
+    bufs = [torch.empty(copy_n, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    copy_fns = [lambda i=i: nat.qlin_stream_copy(bufs[2 * i], bufs[2 * i + 1]) for i in range(2)]
+    ms = timed_calls(torch, copy_fns, reps)
+    ceiling = 2 * copy_n / (ms * 1e-3) / 1e9
+    res["stream_copy"] = {"ms": round(ms, 4), "gbs": round(ceiling, 1),
+                          "frac_hbm": round(ceiling / PEAK_HBM_GBS, 4),
+                          "bytes": 2 * copy_n}
+    del bufs, copy_fns
+
+    def entry(name, fns, footprint):
+        ms = timed_calls(torch, fns, reps)
+        gbs = ALG_BYTES[name] / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 4), "gbs": round(gbs, 1),
+                     "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                     "frac_ceiling": round(gbs / ceiling, 4),
+                     "rotating_mb": round(footprint / 1e6, 1)}
+
+    xs = [x] + [x.clone() for _ in range(2)]
+    qxs = [torch.empty((M, K), dtype=torch.int8, device="cuda") for _ in xs]
+    sxs = [torch.empty(M, dtype=torch.float32, device="cuda") for _ in xs]
+    entry("quantize_x", [lambda i=i: nat.qlin_quantize_rows(xs[i], had_block=HAD, q=qxs[i],
+                                                            s=sxs[i]) for i in range(len(xs))],
+          len(xs) * ALG_BYTES["quantize_x"])
+    del xs, qxs
+
+    dys = [dy] + [dy.clone() for _ in range(2)]
+    outs = [(torch.empty((M, N), dtype=torch.int8, device="cuda"),
+             torch.empty(M, dtype=torch.float32, device="cuda"),
+             torch.empty((M, N), dtype=torch.int8, device="cuda"),
+             torch.empty(N, dtype=torch.float32, device="cuda"),
+             torch.empty(N, dtype=torch.float32, device="cuda")) for _ in dys]
+    entry("quantize_dy",
+          [lambda i=i: nat.qlin_quantize_grad(dys[i], layer.sw, sxs[0], q1=outs[i][0],
+                                              s1=outs[i][1], q2=outs[i][2], s2=outs[i][3],
+                                              col_sum=outs[i][4]) for i in range(len(dys))],
+          len(dys) * (M * N * 2 + 2 * M * N))
+    del dys, outs
+
+    ws = [(layer.qw.clone(), layer.sw.clone(), layer.dw.clone()) for _ in range(3)]
+    entry("sgd_requant",
+          [lambda i=i: nat.qlin_sgd_requant(ws[i][0], ws[i][1], ws[i][2], LR, SEED, i)
+           for i in range(len(ws))], len(ws) * ALG_BYTES["sgd_requant"])
+    del ws
+    return res
+
+
+def forward_2048(torch, reps=50):
+    """The forward workload of 2048 tokens (5376 -> 7168, rotation 128):
+    rotate + quantize X, then the forward product with its fused dequant, per
+    call (median of `reps`, each bracketed by events).  TOPS count 2 M N K."""
+    import numpy as np
+
+    import workloads
+    from w8a8_integer_linear_amd import LinearW8A8Training
+    m = 2048
+    d2 = workloads.linear(m, K, N, seed=SEED, with_dy=False)
+    layer = LinearW8A8Training(torch.from_numpy(d2["w"]).cuda(), had_block=HAD, max_tokens=m)
+    x = torch.from_numpy(d2["x"].view(np.int16)).view(torch.bfloat16).cuda()
+    ms = timed_calls(torch, [lambda: layer.forward(x)], reps)
+    tops = 2.0 * m * N * K / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "tops": round(tops, 1),
+            "frac_mfma": round(tops / PEAK_INT8_TOPS, 4), "shape": [m, K, N],
+            "context_rtx5090_ms": 1.27}
 
 
 def replay_skinny(torch, nat, qx, sx, qws, sw, y, eager, reps, nbytes):
@@ -316,15 +440,15 @@ def main():
     # The timed steps carry no per-call events; the per-call breakdown comes
     # from as many steps again, run after them with an event between calls.
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    t_begin.record(stream)
+    bounds[0].record(stream)
     for i in range(args.steps):
         step(args.warmup + i)
-    t_end.record(stream)
+        bounds[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms_per_step = t_begin.elapsed_time(t_end) / args.steps
+    ms_mean = bounds[0].elapsed_time(bounds[-1]) / args.steps
+    ms_per_step = median([bounds[i].elapsed_time(bounds[i + 1]) for i in range(args.steps)])
 
     print(f"[bench] per-call events over {args.steps} more steps", file=sys.stderr, flush=True)
     layer.timer = tick
@@ -335,7 +459,7 @@ def main():
         step(args.warmup + args.steps + i)
     e_end.record(stream)
     torch.cuda.synchronize()
-    print(f"[bench] {ms_per_step:.4f} ms per step; with per-call events "
+    print(f"[bench] {ms_per_step:.4f} ms per step (median; mean {ms_mean:.4f}); with per-call events "
           f"{e_begin.elapsed_time(e_end) / args.steps:.4f}", file=sys.stderr, flush=True)
 
     per = {}
@@ -373,6 +497,7 @@ def main():
     out = {
         "metric": METRIC, "value": round(tops, 2), "unit": "TOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_mean": round(ms_mean, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
         "data": "synthetic",
         "config": {"workload": "INT8 W8A8 linear training step, 12000 tokens, 5376->7168, "
@@ -401,6 +526,10 @@ def main():
                                        "frac_hbm": round(a_gbs / PEAK_HBM_GBS, 4),
                                        "shape": [N, K]}}
     out["extras"].update(wn_update(torch, layer))
+    print("[bench] memory-bound calls on rotating buffers", file=sys.stderr, flush=True)
+    out["memory_bound_rotating"] = memory_bound_rotating(torch, layer, d)
+    print("[bench] forward of 2048 tokens", file=sys.stderr, flush=True)
+    out["forward_2048"] = forward_2048(torch)
     out["extras"].update(skinny_forward(torch))
     if not args.no_mlp:
         out["extras"].update(mlp_products(torch))

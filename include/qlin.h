@@ -368,6 +368,18 @@ int qlin_adamw_requant(int8_t *qw, float *sw, const float *dw, float *m, float *
 int qlin_gemm_s32(int op, const int8_t *a, const int8_t *b, int64_t M, int64_t N,
                   int64_t K, int32_t *c, void *stream);
 
+/*
+ * Device-to-device copy of nbytes by a plain streaming kernel (16-byte loads
+ * and stores, coalesced, every lane's loads issued before its stores).  It
+ * computes nothing of the layer: it is the measured read+write bandwidth of
+ * the device, the practical ceiling against which the memory-bound calls
+ * (quantize, rotate, requant: HBM-bound steps of the path) are reported
+ * beside the nameplate HBM bandwidth.
+ *   src, dst  device buffers of nbytes, 16-byte aligned, not overlapping.
+ *   nbytes    >= 0, a multiple of 16.
+ */
+int qlin_stream_copy(const void *src, void *dst, int64_t nbytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -49,14 +49,34 @@ def build(verbose=False):
 
 _lib = None
 
+# Flags of the build the CPU baseline times: the same arithmetic (no FMA
+# contraction, no fast-math), optimised for the host it runs on.
+HOST_CFLAGS = ["-O3", "-march=native", "-std=gnu11", "-fPIC", "-shared", "-fopenmp",
+               "-ffp-contract=off", "-fno-fast-math", "-fno-finite-math-only"]
 
-def lib():
+
+def use_host_build():
+    """Compile qlin_oracle.c with HOST_CFLAGS into a private temporary file
+    and load it in place of liboracle.so for the rest of the process (the
+    CPU-baseline leg of the benchmark).  Returns the flags used."""
+    import tempfile
+    global _lib
+    out = os.path.join(tempfile.mkdtemp(prefix="oracle_host_"), "liboracle_host.so")
+    subprocess.run(["gcc", *HOST_CFLAGS, _SRC, "-o", out, "-lm"], check=True)
+    _lib = None
+    lib(out)
+    return HOST_CFLAGS
+
+
+def lib(path=None):
     """Load liboracle.so, building it first only if it does not exist."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build()
-        L = ctypes.CDLL(_LIB)
+        if path is None:
+            path = _LIB
+            if not os.path.exists(path):
+                build()
+        L = ctypes.CDLL(path)
         vp, i64, i32, f32, u64 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                   ctypes.c_float, ctypes.c_uint64)
         L.orc_threads.argtypes = []

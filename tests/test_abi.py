@@ -143,6 +143,15 @@ def test_product_operand_reach(L):
     assert ws_call(2, 1 << 24, 16, 16, None) == 1
 
 
+def test_stream_copy_validation(L):
+    _cpu_only()
+    assert L.qlin_stream_copy(P, Q, 24, None) == 1          # not a multiple of 16
+    assert L.qlin_stream_copy(ODD, Q, 32, None) == 1        # misaligned
+    assert L.qlin_stream_copy(P, P + 16, 64, None) == 1     # overlapping
+    assert L.qlin_stream_copy(None, Q, 16, None) == 1
+    assert L.qlin_stream_copy(None, None, 0, None) == 0     # nothing to copy
+
+
 def test_weight_norm_validation(L):
     _cpu_only()
     T = 0x50000

@@ -5,9 +5,14 @@ layers (8192 tokens, 4096 -> 14336 -> 4096) each on its own.
 
 The oracle recomputes every per-row quantity from the seeded inputs itself
 (weight prep, activation codes, both gradient quantizations) and compares
-them in full; the products are compared at sampled outputs it computes one by
-one (whole 128-blocks for the un-rotated dX, whole rows for dW and the
-stochastic requant).  Everything is bit-exact except the bias gradient."""
+them in full.  The products are compared at outputs it computes one by one,
+stratified over the 256 x 256 output tiles the kernels compute: at least 8
+outputs of every tile of y and dW, and for the un-rotated dX a whole rotation
+block of one row in every 128-column half of every tile.  Both the layer's
+calls (which split the grid's last partial round of tiles along the
+contraction) and the plain product calls are checked this way.  Whole rows
+of dW feed the stochastic requant check.  Everything is bit-exact except the
+bias gradient."""
 import numpy as np
 import pytest
 
@@ -15,6 +20,42 @@ import workloads
 from tests.gpu_util import announce, assert_bitwise, dev, host, torch_cuda
 
 pytestmark = pytest.mark.gpu
+
+
+TILE = 256
+
+
+def tile_samples(rng, R, C, per=8):
+    """Positions (ii, jj) with `per` random outputs inside every TILE x TILE
+    tile of an [R, C] output (fewer distinct ones in tiles smaller than that)."""
+    ii, jj = [], []
+    for r0 in range(0, R, TILE):
+        for c0 in range(0, C, TILE):
+            ii.append(rng.integers(r0, min(r0 + TILE, R), per))
+            jj.append(rng.integers(c0, min(c0 + TILE, C), per))
+    return np.concatenate(ii), np.concatenate(jj)
+
+
+def block_samples(rng, R, C, blk):
+    """(row, first column) of one blk-wide block of one random row in every
+    128-column half of every TILE x TILE tile of an [R, C] output."""
+    half = max(blk, 128)
+    out = []
+    for r0 in range(0, R, TILE):
+        for c0 in range(0, C, half):
+            m = int(rng.integers(r0, min(r0 + TILE, R)))
+            b0 = c0 + int(rng.integers(0, min(half, C - c0) // blk)) * blk
+            out.append((m, b0))
+    return out
+
+
+def _plain_products(layer, M, had):
+    """The plain calls on the layer's saved operands (no grid balancing)."""
+    from w8a8_integer_linear_amd import _native as Q
+    y = Q.qlin_fwd(layer.qx, layer.sx, layer.qw, layer.sw, layer.bias)
+    dx = Q.qlin_bwd_dx(layer._qg1[:M], layer._sg1[:M], layer.qw, had_block=had)
+    dw = Q.qlin_bwd_dw(layer._qg2[:M], layer._sg2, layer.qx)
+    return dict(y=host(y), dx=host(dx), dw=host(dw))
 
 
 def _step(T, d, M, K, N, had, lr, seed, step):
@@ -30,6 +71,7 @@ def _step(T, d, M, K, N, had, lr, seed, step):
                sg2=host(layer._sg2), dx=host(dx), dw=host(layer.dw))
     if layer.db is not None:
         got["db"] = host(layer.db)
+    got["plain"] = _plain_products(layer, M, had)
     layer.sgd_step(lr, seed, step)
     T.cuda.synchronize()
     got["qw1"], got["sw1"] = host(layer.qw), host(layer.sw)
@@ -45,25 +87,37 @@ def _check_step(orc, d, got, M, K, N, had, lr, seed, step, n_samples, rng):
     qx, sx = orc.quantize_rows(d["x"], had_block=had)
     assert_bitwise(got["sx"], sx, "activation scales")
     assert_bitwise(got["qx"], qx, "activation codes")
-    ii, jj = rng.integers(0, M, n_samples), rng.integers(0, N, n_samples)
+    ti, tj = tile_samples(rng, M, N)
+    ii = np.concatenate([ti, rng.integers(0, M, n_samples)])
+    jj = np.concatenate([tj, rng.integers(0, N, n_samples)])
     y_ref = orc.op_at(orc.OP_FWD, qx, sx, qw, sw, d["b"], M, N, K, ii, jj)
-    assert_bitwise(got["y"][ii, jj], y_ref, "y samples")
+    for which, res in (("layer", got), ("plain", got["plain"])):
+        assert_bitwise(res["y"][ii, jj], y_ref, f"y samples ({which})")
     qg1, sg1 = orc.quantize_rows(d["dy"], prescale=sw)
     assert_bitwise(got["sg1"], sg1, "dY row scales")
     assert_bitwise(got["qg1"], qg1, "dY row codes")
     qg2, sg2, db = orc.quantize_cols(d["dy"], prescale=sx, want_sum=True)
     assert_bitwise(got["sg2"], sg2, "dY column scales")
     assert_bitwise(got["qg2"], qg2, "dY column codes")
-    # dX: whole blocks of the rotated-basis gradient, then the rotation back.
+    # dX: whole blocks of the rotated-basis gradient, then the rotation back,
+    # in every 128-column half of every tile.
     blk = had if had else 16
-    for m, b0 in zip(rng.integers(0, M, 6), rng.integers(0, K // blk, 6) * blk):
-        cols = np.arange(b0, b0 + blk)
-        dxr = orc.op_at(orc.OP_DX, qg1, sg1, qw, None, None, M, N, K, np.full(blk, m), cols)
-        ref = orc.hadamard(dxr[None, :], had)[0] if had else dxr
-        assert_bitwise(got["dx"][m, b0:b0 + blk], ref, f"dx row {m} block {b0}")
+    picks = block_samples(rng, M, K, blk)
+    mm = np.repeat([m for m, _ in picks], blk)
+    cc = np.concatenate([np.arange(b0, b0 + blk) for _, b0 in picks])
+    dxr = orc.op_at(orc.OP_DX, qg1, sg1, qw, None, None, M, N, K, mm, cc).reshape(-1, blk)
+    ref = orc.hadamard(dxr, had) if had else dxr
+    for which, res in (("layer", got), ("plain", got["plain"])):
+        dx_got = res["dx"][mm, cc].reshape(-1, blk)
+        assert_bitwise(dx_got, ref, f"dx blocks ({which}, {len(picks)} blocks)")
+    # dW: 8 outputs of every tile, and whole rows (which the update reads).
+    wi, wj = tile_samples(rng, N, K)
+    dw_ref = orc.op_at(orc.OP_DW, qg2, sg2, qx, None, None, M, N, K, wi, wj)
     rows = np.sort(rng.choice(N, 4, replace=False))
     dw_rows = orc.bwd_dw_rows(qg2, sg2, qx, rows)
-    assert_bitwise(got["dw"][rows], dw_rows, "dW rows")
+    for which, res in (("layer", got), ("plain", got["plain"])):
+        assert_bitwise(res["dw"][wi, wj], dw_ref, f"dW tile samples ({which})")
+        assert_bitwise(res["dw"][rows], dw_rows, f"dW rows ({which})")
     if "db" in got:
         xf = workloads.bf16_bits_to_f32(d["dy"]) if d["dy"].dtype == np.uint16 else d["dy"]
         bound = 1e-5 * np.abs(xf.astype(np.float64)).sum(axis=0)
@@ -178,7 +232,8 @@ def test_deterministic(orc):
     a = _step(T, d, 2048, 5376, 7168, 128, 1e-3, 9, 1)
     b = _step(T, d, 2048, 5376, 7168, 128, 1e-3, 9, 1)
     for k in a:
-        assert_bitwise(a[k], b[k], k)
+        if k != "plain":
+            assert_bitwise(a[k], b[k], k)
 
 
 def test_graph_replay_of_step(orc):

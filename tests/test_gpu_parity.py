@@ -820,3 +820,20 @@ def test_rejected_calls_leave_outputs_untouched(T, Q):
                    T.ones(2, device="cuda"), qw, T.ones(16, device="cuda"), y=y)
     T.cuda.synchronize()
     assert bool((q == 5).all()) and bool((s == 3.0).all()) and bool((y == 7.0).all())
+
+
+# ------------------------------------------------------------ streaming copy
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, (64 << 20) + 16 * 777])
+def test_stream_copy(T, Q, nbytes):
+    """The bandwidth reference copies every byte (ragged last iteration and
+    a grid that walks the buffer more than once included)."""
+    announce("stream copy", nbytes)
+    g = T.Generator(device="cuda")
+    g.manual_seed(nbytes)
+    src = T.randint(0, 256, (nbytes,), dtype=T.uint8, device="cuda", generator=g)
+    dst = T.zeros(nbytes + 64, dtype=T.uint8, device="cuda")
+    Q._native.qlin_stream_copy(src, dst[:nbytes])
+    T.cuda.synchronize()
+    assert T.equal(dst[:nbytes], src)
+    assert int(dst[nbytes:].count_nonzero()) == 0

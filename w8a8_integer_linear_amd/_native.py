@@ -43,6 +43,7 @@ SIGNATURES = {
     "qlin_product_ws": ([_i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp,
                          ctypes.c_size_t, _vp], _i32),
     "qlin_product_ws_bytes": ([_i32, _i64, _i64, _i64], ctypes.c_size_t),
+    "qlin_stream_copy": ([_vp, _vp, _i64, _vp], _i32),
 }
 
 
@@ -332,3 +333,16 @@ def qlin_gemm_s32(op, a, b, M, N, K, c=None, stream=None):
     _check("qlin_gemm_s32", lib().qlin_gemm_s32(op, _ptr(a), _ptr(b), M, N, K, _ptr(c),
                                                 _stream(stream)))
     return c
+
+
+def qlin_stream_copy(src, dst, stream=None):
+    """Copy the bytes of src into dst (same size, contiguous) with the
+    library's streaming kernel."""
+    _need(src, "src", src.dtype)
+    _need(dst, "dst", dst.dtype)
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst differ in size")
+    _check("qlin_stream_copy", lib().qlin_stream_copy(_ptr(src), _ptr(dst), nbytes,
+                                                      _stream(stream)))
+    return dst

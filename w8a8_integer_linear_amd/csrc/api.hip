@@ -339,6 +339,18 @@ int qlin_gemm_s32(int op, const int8_t *a, const int8_t *b, int64_t M, int64_t N
     return finish();
 }
 
+int qlin_stream_copy(const void *src, void *dst, int64_t nbytes, void *stream)
+{
+    if (nbytes < 0 || nbytes % 16 != 0 || !array_ok(src, nbytes > 0) || !array_ok(dst, nbytes > 0))
+        return QLIN_EINVAL;
+    if (overlap(src, nbytes, dst, nbytes))
+        return QLIN_EINVAL;
+    if (nbytes == 0)
+        return QLIN_OK;
+    qlin::launch_stream_copy(src, dst, nbytes, as_stream(stream));
+    return finish();
+}
+
 int qlin_sgd_requant(int8_t *qw, float *sw, const float *dw, int64_t N, int64_t K, float lr,
                      uint64_t seed, uint64_t step, float *bias, const float *db, void *stream)
 {

@@ -72,6 +72,10 @@ size_t split_ws_bytes(const SplitPlan &sp);
 // the int64 workspace ws [rows, cols] (8 bytes per output).
 void launch_product_long(const ProductArgs &p, int64_t *ws, hipStream_t st);
 
+// Streaming device copy of nbytes (a multiple of 16) between 16-byte aligned
+// buffers: the reference for the memory-bound kernels' bandwidth.
+void launch_stream_copy(const void *src, void *dst, int64_t nbytes, hipStream_t st);
+
 void launch_sgd_requant(int8_t *qw, float *sw, const float *dw, int64_t N, int64_t K, float lr,
                         uint64_t seed, uint64_t step, float *bias, const float *db,
                         hipStream_t st);
