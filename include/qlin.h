@@ -16,8 +16,11 @@
  *  - All array pointers are device memory owned by the caller, row-major and
  *    contiguous, 16-byte aligned.  A pointer to an array with no element
  *    (for example any [M, *] array when M == 0) may be NULL.  The library
- *    allocates nothing and keeps no mutable global state; calls on different
- *    streams are independent unless they share a qlin_product_ws workspace.
+ *    allocates nothing and keeps no mutable global state, except the
+ *    scratch array of qlin_product_noalloc (one per device, held until the
+ *    process ends) and its looked-up address; calls on different streams are
+ *    independent unless they share a qlin_product_ws workspace or are
+ *    qlin_product_noalloc calls on the same device.
  *  - 'stream' is a hipStream_t (NULL means the null stream).  Every call only
  *    enqueues kernels on that stream and returns without synchronizing.
  *  - Arguments are validated before anything is launched: on any error the
@@ -257,6 +260,33 @@ int qlin_product_ws(int op, const int8_t *a, const float *srow, const int8_t *b,
                     const float *scol, const float *bias, int64_t M, int64_t N, int64_t K,
                     int had_block, float *out, void *workspace, size_t ws_bytes,
                     void *stream);
+
+/*
+ * qlin_product_ws for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same products, bit for bit, with the workspace taken from a scratch
+ * array of QLIN_NOALLOC_SCRATCH_BYTES that the library holds in device
+ * memory, one per device, for the life of the process.  Arguments are those
+ * of qlin_product_ws without the workspace.  The call allocates nothing (no
+ * hipMalloc, no allocating library routine) and uses the scratch of the
+ * current device; 'stream' must belong to that device.
+ *  - Within QLIN_MAX_CONTRACTION the scratch balances the last round of
+ *    tiles when the shape's qlin_product_ws_bytes fits in it, after a small
+ *    kernel zeroes the arrival counters it uses; when nothing is balanced or
+ *    the pieces do not fit, the ordinary product runs (the same results).
+ *  - Beyond QLIN_MAX_CONTRACTION the int64 sums (8 bytes per output, plus
+ *    4096) must fit: larger shapes return QLIN_EUNSUPPORTED before anything
+ *    is launched.
+ * Every call on a device shares that device's scratch and leaves its last
+ * contents there: calls that overlap in time on one device (on different
+ * streams, or from different host threads) race and give wrong results.
+ * The first call on each device looks up the scratch's address
+ * (QLIN_EDEVICE if the runtime cannot).
+ */
+#define QLIN_NOALLOC_SCRATCH_BYTES (4096 + 160 * 262144)
+int qlin_product_noalloc(int op, const int8_t *a, const float *srow, const int8_t *b,
+                         const float *scol, const float *bias, int64_t M, int64_t N, int64_t K,
+                         int had_block, float *out, void *stream);
 
 /* Workspace bytes qlin_product_ws needs for this shape: beyond the int32
  * bound 4096 + 8 per output element; within it 4096 + 256 KiB per balancing

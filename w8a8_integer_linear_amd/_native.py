@@ -44,7 +44,10 @@ SIGNATURES = {
                          ctypes.c_size_t, _vp], _i32),
     "qlin_product_ws_bytes": ([_i32, _i64, _i64, _i64], ctypes.c_size_t),
     "qlin_stream_copy": ([_vp, _vp, _i64, _vp], _i32),
+    "qlin_product_noalloc": ([_i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp],
+                             _i32),
 }
+NOALLOC_SCRATCH_BYTES = 4096 + 160 * 262144
 
 
 class QlinError(RuntimeError):
@@ -322,6 +325,23 @@ def qlin_product_ws(op, a, srow, b, M, N, K, scol=None, bias=None, had_block=0, 
     _check("qlin_product_ws", lib().qlin_product_ws(
         int(op), _ptr(a), _ptr(srow), _ptr(b), _ptr(scol), _ptr(bias), M, N, K, int(had_block),
         _ptr(out), _ptr(workspace), nbytes, _stream(stream)))
+    return out
+
+
+def qlin_product_noalloc(op, a, srow, b, M, N, K, out, scol=None, bias=None, had_block=0,
+                         stream=None):
+    """qlin_product_ws with the library's own device scratch in place of a
+    workspace: nothing is allocated, `out` included (the caller passes it)."""
+    shape = {QLIN_OP_FWD: (M, N), QLIN_OP_DX: (M, K), QLIN_OP_DW: (N, K)}[op]
+    _need(a, "a", torch.int8)
+    _need(b, "b", torch.int8)
+    _need(srow, "srow", torch.float32)
+    _opt(scol, "scol", torch.float32, (N,))
+    _opt(bias, "bias", torch.float32, (N,))
+    _need(out, "out", torch.float32, shape)
+    _check("qlin_product_noalloc", lib().qlin_product_noalloc(
+        int(op), _ptr(a), _ptr(srow), _ptr(b), _ptr(scol), _ptr(bias), M, N, K, int(had_block),
+        _ptr(out), _stream(stream)))
     return out
 
 

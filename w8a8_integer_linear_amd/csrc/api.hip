@@ -4,6 +4,8 @@
 // HIP call.
 #include <math.h>
 
+#include <mutex>
+
 #include "qlin.h"
 #include "launch.hpp"
 
@@ -268,45 +270,35 @@ size_t qlin_product_ws_bytes(int op, int64_t M, int64_t N, int64_t K)
     return qlin::kSplitCountBytes + (size_t)(8 * rows * cols);
 }
 
-int qlin_product_ws(int op, const int8_t *a, const float *srow, const int8_t *b,
-                    const float *scol, const float *bias, int64_t M, int64_t N, int64_t K,
-                    int had_block, float *out, void *workspace, size_t ws_bytes, void *stream)
+// Validation shared by qlin_product_ws and qlin_product_noalloc once a
+// workspace is needed: the shapes and pointers of the product (any
+// contraction up to kMaxLongContraction), the rotation block and the
+// scales.  Returns QLIN_OK, an error, or -1 for an empty forward or dX
+// product (nothing to do).
+static int check_ws_product(int op, const int8_t *a, const float *srow, const int8_t *b,
+                            const float *scol, int64_t M, int64_t N, int64_t K, int had_block,
+                            float *out)
 {
-    if (op < QLIN_OP_FWD || op > QLIN_OP_DW)
-        return QLIN_EINVAL;
-    if (op != QLIN_OP_FWD && (scol || bias))
-        return QLIN_EINVAL;
-    if (op != QLIN_OP_DX && had_block != 0)
-        return QLIN_EINVAL;
-    const int64_t contraction = op == QLIN_OP_FWD ? K : (op == QLIN_OP_DX ? N : M);
-    const bool is_long = contraction > QLIN_MAX_CONTRACTION;
-    const size_t need = qlin_product_ws_bytes(op, M, N, K);
-    if (!is_long && need == 0) {
-        // Nothing to balance: the ordinary product.
-        if (op == QLIN_OP_FWD)
-            return qlin_fwd(a, srow, b, scol, bias, M, N, K, out, stream);
-        if (op == QLIN_OP_DX)
-            return qlin_bwd_dx(a, srow, b, M, N, K, had_block, out, stream);
-        return qlin_bwd_dw(a, srow, b, M, N, K, out, stream);
-    }
     int st = check_product(op, a, b, out, M, N, K, kMaxLongContraction);
     if (st != QLIN_OK)
         return st;
     if (had_block != 0 && !hadamard_block_ok(K, had_block))
         return QLIN_EINVAL;
     if (M == 0)
-        return QLIN_OK;     // forward and dX outputs are empty (dW has M > 0 here)
+        return -1;      // forward and dX outputs are empty (dW has M > 0 here)
     if (!srow || (op == QLIN_OP_FWD && !scol))
         return QLIN_EINVAL;
-    const int64_t rows = op == QLIN_OP_DW ? N : M, cols = op == QLIN_OP_FWD ? N : K;
-    const int64_t la = op == QLIN_OP_FWD ? M * K : M * N, lb = op == QLIN_OP_DW ? M * K : N * K;
-    const int64_t nb = (int64_t)need;
-    if (!workspace || !aligned16(workspace) || ws_bytes < need ||
-        overlap(workspace, nb, out, 4 * rows * cols) || overlap(workspace, nb, a, la) ||
-        overlap(workspace, nb, b, lb))
-        return QLIN_EINVAL;
+    return QLIN_OK;
+}
+
+// Launches a validated product that uses 'workspace' (the arrival counters
+// in its first kSplitCountBytes, then partial or int64 sums).
+static int launch_ws_product(int op, const int8_t *a, const float *srow, const int8_t *b,
+                             const float *scol, const float *bias, int64_t M, int64_t N,
+                             int64_t K, int had_block, float *out, void *workspace, bool is_long,
+                             hipStream_t s)
+{
     qlin::ProductArgs p{op, a, b, M, N, K, srow, scol, bias, out, false};
-    const hipStream_t s = as_stream(stream);
     if (op == QLIN_OP_DX && had_block >= 2 && had_block <= 128) {
         p.had = had_block;
         p.had_scale = hadamard_scale(had_block);
@@ -322,6 +314,116 @@ int qlin_product_ws(int op, const int8_t *a, const float *srow, const int8_t *b,
     if (op == QLIN_OP_DX && had_block > 128)
         qlin::launch_hadamard(out, false, M, K, had_block, hadamard_scale(had_block), out, s);
     return finish();
+}
+
+// The ordinary product call of 'op' (no workspace).
+static int plain_product(int op, const int8_t *a, const float *srow, const int8_t *b,
+                         const float *scol, const float *bias, int64_t M, int64_t N, int64_t K,
+                         int had_block, float *out, void *stream)
+{
+    if (op == QLIN_OP_FWD)
+        return qlin_fwd(a, srow, b, scol, bias, M, N, K, out, stream);
+    if (op == QLIN_OP_DX)
+        return qlin_bwd_dx(a, srow, b, M, N, K, had_block, out, stream);
+    return qlin_bwd_dw(a, srow, b, M, N, K, out, stream);
+}
+
+int qlin_product_ws(int op, const int8_t *a, const float *srow, const int8_t *b,
+                    const float *scol, const float *bias, int64_t M, int64_t N, int64_t K,
+                    int had_block, float *out, void *workspace, size_t ws_bytes, void *stream)
+{
+    if (op < QLIN_OP_FWD || op > QLIN_OP_DW)
+        return QLIN_EINVAL;
+    if (op != QLIN_OP_FWD && (scol || bias))
+        return QLIN_EINVAL;
+    if (op != QLIN_OP_DX && had_block != 0)
+        return QLIN_EINVAL;
+    const int64_t contraction = op == QLIN_OP_FWD ? K : (op == QLIN_OP_DX ? N : M);
+    const bool is_long = contraction > QLIN_MAX_CONTRACTION;
+    const size_t need = qlin_product_ws_bytes(op, M, N, K);
+    if (!is_long && need == 0)     // nothing to balance: the ordinary product
+        return plain_product(op, a, srow, b, scol, bias, M, N, K, had_block, out, stream);
+    int st = check_ws_product(op, a, srow, b, scol, M, N, K, had_block, out);
+    if (st != QLIN_OK)
+        return st < 0 ? QLIN_OK : st;
+    const int64_t rows = op == QLIN_OP_DW ? N : M, cols = op == QLIN_OP_FWD ? N : K;
+    const int64_t la = op == QLIN_OP_FWD ? M * K : M * N, lb = op == QLIN_OP_DW ? M * K : N * K;
+    const int64_t nb = (int64_t)need;
+    if (!workspace || !aligned16(workspace) || ws_bytes < need ||
+        overlap(workspace, nb, out, 4 * rows * cols) || overlap(workspace, nb, a, la) ||
+        overlap(workspace, nb, b, lb))
+        return QLIN_EINVAL;
+    return launch_ws_product(op, a, srow, b, scol, bias, M, N, K, had_block, out, workspace,
+                             is_long, as_stream(stream));
+}
+
+// ------------------------------------------------------------ no allocation
+
+// Scratch of qlin_product_noalloc: arrival counters, then partial or int64
+// sums, exactly as in a qlin_product_ws workspace.  Each device that loads
+// the library holds its own copy until the process ends; every call on a
+// device shares that device's copy.  Host code never passes the array's name
+// to a kernel or a copy (on the host it is only a stand-in for the symbol):
+// it takes the device address hipGetSymbolAddress gives for the current
+// device, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[QLIN_NOALLOC_SCRATCH_BYTES];
+
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[kMaxDevices];
+
+// Device address of 'scratch' on the current device, looked up (with that
+// device current) on the first call on it.
+static int scratch_on_current_device(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return QLIN_EDEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+            return QLIN_EDEVICE;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return QLIN_OK;
+}
+
+int qlin_product_noalloc(int op, const int8_t *a, const float *srow, const int8_t *b,
+                         const float *scol, const float *bias, int64_t M, int64_t N, int64_t K,
+                         int had_block, float *out, void *stream)
+{
+    if (op < QLIN_OP_FWD || op > QLIN_OP_DW)
+        return QLIN_EINVAL;
+    if (op != QLIN_OP_FWD && (scol || bias))
+        return QLIN_EINVAL;
+    if (op != QLIN_OP_DX && had_block != 0)
+        return QLIN_EINVAL;
+    const int64_t contraction = op == QLIN_OP_FWD ? K : (op == QLIN_OP_DX ? N : M);
+    const bool is_long = contraction > QLIN_MAX_CONTRACTION;
+    const size_t need = qlin_product_ws_bytes(op, M, N, K);
+    // Within the int32 bound the scratch only balances the last round of
+    // tiles: with nothing to balance, or more pieces than the scratch holds,
+    // the ordinary product gives the same bits.
+    if (!is_long && (need == 0 || need > (size_t)QLIN_NOALLOC_SCRATCH_BYTES))
+        return plain_product(op, a, srow, b, scol, bias, M, N, K, had_block, out, stream);
+    int st = check_ws_product(op, a, srow, b, scol, M, N, K, had_block, out);
+    if (st != QLIN_OK)
+        return st < 0 ? QLIN_OK : st;
+    if (need > (size_t)QLIN_NOALLOC_SCRATCH_BYTES)
+        return QLIN_EUNSUPPORTED;     // int64 sums of a long contraction do not fit
+    void *ws = nullptr;
+    st = scratch_on_current_device(&ws);
+    if (st != QLIN_OK)
+        return st;
+    const hipStream_t s = as_stream(stream);
+    if (!is_long) {
+        // The arrival counters of this call's split tiles start at zero
+        // whatever an earlier call left.
+        qlin::launch_zero_words(ws, qlin::split_plan(op, M, N, K).tail, s);
+    }
+    return launch_ws_product(op, a, srow, b, scol, bias, M, N, K, had_block, out, ws, is_long, s);
 }
 
 int qlin_gemm_s32(int op, const int8_t *a, const int8_t *b, int64_t M, int64_t N, int64_t K,

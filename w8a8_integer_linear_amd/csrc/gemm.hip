@@ -1088,6 +1088,15 @@ __global__ __launch_bounds__(256) void skinny_fwd_kernel(const int8_t *__restric
     }
 }
 
+// Zero fill of n 32-bit words (arrival counters), a kernel rather than a
+// memset so that it can sit in a captured graph.
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t *p, int n)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n)
+        p[i] = 0;
+}
+
 template <int WM, int WN, bool AKM, bool BKM, int EPI>
 void run_gemm(const GemmParams &p0, hipStream_t st)
 {
@@ -1165,6 +1174,13 @@ bool product_addressable(int op, int64_t M, int64_t N, int64_t K)
     if (op == 1)
         return row_ok(M, N) && km_ok(K);
     return km_ok(N) && km_ok(K);
+}
+
+void launch_zero_words(void *p, int n, hipStream_t st)
+{
+    if (n > 0)
+        hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                           static_cast<uint32_t *>(p), n);
 }
 
 size_t split_ws_bytes(const SplitPlan &sp)

@@ -67,6 +67,9 @@ constexpr size_t kSplitCountBytes = 4096;
 SplitPlan split_plan(int op, int64_t M, int64_t N, int64_t K);
 // Workspace bytes the plan needs (0 when it splits nothing).
 size_t split_ws_bytes(const SplitPlan &sp);
+// Zero n 32-bit words at p on the stream (a kernel, so graph capture holds
+// no memset node).
+void launch_zero_words(void *p, int n, hipStream_t st);
 
 // A product whose contraction exceeds the int32 bound, in chunks combined in
 // the int64 workspace ws [rows, cols] (8 bytes per output).
