@@ -378,6 +378,10 @@ def main():
     ap.add_argument("--no-mlp", action="store_true",
                     help="skip the MLP workload's products, whose kernels share names with "
                          "the step's (for per-kernel profiler summaries of the step)")
+    ap.add_argument("--step-kernels-only", action="store_true",
+                    help="also skip the timings whose kernels share names with the step's "
+                         "(the 2048-token forward and the memory-bound calls on rotating "
+                         "buffers): implies --no-mlp")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before the steps, run a plain device copy of 512 MiB (three times) "
                          "whose counter readings calibrate HBM byte counters")
@@ -526,12 +530,13 @@ def main():
                                        "frac_hbm": round(a_gbs / PEAK_HBM_GBS, 4),
                                        "shape": [N, K]}}
     out["extras"].update(wn_update(torch, layer))
-    print("[bench] memory-bound calls on rotating buffers", file=sys.stderr, flush=True)
-    out["memory_bound_rotating"] = memory_bound_rotating(torch, layer, d)
-    print("[bench] forward of 2048 tokens", file=sys.stderr, flush=True)
-    out["forward_2048"] = forward_2048(torch)
+    if not args.step_kernels_only:
+        print("[bench] memory-bound calls on rotating buffers", file=sys.stderr, flush=True)
+        out["memory_bound_rotating"] = memory_bound_rotating(torch, layer, d)
+        print("[bench] forward of 2048 tokens", file=sys.stderr, flush=True)
+        out["forward_2048"] = forward_2048(torch)
     out["extras"].update(skinny_forward(torch))
-    if not args.no_mlp:
+    if not (args.no_mlp or args.step_kernels_only):
         out["extras"].update(mlp_products(torch))
     if args.cpu_tokens > 0:
         print(f"[bench] cpu baseline on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)

@@ -1030,19 +1030,28 @@ __global__ __launch_bounds__(256) void skinny_fwd_kernel(const int8_t *__restric
         // This wave's steps of the chunk: x fragments from global memory
         // (the same few rows for every workgroup, so L2-resident); rows past
         // M and bytes past K read as zeros through the buffer range check.
+        // (Only lanes of existing rows load: the others keep zeros.)
         i32x4 av[kPer];
 #pragma unroll
-        for (int t = 0; t < kPer; t++) {
-            const int k = kc * CHUNK + (w + 4 * t) * 64 + g * 16;
-            const uint32_t off = xok && k < K ? (uint32_t)(col * K + k) : kOob;
-            av[t] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+        for (int t = 0; t < kPer; t++)
+            av[t] = i32x4{0, 0, 0, 0};
+        if (xok) {
+#pragma unroll
+            for (int t = 0; t < kPer; t++) {
+                const int k = kc * CHUNK + (w + 4 * t) * 64 + g * 16;
+                const uint32_t off = k < K ? (uint32_t)(col * K + k) : kOob;
+                av[t] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+            }
         }
-        // The next chunk's loads (past the last chunk they are all out of
-        // range: zero fills of the idle buffer), then wait until only they
-        // are outstanding.  The same instruction sequence every iteration
-        // keeps the compiler from adding waits of its own.
-        issue(kc + 1, (kc + 1) & 1);
-        wait_vmcnt<kPer>();
+        // The next chunk's loads, then wait until only they are outstanding;
+        // after the last chunk, for everything.  (Every wave issues the x
+        // loads: each holds lanes of row 0.)
+        if (kc + 1 < chunks) {
+            issue(kc + 1, (kc + 1) & 1);
+            wait_vmcnt<kPer>();
+        } else {
+            wait_vmcnt<0>();
+        }
         barrier_no_fence();
         const int8_t *buf = smem + (kc & 1) * kBuf;
 #pragma unroll
@@ -1057,7 +1066,6 @@ __global__ __launch_bounds__(256) void skinny_fwd_kernel(const int8_t *__restric
         // of chunk kc + 1 stay in flight.
         barrier_no_fence();
     }
-    wait_vmcnt<0>();    // the zero fills issued by the last iteration
     i32x4 *red = reinterpret_cast<i32x4 *>(smem + 2 * kBuf);
     red[w * kWave + lane] = acc;
     __syncthreads();
