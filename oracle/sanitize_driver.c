@@ -81,7 +81,6 @@ static uint32_t next_u32(void)
     return lcg;
 }
 static float randf(void) { return (float)(int)(next_u32() % 2001u - 1000) * 0.001f; }
-static int8_t randq(void) { return (int8_t)((int)(next_u32() % 255u) - 127); }
 
 static float *rand_f32(size_t n)
 {
