@@ -10,13 +10,20 @@ Reads  OUT_DIR/kt/*kernel_stats.csv      (rocprofv3 --kernel-trace --stats)
        OUT_DIR/write/*counter_collection.csv (rocprofv3 --pmc WRITE_SIZE)
        OUT_DIR/busy/*counter_collection.csv (rocprofv3 --pmc SQ_BUSY_CYCLES
                                     SQ_VALU_MFMA_BUSY_CYCLES), if present
+       OUT_DIR/valu/*counter_collection.csv (rocprofv3 --pmc SQ_INSTS_VALU
+                                    SQ_BUSY_CYCLES SQ_WAVES), if present
+       OUT_DIR/power.txt (amd-smi metric -p -c samples taken while bench.py
+                          ran its step loop), if present
 Writes profiles/kernels_headline_step.txt (per-kernel durations),
        profiles/pmc_traffic.json + profiles/pmc_traffic.txt (HBM bytes per
        launch, scaled by the reading of the calibration copy of 512 MiB) and
        profiles/mfma_busy_clock.txt (per kernel: the shader clock it ran at,
        SQ busy cycles per shader engine over the dispatch's duration, and the
        fraction of those cycles the SIMDs' matrix pipes were busy) and
-       profiles/lds_bank_conflicts.txt (from OUT_DIR/lds, if present).
+       profiles/lds_bank_conflicts.txt (from OUT_DIR/lds, if present),
+       profiles/valu_issue.txt (per kernel: the time its vector instructions
+       alone take to issue, against its duration) and
+       profiles/power_headline_step.txt.
 """
 import csv
 import glob
@@ -104,7 +111,7 @@ def main(out_dir, digest=None):
         f.write("# rocprofv3 --kernel-trace --stats of the headline training step\n")
         f.write("# (12000 tokens, 5376 -> 7168, Hadamard block 128).  Command:\n")
         f.write("#   rocprofv3 --kernel-trace --stats -d OUT/kt -o kt --output-format csv -- "
-                "python bench.py --cpu-tokens 0 --no-mlp\n")
+                "python bench.py --cpu-tokens 0 --step-kernels-only\n")
         f.write(f"# {'kernel':<70} {'calls':>5} {'avg_us':>9} {'pct':>6}\n")
         for s in sorted(stats, key=lambda r: -r["total_ns"]):
             f.write(f"  {s['kernel'][:70]:<70} {s['calls']:>5} {s['avg_ns'] / 1e3:>9.2f} "
@@ -145,9 +152,9 @@ def main(out_dir, digest=None):
     rec = {"source_digest": digest, "calibration_dispatches": cal, "fetch_scale": f_fac,
            "write_scale": w_fac, "kernels": kernels,
            "commands": ["rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o fetch --output-format csv -- "
-                        "python bench.py --steps 2 --warmup 1 --cpu-tokens 0 --no-mlp --copy-calibration",
+                        "python bench.py --steps 2 --warmup 1 --cpu-tokens 0 --step-kernels-only --copy-calibration",
                         "rocprofv3 --pmc WRITE_SIZE -d OUT/write -o write --output-format csv -- "
-                        "python bench.py --steps 2 --warmup 1 --cpu-tokens 0 --no-mlp --copy-calibration"]}
+                        "python bench.py --steps 2 --warmup 1 --cpu-tokens 0 --step-kernels-only --copy-calibration"]}
     with open(os.path.join(PROFILES, "pmc_traffic.json"), "w") as f:
         json.dump(rec, f, indent=1)
     with open(os.path.join(PROFILES, "pmc_traffic.txt"), "w") as f:
@@ -167,7 +174,7 @@ def main(out_dir, digest=None):
         with open(os.path.join(PROFILES, "mfma_busy_clock.txt"), "w") as f:
             f.write("# Shader clock and matrix-pipe occupancy per kernel of the headline step.\n")
             f.write("#   rocprofv3 --pmc SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES -d OUT/busy -o busy "
-                    "--output-format csv -- python bench.py --steps 2 --warmup 1 --cpu-tokens 0 --no-mlp\n")
+                    "--output-format csv -- python bench.py --steps 2 --warmup 1 --cpu-tokens 0 --step-kernels-only\n")
             f.write(f"# clock = SQ_BUSY_CYCLES / {n_se} shader engines / dispatch duration; "
                     f"mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / {n_simd} SIMDs / busy cycles.\n")
             f.write("# Fraction of the 2.4 GHz dense INT8 peak = mfma_busy x clock / 2.4.\n")
@@ -179,6 +186,71 @@ def main(out_dir, digest=None):
         print(open(os.path.join(PROFILES, "mfma_busy_clock.txt")).read())
     if glob.glob(os.path.join(out_dir, "lds", "*counter_collection.csv")):
         lds_summary(out_dir)
+    if glob.glob(os.path.join(out_dir, "valu", "*counter_collection.csv")):
+        valu_summary(out_dir)
+    if os.path.exists(os.path.join(out_dir, "power.txt")):
+        power_summary(out_dir)
+
+
+def valu_summary(out_dir):
+    """profiles/valu_issue.txt: per kernel, the vector instructions issued per
+    dispatch and the time they take to issue at the kernel's own clock (a
+    wave64 VALU instruction occupies its SIMD for 4 cycles), against the
+    dispatch duration: where the two are close, the kernel is bound by its
+    vector instructions as much as by memory."""
+    path = _one(os.path.join(out_dir, "valu", "*counter_collection.csv"))
+    info = list(csv.DictReader(open(_one(os.path.join(out_dir, "valu", "*agent_info.csv")))))
+    gpu = [r for r in info if r["Agent_Type"] == "GPU"][0]
+    n_se, n_simd = int(gpu["Array_Count"]), int(gpu["Simd_Count"])
+    per = {}
+    for r in csv.DictReader(open(path)):
+        d = per.setdefault(int(r["Dispatch_Id"]), {"name": _short(r["Kernel_Name"])})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        d["dur_s"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    by = {}
+    for d in per.values():
+        if d["dur_s"] <= 0 or not d.get("SQ_BUSY_CYCLES") or "SQ_INSTS_VALU" not in d:
+            continue
+        clock = d["SQ_BUSY_CYCLES"] / n_se / d["dur_s"]
+        issue_s = d["SQ_INSTS_VALU"] * 4 / n_simd / clock
+        by.setdefault(d["name"], []).append((d["dur_s"] * 1e6, clock / 1e9, d["SQ_INSTS_VALU"],
+                                             issue_s * 1e6))
+    with open(os.path.join(PROFILES, "valu_issue.txt"), "w") as f:
+        f.write("# Vector-instruction issue time per dispatch of the headline step's kernels.\n")
+        f.write("#   rocprofv3 --pmc SQ_INSTS_VALU SQ_BUSY_CYCLES SQ_WAVES -d OUT/valu -o valu "
+                "--output-format csv -- python bench.py --steps 2 --warmup 1 --cpu-tokens 0 "
+                "--step-kernels-only\n")
+        f.write(f"# valu_us = SQ_INSTS_VALU x 4 cycles / {n_simd} SIMDs / clock, clock = "
+                f"SQ_BUSY_CYCLES / {n_se} shader engines / duration.\n")
+        f.write(f"# {'kernel':<62} {'dur_us':>8} {'clock_GHz':>9} {'valu_insts':>11} "
+                f"{'valu_us':>8} {'ratio':>6}\n")
+        for k, vals in sorted(by.items(), key=lambda kv: -statistics.median(v[0] for v in kv[1])):
+            dur, clk, ins, iss = (statistics.median(v[i] for v in vals) for i in range(4))
+            f.write(f"  {k[:62]:<62} {dur:>8.1f} {clk:>9.3f} {ins:>11.0f} {iss:>8.1f} "
+                    f"{iss / dur:>6.2f}\n")
+    print(open(os.path.join(PROFILES, "valu_issue.txt")).read())
+
+
+def power_summary(out_dir):
+    """profiles/power_headline_step.txt from amd-smi samples taken while
+    bench.py ran its timed steps."""
+    import re
+    text = open(os.path.join(out_dir, "power.txt")).read()
+    rows = []
+    for block in text.split("--- sample")[1:]:
+        p = re.search(r"SOCKET_POWER:\s*(\d+)", block)
+        clocks = [int(c) for c in re.findall(r"GFX_\d+:\s+CLK:\s*(\d+)", block)]
+        if p and clocks:
+            rows.append((int(p.group(1)), min(clocks), max(clocks)))
+    with open(os.path.join(PROFILES, "power_headline_step.txt"), "w") as f:
+        f.write("# Socket power and graphics clocks while the headline step runs back to back.\n")
+        f.write("#   python bench.py --steps 3000 --cpu-tokens 0 --step-kernels-only &  sleep 4;\n")
+        f.write("#   10 x (amd-smi metric -p -c; sleep 0.2)\n")
+        f.write("# The MI355X board power limit is 1400 W.\n")
+        f.write(f"# {'sample':>6} {'socket_W':>9} {'gfx_clk_min_MHz':>16} {'gfx_clk_max_MHz':>16}\n")
+        for i, (pw, lo, hi) in enumerate(rows):
+            f.write(f"  {i + 1:>6} {pw:>9} {lo:>16} {hi:>16}\n")
+    print(open(os.path.join(PROFILES, "power_headline_step.txt")).read())
 
 
 def lds_summary(out_dir):
@@ -195,7 +267,7 @@ def lds_summary(out_dir):
         f.write("# LDS activity per dispatch of the headline step's kernels.\n")
         f.write("#   rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS SQ_WAVES "
                 "-d OUT/lds -o lds --output-format csv -- python bench.py --steps 2 --warmup 1 "
-                "--cpu-tokens 0 --no-mlp\n")
+                "--cpu-tokens 0 --step-kernels-only\n")
         f.write(f"# {'kernel':<70} {'lds_insts':>12} {'conflict_cyc':>12} {'waves':>7}\n")
         for k, d in sorted(vals.items(), key=lambda kv: -statistics.mean(
                 kv[1].get("SQ_INSTS_LDS", [0]))):
