@@ -368,6 +368,55 @@ def mlp_products(torch, reps=10):
     return res
 
 
+def mlp_step(torch, reps=10, warm=3):
+    """One training step of the transformer MLP workload (8192 tokens, fc1
+    4096 -> 14336, exact erf-GELU in fp32, fc2 14336 -> 4096, rotation 128 on
+    both inputs, seeded inputs): both forwards, both backwards with the GELU's
+    derivative in fp32 between them, and both SGD stochastic requants (seeds 0
+    and 1).  Median of `reps` steps, each bracketed by events.  TOPS count the
+    six products (2 M N K each); the GELU and its derivative are part of the
+    step's time."""
+    import math
+
+    import numpy as np
+
+    import workloads
+    from w8a8_integer_linear_amd import LinearW8A8Training
+    d = workloads.mlp()
+    dev = lambda a: (torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+                     if a.dtype == np.uint16 else torch.from_numpy(a).cuda())
+    m, dm, hm = d["x"].shape[0], d["x"].shape[1], d["w1"].shape[0]
+    fc1 = LinearW8A8Training(dev(d["w1"]), had_block=HAD, max_tokens=m)
+    fc2 = LinearW8A8Training(dev(d["w2"]), had_block=HAD, max_tokens=m)
+    x, dy2 = dev(d["x"]), dev(d["dy2"])
+    inv_sqrt2, inv_sqrt2pi = 1.0 / math.sqrt(2.0), 1.0 / math.sqrt(2.0 * math.pi)
+
+    def step(i):
+        h = fc1.forward(x)
+        a = torch.nn.functional.gelu(h)
+        fc2.forward(a)
+        da = fc2.backward(dy2)
+        dh = da * (0.5 * (1.0 + torch.erf(h * inv_sqrt2)) + h * torch.exp(-0.5 * h * h) * inv_sqrt2pi)
+        fc1.backward(dh)
+        fc2.sgd_step(d["lr"], d["seeds"][1], i)
+        fc1.sgd_step(d["lr"], d["seeds"][0], i)
+
+    for i in range(warm):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        step(warm + i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])
+    ops = 6 * 2.0 * m * dm * hm
+    tops = ops / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "tops": round(tops, 1),
+            "frac_mfma": round(tops / PEAK_INT8_TOPS, 4), "shape": [m, dm, hm]}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -538,6 +587,8 @@ def main():
     out["extras"].update(skinny_forward(torch))
     if not (args.no_mlp or args.step_kernels_only):
         out["extras"].update(mlp_products(torch))
+        print("[bench] MLP training step", file=sys.stderr, flush=True)
+        out["extras"]["mlp_step"] = mlp_step(torch)
     if args.cpu_tokens > 0:
         print(f"[bench] cpu baseline on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(d, args.cpu_tokens)
