@@ -134,12 +134,15 @@ def test_quantize_cols(T, Q, orc, rows, cols, bf16, pre):
 
 
 GRAD_CASES = [
-    # rows, cols, bf16: fused pass (rows >= 512, cols <= 8192) and the fallback
+    # rows, cols, bf16: fused pass (rows >= 512, cols <= 16384) and the fallback
     (600, 4096, True),
     (513, 7168, True),         # dY of the headline layer's width, few rows per group
-    (1000, 8192, False),       # widest fused row, fp32 gradient
+    (1000, 8192, False),       # widest row of the 512-thread fused pass, fp32 gradient
     (777, 4112, True),         # ragged last pass of the row workgroup
-    (700, 8208, True),         # wider than the fused pass: separate passes
+    (700, 8208, True),         # narrowest row of the 1024-thread fused pass
+    (600, 14336, False),       # the MLP's fc1 gradient width, fp32
+    (513, 16384, True),        # widest fused row
+    (520, 16400, True),        # wider than the fused pass: separate passes
     (100, 256, False),         # too few rows for the fused pass
 ]
 
@@ -170,7 +173,7 @@ def test_quantize_grad(T, Q, orc, rows, cols, bf16):
 
 def _random_grad_cases(n=8, seed=7303):
     """Seeded random dY shapes for both quantizations: mostly the fused pass
-    (>= 512 rows, <= 8192 columns), some of the separate passes."""
+    (>= 512 rows, <= 16384 columns), some of the separate passes."""
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):

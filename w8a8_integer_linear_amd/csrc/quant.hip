@@ -67,8 +67,9 @@ __global__ __launch_bounds__(THREADS) void quant_rows_kernel(
     int had, float cb, int8_t *__restrict__ q, float *__restrict__ s,
     const float *__restrict__ colpre, float *__restrict__ part)
 {
-    static_assert(!COLS || (HAD == 0 && THREADS == 512 && J <= 2),
-                  "column partials: no rotation, 512 threads, at most 16 columns per lane");
+    static_assert(!COLS || (HAD == 0 && (THREADS == 512 || THREADS == 1024) && J <= 2),
+                  "column partials: no rotation, 512 or 1024 threads, at most 16 columns per "
+                  "lane");
     // 1024-thread workgroups have 128 registers per lane: no room for the
     // prescale or the next row's data, which they load when they need it.
     constexpr bool kKeepPrescale = THREADS <= 256 || COLS;
@@ -451,21 +452,22 @@ __global__ __launch_bounds__(1024) void grad_cols_reduce_kernel(const float *__r
 }
 
 // The fused pass keeps the prescale and two partials per element it owns in
-// registers, so it takes rows of up to 8192 columns (2 chunks per lane at 512
-// threads).
+// registers, so it takes rows of up to 16384 columns: 2 chunks per lane at
+// 512 threads up to 8192 columns, at 1024 threads (one workgroup per compute
+// unit, half as many workgroups) above.
 // Its workgroups write 8 bytes per column of partials into q2, which must
 // therefore hold at least 8 * groups * cols bytes: groups <= rows / 8.
-constexpr int64_t kGradMaxCols = 8192;
+constexpr int64_t kGradMaxCols = 16384;
 constexpr int64_t kGradMinRows = 512;
 constexpr int kGradGroups = 512;
 
-template <bool BF16, int J>
+template <bool BF16, int THREADS, int J>
 static void launch_grad_rows(const void *x, int64_t rows, int64_t cols, const float *sw,
                              const float *sx, int8_t *q1, float *s1, float *part, int groups,
                              hipStream_t st)
 {
-    hipLaunchKernelGGL((quant_rows_kernel<BF16, 512, J, 0, true>), dim3(groups), dim3(512), 0, st,
-                       x, rows, cols, sw, 0, 1.0f, q1, s1, sx, part);
+    hipLaunchKernelGGL((quant_rows_kernel<BF16, THREADS, J, 0, true>), dim3(groups),
+                       dim3(THREADS), 0, st, x, rows, cols, sw, 0, 1.0f, q1, s1, sx, part);
 }
 
 void launch_quantize_grad(const void *x, bool bf16, int64_t rows, int64_t cols, const float *sw,
@@ -478,15 +480,19 @@ void launch_quantize_grad(const void *x, bool bf16, int64_t rows, int64_t cols, 
         launch_quantize_cols(x, bf16, rows, cols, sx, q2, s2, col_sum, st);
         return;
     }
-    const int groups = (int)(rows / 8 < kGradGroups ? rows / 8 : kGradGroups);
+    const bool wide = cols > 8192;
+    const int max_groups = wide ? kGradGroups / 2 : kGradGroups;
+    const int groups = (int)(rows / 8 < max_groups ? rows / 8 : max_groups);
     float *part = reinterpret_cast<float *>(q2);
-    const int64_t j = (cols / 8 + 511) / 512;
+    const int64_t j = (cols / 8 + (wide ? 1023 : 511)) / (wide ? 1024 : 512);
     auto go = [&](auto bf) {
         constexpr bool B = decltype(bf)::value;
-        if (j == 1)
-            launch_grad_rows<B, 1>(x, rows, cols, sw, sx, q1, s1, part, groups, st);
+        if (wide)
+            launch_grad_rows<B, 1024, 2>(x, rows, cols, sw, sx, q1, s1, part, groups, st);
+        else if (j == 1)
+            launch_grad_rows<B, 512, 1>(x, rows, cols, sw, sx, q1, s1, part, groups, st);
         else
-            launch_grad_rows<B, 2>(x, rows, cols, sw, sx, q1, s1, part, groups, st);
+            launch_grad_rows<B, 512, 2>(x, rows, cols, sw, sx, q1, s1, part, groups, st);
     };
     if (bf16)
         go(std::true_type());
