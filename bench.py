@@ -64,9 +64,9 @@ COPY_BYTES = 512 << 20        # calibration copy: reads and writes this many byt
 KERNEL_OF = {"fwd": ["gemm_kernel<2, 4, false, false, 2, 2>"],
              "bwd_dx": ["gemm_kernel<2, 4, false, true, 3, 0>"],
              "bwd_dw": ["gemm_kernel<2, 4, true, true, 1, 2>"],
-             "quantize_x": ["quant_rows_kernel<true, 256, 3, 128, false>"],
-             "quantize_dy": ["quant_rows_kernel<true, 512, 2, 0, true>", "grad_cols_reduce_kernel",
-                             "colquant_kernel<true>"],
+             "quantize_x": ["quant_rows_kernel<true, 256, 3, 128>"],
+             "quantize_dy": ["grad_stats_kernel<true>", "grad_scales_kernel",
+                             "grad_codes_kernel<true>"],
              "sgd_requant": ["sgd_requant_kernel<256, 3, false>"]}
 
 

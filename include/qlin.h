@@ -138,13 +138,15 @@ int qlin_quantize_cols(const void *x, int dtype, int64_t rows, int64_t cols,
 
 /*
  * Both quantizations of the output gradient dY in one call, reading dY twice
- * instead of three times: the row pass of the first also gathers the column
- * maxima and sums of the second (mini_trainer guide: the backward products
- * are integer; the scales of each operand sit on its product's output axis).
+ * instead of three times: a first pass gathers the row maxima of the first,
+ * the column maxima and sums of the second, a second pass writes both code
+ * arrays (mini_trainer guide: the backward products are integer; the scales
+ * of each operand sit on its product's output axis).
  * Results are those of
  *   qlin_quantize_rows(dy, prescale = sw, had_block = 0) -> (q1, s1)   and
  *   qlin_quantize_cols(dy, prescale = sx, col_sum)        -> (q2, s2, col_sum)
- * bit for bit, except col_sum (fp32 sums in an unspecified order).
+ * bit for bit, except col_sum (fp32 sums in an unspecified order; from 16
+ * rows on it is fixed for a given shape, so repeated calls agree bit for bit).
  *
  *   dy       [rows, cols] fp32 or bf16 (rows = tokens, cols = out features).
  *   sw       [cols] fp32, the weight row scales (required).

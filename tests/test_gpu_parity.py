@@ -134,16 +134,18 @@ def test_quantize_cols(T, Q, orc, rows, cols, bf16, pre):
 
 
 GRAD_CASES = [
-    # rows, cols, bf16: fused pass (rows >= 512, cols <= 16384) and the fallback
+    # rows, cols, bf16: the two-read path (rows >= 16) and the separate passes
     (600, 4096, True),
-    (513, 7168, True),         # dY of the headline layer's width, few rows per group
-    (1000, 8192, False),       # widest row of the 512-thread fused pass, fp32 gradient
-    (777, 4112, True),         # ragged last pass of the row workgroup
-    (700, 8208, True),         # narrowest row of the 1024-thread fused pass
+    (513, 7168, True),         # dY of the headline layer's width
+    (1000, 8192, False),       # fp32 gradient
+    (777, 4112, True),         # ragged last 512-column window and row batch
+    (700, 8208, True),
     (600, 14336, False),       # the MLP's fc1 gradient width, fp32
-    (513, 16384, True),        # widest fused row
-    (520, 16400, True),        # wider than the fused pass: separate passes
-    (100, 256, False),         # too few rows for the fused pass
+    (520, 16400, True),        # more windows than the waves' budget fills
+    (100, 256, False),         # one window, half of it past the last column
+    (16, 1040, True),          # fewest rows of the two-read path: one row group
+    (15, 4096, True),          # too few rows: separate passes
+    (1, 272, False),
 ]
 
 
@@ -172,12 +174,12 @@ def test_quantize_grad(T, Q, orc, rows, cols, bf16):
 
 
 def _random_grad_cases(n=8, seed=7303):
-    """Seeded random dY shapes for both quantizations: mostly the fused pass
-    (>= 512 rows, <= 16384 columns), some of the separate passes."""
+    """Seeded random dY shapes for both quantizations: mostly the two-read
+    path (>= 16 rows), some of the separate passes."""
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
-        rows = int(rng.integers(512, 5000)) if i % 4 else int(rng.integers(1, 512))
+        rows = int(rng.integers(16, 5000)) if i % 4 else int(rng.integers(1, 16))
         cols = 16 * int(rng.integers(1, 513 if i % 3 else 1024))
         cases.append((i, rows, cols, bool(rng.integers(0, 2))))
     return cases
@@ -201,6 +203,31 @@ def test_quantize_grad_random(T, Q, orc, i, rows, cols, bf16):
     xf = workloads.bf16_bits_to_f32(x) if bf16 else x
     bound = 1e-5 * np.abs(xf.astype(np.float64)).sum(axis=0) + 1e-30
     assert np.all(np.abs(host(db).astype(np.float64) - dbr) <= bound)
+
+
+def test_quantize_grad_tiny_scales(T, Q, orc):
+    """Zero, subnormal and normal row and column scales in one call: the code
+    pass's exact quotients for subnormal scales, fast path elsewhere."""
+    rows, cols = 64, 1024
+    rng = np.random.default_rng(77)
+    x = rng.standard_normal((rows, cols), dtype=np.float32)
+    x[:32] *= np.float32(1e-36)                   # rows whose scales are subnormal
+    x[:, :128] *= np.float32(1e-36)               # columns whose scales are subnormal
+    x[40] = 0                                     # a zero row scale
+    x[:, 200] = 0                                 # a zero column scale
+    sw = rng.uniform(1e-3, 1e-2, cols).astype(np.float32)
+    sx = rng.uniform(1e-3, 1e-1, rows).astype(np.float32)
+    announce("quantize_grad tiny scales", rows, cols)
+    q1, s1, q2, s2, db = Q.qlin_quantize_grad(dev(x), dev(sw), dev(sx), want_sum=True)
+    T.cuda.synchronize()
+    q1r, s1r = orc.quantize_rows(x, prescale=sw)
+    q2r, s2r, _ = orc.quantize_cols(x, prescale=sx, want_sum=True)
+    assert np.any((s1r > 0) & (s1r < np.float32(2.0 ** -126)))
+    assert np.any((s2r > 0) & (s2r < np.float32(2.0 ** -126)))
+    assert_bitwise(host(s1), s1r, "row scales")
+    assert_bitwise(host(q1), q1r, "row codes")
+    assert_bitwise(host(s2), s2r, "column scales")
+    assert_bitwise(host(q2), q2r, "column codes")
 
 
 def test_quantize_grad_no_tokens(T, Q, orc):

@@ -222,11 +222,22 @@ __device__ __forceinline__ void fwht8_fixed(float v[8], float cb)
         v[i] = v[i] * scale;
 }
 
+// 1 / s for a normal s whose reciprocal is normal, within half an ulp plus a
+// relative 2^-46: the hardware reciprocal (within 1 ulp) refined by one Newton
+// step, three instructions against about twelve for a correctly rounded
+// division.
+__device__ __forceinline__ float recip_refined(float s)
+{
+    const float r = __builtin_amdgcn_rcpf(s);
+    return __builtin_fmaf(r, __builtin_fmaf(-s, r, 1.0f), r);
+}
+
 // Eight INT8 codes rne(fl(g / s)) packed into two dwords, for a scale s > 0
-// that is a normal number, with inv = fl(1 / s).  Fast path: t = fl(g * inv)
-// is within 2^-15 of fl(g / s) for |g| <= 127.01 s, so both round to the same
-// integer unless t lies within 2^-14 of a half-integer; if any of the eight
-// does, all eight take the exact quotient.  Rounding to an integer is done by
+// that is a normal number, with inv = fl(1 / s) or recip_refined(s) (either
+// is within 2^-24 (1 + 2^-22) of 1 / s, relatively).  Fast path: t =
+// fl(g * inv) is then within 2^-15 of fl(g / s) for |g| <= 127.01 s, so both
+// round to the same integer unless t lies within 2^-14 of a half-integer; if
+// any of the eight does, all eight take the exact quotient.  Rounding to an integer is done by
 // adding 1.5 * 2^23 (round to nearest even in the addition), which also leaves
 // the code as the low byte of the sum's bits.  The quotient is at most
 // 127 (1 + 2^-22) < 127.5 in magnitude, so no clamp is needed.

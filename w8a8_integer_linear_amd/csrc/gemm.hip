@@ -420,7 +420,7 @@ __device__ __forceinline__ int stage_slot(int row, int chunk)
 // columns of each 2 CW-column block): every value v and its partner value w
 // become fl(fl(v + w) * had_scale) in the lower wave of the pair and
 // fl(fl(w - v) * had_scale) in the upper one.
-template <int CW, bool PAIR = false>
+template <int CW, bool PAIR = false, bool NTS = false>
 __device__ __forceinline__ void store_pass(const GemmParams &p, const lds_i8 *stage, int i, int j,
                                            const lds_i8 *partner = nullptr, bool upper = false)
 {
@@ -467,8 +467,12 @@ __device__ __forceinline__ void store_pass(const GemmParams &p, const lds_i8 *st
                     t[k][e] = __float_as_uint(__builtin_fmaf(sign, v, x) * p.had_scale);
                 }
             }
-            if (col_ok && i + (k0 + k) * kRowsPer + r0 < p.R)
-                *reinterpret_cast<u32x4 *>(dst) = t[k];
+            if (col_ok && i + (k0 + k) * kRowsPer + r0 < p.R) {
+                if constexpr (NTS)
+                    __builtin_nontemporal_store(t[k], reinterpret_cast<u32x4 *>(dst));
+                else
+                    *reinterpret_cast<u32x4 *>(dst) = t[k];
+            }
             dst += step;
         }
     }
@@ -933,7 +937,14 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
     };
 
     // Stores pass through the wave's 16 KiB slice of the idle stage buffers
-    // (see store_pass), kPassRows rows at a time.
+    // (see store_pass), kPassRows rows at a time.  The forward and dX outputs
+    // are stored non-temporally: nothing in a training step reads them again
+    // soon, and stored through the 256 MB infinity cache they leave it full of
+    // dirty lines that the next kernels' reads must first write back (the dY
+    // statistics after the forward product, dW's operands after dX).  dW
+    // stays cached: the weight update reads it next.
+    constexpr bool kStream = EPI == EPI_FWD || EPI == EPI_ROWSCALE_HAD ||
+                             (EPI == EPI_ROWSCALE && !AKM);
     constexpr int kPassRows = 4096 / CW;
     constexpr int kPassBlocks = kPassRows / 16;
     static_assert(FM % kPassBlocks == 0 && 2 * kStage >= NT / kWave * 4096 * 4, "staging shape");
@@ -961,10 +972,11 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
             // barriers carry no fence, so the output stores stay in flight.
             wait_lgkmcnt0();
             barrier_no_fence();
-            store_pass<CW, true>(p, stage_base, i, j, (lds_i8 *)smem + (w ^ 1) * 4096 * 4, wj & 1);
+            store_pass<CW, true, kStream>(p, stage_base, i, j, (lds_i8 *)smem + (w ^ 1) * 4096 * 4,
+                                          wj & 1);
             barrier_no_fence();
         } else {
-            store_pass<CW>(p, stage_base, i, j);
+            store_pass<CW, false, kStream>(p, stage_base, i, j);
         }
     }
 }

@@ -12,9 +12,9 @@
 // product's output axis): pass 1 reduces |x * prescale[r]| over row slabs and
 // merges slabs with an order-free integer atomicMax on the fp32 bits of the
 // non-negative maxima; a tiny kernel turns maxima into scales; pass 2
-// quantizes elementwise.  Both quantizations of dY in one call share the read
-// of pass 1 with the row quantizer (column partials per workgroup, then a
-// reduce).
+// quantizes elementwise.  Both quantizations of dY in one call read it twice:
+// once for the statistics of both (row and column maxima, column sums), once
+// for both code arrays.
 //
 // Also here: the standalone rotation and the weight export (dequantize and
 // rotate back).
@@ -56,24 +56,15 @@ __device__ __forceinline__ int64_t lane_chunk(int64_t c)
 // end are clamped to its last chunk and the values dropped) so that they all
 // issue back to back.  The per-column prescale of the thread's chunks is
 // loaded into registers once and reused for every row.
-//
-// COLS (no rotation, 256 threads) also gathers, over the workgroup's rows, the
-// column maxima of |x * colpre[row]| and the column sums of the raw x, and
-// writes them to part[2 * blockIdx.x][cols] and part[2 * blockIdx.x + 1][cols]
-// at the end: one read of dY serves both of its quantizations.
-template <bool BF16, int THREADS, int J, int HAD, bool COLS>
+template <bool BF16, int THREADS, int J, int HAD>
 __global__ __launch_bounds__(THREADS) void quant_rows_kernel(
     const void *__restrict__ x, int64_t rows, int64_t cols, const float *__restrict__ prescale,
-    int had, float cb, int8_t *__restrict__ q, float *__restrict__ s,
-    const float *__restrict__ colpre, float *__restrict__ part)
+    int had, float cb, int8_t *__restrict__ q, float *__restrict__ s)
 {
-    static_assert(!COLS || (HAD == 0 && (THREADS == 512 || THREADS == 1024) && J <= 2),
-                  "column partials: no rotation, 512 or 1024 threads, at most 16 columns per "
-                  "lane");
     // 1024-thread workgroups have 128 registers per lane: no room for the
     // prescale or the next row's data, which they load when they need it.
-    constexpr bool kKeepPrescale = THREADS <= 256 || COLS;
-    constexpr bool kPrefetch = THREADS <= 256 || COLS;
+    constexpr bool kKeepPrescale = THREADS <= 256;
+    constexpr bool kPrefetch = THREADS <= 256;
     __shared__ float red[THREADS / kWave];
     const int t = threadIdx.x;
     const int64_t nch = cols / 8;
@@ -89,16 +80,6 @@ __global__ __launch_bounds__(THREADS) void quant_rows_kernel(
 #pragma unroll
         for (int j = 0; j < J; j++)
             load8<false>(prescale, chunk(j) * 8, p[kKeepPrescale ? j : 0]);
-    }
-    float cmax[COLS ? J : 1][8], csum[COLS ? J : 1][8];
-    if constexpr (COLS) {
-#pragma unroll
-        for (int j = 0; j < J; j++)
-#pragma unroll
-            for (int e = 0; e < 8; e++) {
-                cmax[j][e] = 0.0f;
-                csum[j][e] = 0.0f;
-            }
     }
     Raw8<BF16> cur[J];
     int64_t row = blockIdx.x;
@@ -120,17 +101,6 @@ __global__ __launch_bounds__(THREADS) void quant_rows_kernel(
         for (int j = 0; j < J; j++) {
             const bool ok = t + (int64_t)j * THREADS < nch;
             unpack8<BF16>(cur[j], v[j]);
-            if constexpr (COLS) {
-                if (ok) {
-                    const float cp = colpre ? colpre[row] : 1.0f;
-#pragma unroll
-                    for (int e = 0; e < 8; e++) {
-                        csum[COLS ? j : 0][e] = csum[COLS ? j : 0][e] + v[j][e];
-                        const float g = colpre ? v[j][e] * cp : v[j][e];
-                        cmax[COLS ? j : 0][e] = fmaxf(cmax[COLS ? j : 0][e], __builtin_fabsf(g));
-                    }
-                }
-            }
             // Chunk index c is the same function of the lane in every pass, so
             // lanes of one block stay together; a block is all valid or all
             // clamped because had divides cols.
@@ -184,16 +154,6 @@ __global__ __launch_bounds__(THREADS) void quant_rows_kernel(
         for (int j = 0; j < J; j++)
             cur[j] = kPrefetch ? nxt[kPrefetch ? j : 0] : load_raw8<BF16>(x, next * cols + chunk(j) * 8);
     }
-    if constexpr (COLS) {
-#pragma unroll
-        for (int j = 0; j < J; j++) {
-            const int64_t c = t + (int64_t)j * THREADS;
-            if (c < nch) {
-                store8(part + (2 * (int64_t)blockIdx.x) * cols, c * 8, cmax[j]);
-                store8(part + (2 * (int64_t)blockIdx.x + 1) * cols, c * 8, csum[j]);
-            }
-        }
-    }
 }
 
 // Workgroups per launch: enough to fill the GPU several times over; each
@@ -205,9 +165,8 @@ static void launch_rows_t(const void *x, int64_t rows, int64_t cols, const float
                           int had, float cb, int8_t *q, float *s, hipStream_t st)
 {
     const unsigned grid = (unsigned)(rows < kRowGrid ? rows : kRowGrid);
-    hipLaunchKernelGGL((quant_rows_kernel<BF16, THREADS, J, HAD, false>), dim3(grid),
-                       dim3(THREADS), 0, st, x, rows, cols, prescale, had, cb, q, s, nullptr,
-                       nullptr);
+    hipLaunchKernelGGL((quant_rows_kernel<BF16, THREADS, J, HAD>), dim3(grid), dim3(THREADS), 0,
+                       st, x, rows, cols, prescale, had, cb, q, s);
 }
 
 template <bool BF16, int HAD>
@@ -415,16 +374,151 @@ void launch_quantize_cols(const void *x, bool bf16, int64_t rows, int64_t cols,
 }
 
 // ------------------------------------------------ both dY quantizations
+//
+// Two reads of dY.  Pass 1 (grad_stats_kernel) reads it for the statistics
+// of both quantizations: for each row, the maximum of |dY[r, c] * sw[c]| over
+// each window of kStatCols columns, and for each column, the maximum of
+// |dY[r, c] * sx[r]| and the sum of dY[r, c] over each group of rows.
+// grad_scales_kernel reduces these partials into s1, s2 and the column sums
+// (maxima are exact in any order; the sums run in a fixed order, so the
+// result does not vary from run to run).  Pass 2 (grad_codes_kernel) reads dY
+// again and writes both code arrays.  No kernel holds a whole row, so every
+// width takes this path; the partials live in q2 until pass 2 overwrites it.
+constexpr int kStatCols = 512;
+constexpr int kStatBatch = 8;    // rows a lane loads before using any of them
+constexpr int kStatWaves = 4096; // waves of pass 1 (row groups x column windows)
+constexpr int kCodeRows = 16;    // rows per thread in pass 2
 
-// Partials from the fused row pass -> column scales s = fl(max / 127) and
-// column sums.  A workgroup owns 64 columns; its 16 waves take every 16th
-// workgroup partial and are combined through LDS (the maximum is exact in any
-// order; the sums run in a fixed order, so the result is deterministic).
-__global__ __launch_bounds__(1024) void grad_cols_reduce_kernel(const float *__restrict__ part,
-                                                                int groups, int64_t cols,
-                                                                float *__restrict__ s,
-                                                                float *__restrict__ col_sum)
+// Maximum over the wave of each of kStatBatch values, left in lane 63: per
+// step, one v_max_f32 whose first source is read through DPP.  The quad
+// permutes and the half-row and row mirrors give every lane its 16-lane row's
+// maximum, then row_bcast:15 (into rows 1 and 3) and row_bcast:31 (into rows
+// 2 and 3) carry it up; the rows a step does not write keep their values.  As
+// asm because the compiler does not fold a DPP move into the maximum.  The
+// s_nop covers the two wait states a DPP read needs after a VALU write of its
+// source; inside a step each instruction writes only its own register, which
+// the next step reads eight instructions later.
+#define QLIN_MAX_DPP_STEP(V, CTRL)                                                               \
+    asm("s_nop 1\n\t"                                                                           \
+        "v_max_f32_dpp %0, %0, %0 " CTRL " bank_mask:0xf\n\t"                                   \
+        "v_max_f32_dpp %1, %1, %1 " CTRL " bank_mask:0xf\n\t"                                   \
+        "v_max_f32_dpp %2, %2, %2 " CTRL " bank_mask:0xf\n\t"                                   \
+        "v_max_f32_dpp %3, %3, %3 " CTRL " bank_mask:0xf\n\t"                                   \
+        "v_max_f32_dpp %4, %4, %4 " CTRL " bank_mask:0xf\n\t"                                   \
+        "v_max_f32_dpp %5, %5, %5 " CTRL " bank_mask:0xf\n\t"                                   \
+        "v_max_f32_dpp %6, %6, %6 " CTRL " bank_mask:0xf\n\t"                                   \
+        "v_max_f32_dpp %7, %7, %7 " CTRL " bank_mask:0xf"                                       \
+        : "+v"(V[0]), "+v"(V[1]), "+v"(V[2]), "+v"(V[3]), "+v"(V[4]), "+v"(V[5]), "+v"(V[6]),    \
+          "+v"(V[7]))
+
+static_assert(kStatBatch == 8, "the DPP maximum steps take eight values");
+
+__device__ __forceinline__ void wave_max8_to_last(float v[8])
 {
+    QLIN_MAX_DPP_STEP(v, "quad_perm:[1,0,3,2] row_mask:0xf");
+    QLIN_MAX_DPP_STEP(v, "quad_perm:[2,3,0,1] row_mask:0xf");
+    QLIN_MAX_DPP_STEP(v, "row_half_mirror row_mask:0xf");
+    QLIN_MAX_DPP_STEP(v, "row_mirror row_mask:0xf");
+    QLIN_MAX_DPP_STEP(v, "row_bcast:15 row_mask:0xa");
+    QLIN_MAX_DPP_STEP(v, "row_bcast:31 row_mask:0xc");
+}
+
+#undef QLIN_MAX_DPP_STEP
+
+// rowpart[win][rows]: row maxima over the 512-column window win;
+// colpart[2 g][cols] and colpart[2 g + 1][cols]: column maxima and sums over
+// the rows of row group g = blockIdx.y.  Each wave owns one window (the four
+// waves of a workgroup sit side by side) and walks its group's batches of
+// kStatBatch rows, which interleave with the other groups' (grid-stride), so
+// that at any time the whole grid reads a compact band of rows: spread over
+// the whole array, the same reads ran at half the bandwidth.
+template <bool BF16>
+__global__ __launch_bounds__(256) void grad_stats_kernel(const void *__restrict__ x, int64_t rows,
+                                                         int64_t cols, const float *__restrict__ sw,
+                                                         const float *__restrict__ sx,
+                                                         float *__restrict__ rowpart,
+                                                         float *__restrict__ colpart)
+{
+    const int lc = threadIdx.x % kWave;
+    const int64_t win =
+        (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    if (win * kStatCols >= cols)
+        return;
+    const int64_t c0 = win * kStatCols + lc * 8;
+    const bool cok = c0 < cols;      // then all eight columns are (cols % 16 == 0)
+    // Lanes past the last column read the last chunk (so that every load is
+    // unconditional): their weight scales are zero and their column partials
+    // are not written.  Rows past the end read the last row and are skipped.
+    const int64_t cl = cok ? c0 : cols - 8;
+    float w[8], mx[8], sm[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        w[e] = cok ? sw[c0 + e] : 0.0f;
+        mx[e] = 0.0f;
+        sm[e] = 0.0f;
+    }
+    float *rp = rowpart + win * rows;
+    const int64_t step = (int64_t)gridDim.y * kStatBatch;
+    for (int64_t rb = (int64_t)blockIdx.y * kStatBatch; rb < rows; rb += step) {
+        Raw8<BF16> raw[kStatBatch];
+        float px[kStatBatch];
+#pragma unroll
+        for (int u = 0; u < kStatBatch; u++) {
+            const int64_t r = rb + u < rows ? rb + u : rows - 1;
+            raw[u] = load_raw8<BF16>(x, r * cols + cl);
+            px[u] = sx[r];
+        }
+        float rm[kStatBatch];
+#pragma unroll
+        for (int u = 0; u < kStatBatch; u++) {
+            float v[8];
+            unpack8<BF16>(raw[u], v);
+            float m = 0.0f;
+            if (rb + u < rows) {
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    sm[e] = sm[e] + v[e];
+                    mx[e] = fmaxf(mx[e], __builtin_fabsf(v[e] * px[u]));
+                    m = fmaxf(m, __builtin_fabsf(v[e] * w[e]));
+                }
+            }
+            rm[u] = m;
+        }
+        wave_max8_to_last(rm);
+        if (lc == kWave - 1) {
+#pragma unroll
+            for (int u = 0; u < kStatBatch; u++)
+                if (rb + u < rows)
+                    rp[rb + u] = rm[u];
+        }
+    }
+    if (cok) {
+        float *cm = colpart + 2 * (int64_t)blockIdx.y * cols;
+        store8(cm, c0, mx);
+        store8(cm + cols, c0, sm);
+    }
+}
+
+// Partials -> s1 = fl(row max / 127), s2 = fl(column max / 127) and the column
+// sums.  The first ceil(cols / 64) workgroups own 64 columns each: their 16
+// waves take every 16th row group and are combined through LDS in a fixed
+// order.  The workgroups after them own 1024 rows each.
+__global__ __launch_bounds__(1024) void grad_scales_kernel(
+    const float *__restrict__ rowpart, int wins, const float *__restrict__ colpart, int groups,
+    int64_t rows, int64_t cols, float *__restrict__ s1, float *__restrict__ s2,
+    float *__restrict__ col_sum)
+{
+    const int64_t cblocks = (cols + 63) / 64;
+    if ((int64_t)blockIdx.x >= cblocks) {
+        const int64_t r = ((int64_t)blockIdx.x - cblocks) * 1024 + threadIdx.x;
+        if (r < rows) {
+            float m = 0.0f;
+            for (int k = 0; k < wins; k++)
+                m = fmaxf(m, rowpart[k * rows + r]);
+            s1[r] = m / 127.0f;
+        }
+        return;
+    }
     __shared__ float red_max[16][64], red_sum[16][64];
     const int lc = threadIdx.x % 64, sl = threadIdx.x / 64;
     const int64_t c = (int64_t)blockIdx.x * 64 + lc;
@@ -432,8 +526,8 @@ __global__ __launch_bounds__(1024) void grad_cols_reduce_kernel(const float *__r
     if (c < cols) {
 #pragma unroll 4
         for (int g = sl; g < groups; g += 16) {
-            m = fmaxf(m, part[(2 * (int64_t)g) * cols + c]);
-            sum = sum + part[(2 * (int64_t)g + 1) * cols + c];
+            m = fmaxf(m, colpart[(2 * (int64_t)g) * cols + c]);
+            sum = sum + colpart[(2 * (int64_t)g + 1) * cols + c];
         }
     }
     red_max[sl][lc] = m;
@@ -445,67 +539,144 @@ __global__ __launch_bounds__(1024) void grad_cols_reduce_kernel(const float *__r
             m = fmaxf(m, red_max[i][lc]);
             sum = sum + red_sum[i][lc];
         }
-        s[c] = m / 127.0f;
+        s2[c] = m / 127.0f;
         if (col_sum)
             col_sum[c] = sum;
     }
 }
 
-// The fused pass keeps the prescale and two partials per element it owns in
-// registers, so it takes rows of up to 16384 columns: 2 chunks per lane at
-// 512 threads up to 8192 columns, at 1024 threads (one workgroup per compute
-// unit, half as many workgroups) above.
-// Its workgroups write 8 bytes per column of partials into q2, which must
-// therefore hold at least 8 * groups * cols bytes: groups <= rows / 8.
-constexpr int64_t kGradMaxCols = 16384;
-constexpr int64_t kGradMinRows = 512;
-constexpr int kGradGroups = 512;
-
-template <bool BF16, int THREADS, int J>
-static void launch_grad_rows(const void *x, int64_t rows, int64_t cols, const float *sw,
-                             const float *sx, int8_t *q1, float *s1, float *part, int groups,
-                             hipStream_t st)
+// Eight codes rne(fl(g[e] / s[e])) with a scale per element, each s[e] > 0
+// normal and inv[e] as quant8 takes it: the fast path and tie check of
+// quant8, element by element.
+__device__ __forceinline__ i32x2 quant8_each(const float g[8], const float s[8],
+                                             const float inv[8])
 {
-    hipLaunchKernelGGL((quant_rows_kernel<BF16, THREADS, J, 0, true>), dim3(groups),
-                       dim3(THREADS), 0, st, x, rows, cols, sw, 0, 1.0f, q1, s1, sx, part);
+    constexpr float kMagic = 0x1.8p23f;
+    float f[8];
+    float dmax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        const float t = g[e] * inv[e];
+        f[e] = t + kMagic;
+        dmax = fmaxf(dmax, __builtin_fabsf(t - (f[e] - kMagic)));
+    }
+    if (!(dmax < 0.5f - 0x1p-14f)) {
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            f[e] = __builtin_rintf(g[e] / s[e]) + kMagic;
+    }
+    auto pack = [&](int o) {
+        const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(f[o + 1]), __float_as_uint(f[o]),
+                                                  0x0C0C0400u);
+        const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(f[o + 3]),
+                                                  __float_as_uint(f[o + 2]), 0x04000C0Cu);
+        return (int)(lo | hi);
+    };
+    return i32x2{pack(0), pack(4)};
+}
+
+// Pass 2: each thread owns 8 columns (their weight scales, column scales and
+// reciprocals stay in registers) and walks kCodeRows rows, writing the row
+// codes rne(fl(fl(dY * sw) / s1[r])) to q1 and the column codes
+// rne(fl(fl(dY * sx[r]) / s2[c])) to q2.  A zero scale gives zero codes; a
+// subnormal one (its reciprocal loses precision) the exact quotient.
+template <bool BF16>
+__global__ __launch_bounds__(256) void grad_codes_kernel(
+    const void *__restrict__ x, int64_t rows, int64_t cols, const float *__restrict__ sw,
+    const float *__restrict__ sx, const float *__restrict__ s1, const float *__restrict__ s2,
+    int8_t *__restrict__ q1, int8_t *__restrict__ q2)
+{
+    const int64_t nch = cols / 8;
+    const int64_t ch = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (ch >= nch)
+        return;
+    const int64_t c0 = ch * 8;
+    float w[8], sc[8], inv[8];
+    bool cexact = false;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        w[e] = sw[c0 + e];
+        sc[e] = s2[c0 + e];
+        inv[e] = recip_refined(sc[e]);     // unused for a zero or subnormal scale
+        cexact |= sc[e] < 0x1p-126f;
+    }
+    const int64_t r0 = (int64_t)blockIdx.y * kCodeRows;
+    const int64_t r1 = r0 + kCodeRows < rows ? r0 + kCodeRows : rows;
+    for (int64_t r = r0; r < r1; r++) {
+        float v[8], g[8];
+        load8<BF16>(x, r * cols + c0, v);
+        const float sr = s1[r];
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            g[e] = v[e] * w[e];
+        i32x2 o;
+        if (sr == 0.0f) {
+            o = i32x2{0, 0};
+        } else if (sr < 0x1p-126f) {
+            float c[8];
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                c[e] = quant_code_exact(g[e], sr);
+            o[0] = (int)pack4(c[0], c[1], c[2], c[3]);
+            o[1] = (int)pack4(c[4], c[5], c[6], c[7]);
+        } else {
+            o = quant8(g, sr, recip_refined(sr));
+        }
+        *reinterpret_cast<i32x2 *>(q1 + r * cols + c0) = o;
+        const float p = sx[r];
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            g[e] = v[e] * p;
+        if (!cexact) {
+            o = quant8_each(g, sc, inv);
+        } else {
+            float c[8];
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                c[e] = sc[e] == 0.0f ? 0.0f : quant_code_exact(g[e], sc[e]);
+            o[0] = (int)pack4(c[0], c[1], c[2], c[3]);
+            o[1] = (int)pack4(c[4], c[5], c[6], c[7]);
+        }
+        *reinterpret_cast<i32x2 *>(q2 + r * cols + c0) = o;
+    }
 }
 
 void launch_quantize_grad(const void *x, bool bf16, int64_t rows, int64_t cols, const float *sw,
                           const float *sx, int8_t *q1, float *s1, int8_t *q2, float *s2,
                           float *col_sum, hipStream_t st)
 {
-    if (cols > kGradMaxCols || rows < kGradMinRows) {
+    // Row groups: about kStatWaves waves in all, at most one per 16 rows, so
+    // that the partials (4 bytes per row per column window, 8 per column per
+    // group) fit in q2 from 16 rows on.  Fewer rows, or none, take the two
+    // quantizers separately.
+    const int64_t wins = (cols + kStatCols - 1) / kStatCols;
+    int64_t groups = kStatWaves / wins;
+    groups = groups < rows / 16 ? groups : rows / 16;
+    if (rows == 0 || groups < 1 || 4 * (wins * rows + 2 * groups * cols) > rows * cols) {
         if (rows > 0)
             launch_quantize_rows(x, bf16, rows, cols, sw, 0, 1.0f, q1, s1, st);
         launch_quantize_cols(x, bf16, rows, cols, sx, q2, s2, col_sum, st);
         return;
     }
-    const bool wide = cols > 8192;
-    const int max_groups = wide ? kGradGroups / 2 : kGradGroups;
-    const int groups = (int)(rows / 8 < max_groups ? rows / 8 : max_groups);
-    float *part = reinterpret_cast<float *>(q2);
-    const int64_t j = (cols / 8 + (wide ? 1023 : 511)) / (wide ? 1024 : 512);
-    auto go = [&](auto bf) {
-        constexpr bool B = decltype(bf)::value;
-        if (wide)
-            launch_grad_rows<B, 1024, 2>(x, rows, cols, sw, sx, q1, s1, part, groups, st);
-        else if (j == 1)
-            launch_grad_rows<B, 512, 1>(x, rows, cols, sw, sx, q1, s1, part, groups, st);
-        else
-            launch_grad_rows<B, 512, 2>(x, rows, cols, sw, sx, q1, s1, part, groups, st);
-    };
+    float *rowpart = reinterpret_cast<float *>(q2);
+    float *colpart = rowpart + wins * rows;
+    const dim3 g1((unsigned)((wins + 3) / 4), (unsigned)groups);
     if (bf16)
-        go(std::true_type());
+        hipLaunchKernelGGL(grad_stats_kernel<true>, g1, dim3(256), 0, st, x, rows, cols, sw, sx,
+                           rowpart, colpart);
     else
-        go(std::false_type());
-    hipLaunchKernelGGL(grad_cols_reduce_kernel, dim3((unsigned)((cols + 63) / 64)), dim3(1024), 0,
-                       st, part, groups, cols, s2, col_sum);
-    dim3 g2((unsigned)((cols / 8 + 255) / 256), (unsigned)((rows + kColRows - 1) / kColRows));
+        hipLaunchKernelGGL(grad_stats_kernel<false>, g1, dim3(256), 0, st, x, rows, cols, sw, sx,
+                           rowpart, colpart);
+    const unsigned gs = (unsigned)((cols + 63) / 64 + (rows + 1023) / 1024);
+    hipLaunchKernelGGL(grad_scales_kernel, dim3(gs), dim3(1024), 0, st, rowpart, (int)wins,
+                       colpart, (int)groups, rows, cols, s1, s2, col_sum);
+    const dim3 g2((unsigned)((cols / 8 + 255) / 256), (unsigned)((rows + kCodeRows - 1) / kCodeRows));
     if (bf16)
-        hipLaunchKernelGGL(colquant_kernel<true>, g2, dim3(256), 0, st, x, rows, cols, sx, s2, q2);
+        hipLaunchKernelGGL(grad_codes_kernel<true>, g2, dim3(256), 0, st, x, rows, cols, sw, sx,
+                           s1, s2, q1, q2);
     else
-        hipLaunchKernelGGL(colquant_kernel<false>, g2, dim3(256), 0, st, x, rows, cols, sx, s2,
-                           q2);
+        hipLaunchKernelGGL(grad_codes_kernel<false>, g2, dim3(256), 0, st, x, rows, cols, sw, sx,
+                           s1, s2, q1, q2);
 }
 
 // --------------------------------------------------------------- rotation
