@@ -50,6 +50,9 @@ ROW_CASES = [
     (4200, 20480, 0, False, True),     # grid-strided 1024-thread path
     (33, 1088, 64, True, True),        # fixed 64-block rotation, ragged pass
     (9, 384, 128, False, True),        # one partial 256-thread pass, 3 blocks
+    (2, 5376, 128, True, False),       # two rows, fewer than the workgroups
+    (33, 2560, 0, False, True),        # second pass 25% full
+    (64, 768, 128, True, True),        # one pass 37.5% full, 6 blocks
 ]
 
 
@@ -144,6 +147,8 @@ GRAD_CASES = [
     (520, 16400, True),        # more windows than the waves' budget fills
     (100, 256, False),         # one window, half of it past the last column
     (16, 1040, True),          # fewest rows of the two-read path: one row group
+    (20, 131072, True),        # longest row: 256 windows
+    (40, 131056, False),       # longest ragged row
     (15, 4096, True),          # too few rows: separate passes
     (1, 272, False),
 ]
