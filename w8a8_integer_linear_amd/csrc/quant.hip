@@ -429,9 +429,9 @@ __device__ __forceinline__ void wave_max8_to_last(float v[8])
 // colpart[2 g][cols] and colpart[2 g + 1][cols]: column maxima and sums over
 // the rows of row group g = blockIdx.y.  Each wave owns one window (the four
 // waves of a workgroup sit side by side) and walks its group's batches of
-// kStatBatch rows, which interleave with the other groups' (grid-stride), so
-// that at any time the whole grid reads a compact band of rows: spread over
-// the whole array, the same reads ran at half the bandwidth.
+// kStatBatch rows, which interleave with the other groups' (grid-stride).
+// Slabs of consecutive rows per workgroup, or waves stacked in rows, ran at
+// the same speed.
 template <bool BF16>
 __global__ __launch_bounds__(256) void grad_stats_kernel(const void *__restrict__ x, int64_t rows,
                                                          int64_t cols, const float *__restrict__ sw,
