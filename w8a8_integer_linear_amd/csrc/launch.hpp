@@ -17,7 +17,7 @@ void launch_quantize_cols(const void *x, bool bf16, int64_t rows, int64_t cols,
 
 // Both quantizations of the output gradient: rows of x * sw -> (q1, s1),
 // columns of x * sx -> (q2, s2) and the column sums of x.  q2 serves as
-// scratch for column partials before its codes are written.
+// scratch for the row and column partials before its codes are written.
 void launch_quantize_grad(const void *x, bool bf16, int64_t rows, int64_t cols, const float *sw,
                           const float *sx, int8_t *q1, float *s1, int8_t *q2, float *s2,
                           float *col_sum, hipStream_t st);
