@@ -432,6 +432,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before the steps, run a plain device copy of 512 MiB (three times) "
                          "whose counter readings calibrate HBM byte counters")
+    ap.add_argument("--mfma-ceiling-seconds", type=float, default=0.0,
+                    help="only run the matrix-core ceiling kernel back to back for this many "
+                         "seconds (for power sampling) and print its JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer's data-"
@@ -447,6 +450,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.mfma_ceiling_seconds > 0:
+        print(json.dumps({"mfma_ceiling": mfma_ceiling(torch, warm_s=args.mfma_ceiling_seconds)}),
+              flush=True)
+        return
 
     print(f"[bench] generating inputs {M}x{K}->{N}", file=sys.stderr, flush=True)
     d = workloads.linear(M, K, N, seed=SEED)
@@ -582,6 +589,12 @@ def main():
         out["memory_bound_rotating"] = memory_bound_rotating(torch, layer, d)
         print("[bench] forward of 2048 tokens", file=sys.stderr, flush=True)
         out["forward_2048"] = forward_2048(torch)
+        print("[bench] matrix-core ceiling", file=sys.stderr, flush=True)
+        ceil = mfma_ceiling(torch)
+        out["mfma_ceiling"] = ceil
+        for k in GEMMS:
+            if k in breakdown:
+                breakdown[k]["frac_ceiling"] = round(breakdown[k]["tops"] / ceil["tops"], 4)
     out["extras"].update(skinny_forward(torch))
     if not (args.no_mlp or args.step_kernels_only):
         out["extras"].update(mlp_products(torch))
@@ -591,6 +604,37 @@ def main():
         print(f"[bench] cpu baseline on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(d, args.cpu_tokens)
     print(json.dumps(out), flush=True)
+
+
+def mfma_ceiling(torch, warm_s=1.0, reps=20, iters=1000):
+    """The library's matrix-core ceiling kernel (the products' register tile
+    and MFMA sequence on random fragments, no memory traffic, one workgroup of
+    8 waves per compute unit): run back to back for about a second so that
+    power and clocks settle where the products run, then `reps` launches timed
+    with an event between launches.  Int8 TOPS of the median launch."""
+    import time
+    from w8a8_integer_linear_amd import _native as nat
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    g = torch.Generator(device="cuda").manual_seed(3)
+    frags = torch.randint(-128, 128, (nat.MFMA_CEILING_FRAG_BYTES,), dtype=torch.int32,
+                          device="cuda", generator=g).to(torch.int8)
+    out = torch.empty(cus * 512 * 4, dtype=torch.int32, device="cuda")
+    ops = 2.0 * 16 * 16 * 64 * 64 * 8 * cus * iters
+    t0 = time.time()
+    while time.time() - t0 < warm_s:
+        for _ in range(10):
+            nat.qlin_mfma_ceiling(frags, out, cus, iters)
+        torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        nat.qlin_mfma_ceiling(frags, out, cus, iters)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])
+    tops = ops / (ms * 1e-3) / 1e12
+    return {"ms_per_launch": round(ms, 4), "tops": round(tops, 1),
+            "frac_peak": round(tops / PEAK_INT8_TOPS, 4), "workgroups": cus, "iters": iters}
 
 
 def wn_update(torch, layer):

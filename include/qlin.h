@@ -412,6 +412,28 @@ int qlin_gemm_s32(int op, const int8_t *a, const int8_t *b, int64_t M, int64_t N
  */
 int qlin_stream_copy(const void *src, void *dst, int64_t nbytes, void *stream);
 
+/*
+ * Matrix-core ceiling: the products' register tile and MFMA sequence with no
+ * memory traffic.  Each of `workgroups` workgroups runs 8 waves; each wave
+ * reads 24 fragments of 1 KiB (two 64-byte contraction steps of 8 row blocks
+ * and 4 column blocks, lane l's 16 bytes at 16 l of a fragment, wave w
+ * starting at fragment w) once from frags and then repeats, `iters` times,
+ * the products' step-major sequence of 64 v_mfma_i32_16x16x64_i8 into 8 x 4
+ * blocks of 16 x 16 int32 sums.  It computes nothing of the layer: its rate
+ * on random fragments, with one workgroup per compute unit, is the int8
+ * matrix throughput the device sustains within its power limit, the practical
+ * ceiling against which the products are reported beside the nameplate peak.
+ *   frags       device buffer of QLIN_MFMA_CEILING_FRAG_BYTES int8 values,
+ *               16-byte aligned.
+ *   out         device buffer of workgroups * 512 * 4 int32, 16-byte aligned:
+ *               lane t of workgroup g writes, at out[4 (512 g + t) + e], the
+ *               sum over its 32 blocks of register e (int32, wrapping).
+ *   workgroups  in [1, 65535]; iters in [1, 1048576].
+ */
+#define QLIN_MFMA_CEILING_FRAG_BYTES (24 * 1024)
+int qlin_mfma_ceiling(const int8_t *frags, int32_t *out, int workgroups, int iters,
+                      void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -152,6 +152,18 @@ def test_stream_copy_validation(L):
     assert L.qlin_stream_copy(None, None, 0, None) == 0     # nothing to copy
 
 
+def test_mfma_ceiling_validation(L):
+    _cpu_only()
+    assert L.qlin_mfma_ceiling(P, Q, 0, 10, None) == 1             # no workgroups
+    assert L.qlin_mfma_ceiling(P, Q, 65536, 10, None) == 1
+    assert L.qlin_mfma_ceiling(P, Q, 4, 0, None) == 1              # no repetitions
+    assert L.qlin_mfma_ceiling(P, Q, 4, (1 << 20) + 1, None) == 1
+    assert L.qlin_mfma_ceiling(None, Q, 4, 10, None) == 1
+    assert L.qlin_mfma_ceiling(P, None, 4, 10, None) == 1
+    assert L.qlin_mfma_ceiling(ODD, Q, 4, 10, None) == 1           # misaligned
+    assert L.qlin_mfma_ceiling(P, P + 1024, 4, 10, None) == 1      # out overlaps the fragments
+
+
 def test_weight_norm_validation(L):
     _cpu_only()
     T = 0x50000

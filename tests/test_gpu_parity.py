@@ -210,6 +210,42 @@ def test_quantize_grad_random(T, Q, orc, i, rows, cols, bf16):
     assert np.all(np.abs(host(db).astype(np.float64) - dbr) <= bound)
 
 
+def _fragment_matrix(frag):
+    """A 1 KiB MFMA fragment (lane l's 16 bytes at 16 l) as the 16 x 64 block
+    it carries: lane 16 g + r holds row r, contraction bytes 16 g .. 16 g + 15."""
+    f = frag.reshape(4, 16, 16)                       # [g, r, j]
+    return f.transpose(1, 0, 2).reshape(16, 64).astype(np.int64)
+
+
+@pytest.mark.parametrize("iters", [1, 3])
+def test_mfma_ceiling(T, Q, iters):
+    """The matrix-core ceiling kernel does the products' MFMA work: every lane's
+    sums against plain int64 matrix products of its wave's fragments."""
+    rng = np.random.default_rng(31)
+    frags = rng.integers(-128, 128, Q.MFMA_CEILING_FRAG_BYTES, dtype=np.int64).astype(np.int8)
+    wg = 2
+    announce("mfma ceiling", iters)
+    out = T.zeros(wg * 512 * 4, dtype=T.int32, device="cuda")
+    Q.qlin_mfma_ceiling(dev(frags), out, wg, iters)
+    T.cuda.synchronize()
+    got = host(out).reshape(wg, 8, 64, 4)
+    fr = frags.reshape(24, 1024)
+    lane = np.arange(64)
+    for w in range(8):
+        s = np.zeros((16, 16), np.int64)              # block sums [A row, B row]
+        for st in range(2):
+            for f in range(8):
+                a = _fragment_matrix(fr[(w + 8 * st + f) % 24])
+                for b in range(4):
+                    bm = _fragment_matrix(fr[(w + 16 + 4 * st + b) % 24])
+                    s += a @ bm.T
+        # Lane l, register e holds row l % 16, column 4 (l // 16) + e.
+        want = np.stack([s[lane % 16, 4 * (lane // 16) + e] for e in range(4)], axis=1) * iters
+        want = want.astype(np.int64).astype(np.int32)
+        for g in range(wg):
+            assert np.array_equal(got[g, w], want), (g, w)
+
+
 def test_quantize_grad_tiny_scales(T, Q, orc):
     """Zero, subnormal and normal row and column scales in one call: the code
     pass's exact quotients for subnormal scales, fast path elsewhere."""

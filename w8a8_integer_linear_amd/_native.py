@@ -46,7 +46,9 @@ SIGNATURES = {
     "qlin_stream_copy": ([_vp, _vp, _i64, _vp], _i32),
     "qlin_product_noalloc": ([_i32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp],
                              _i32),
+    "qlin_mfma_ceiling": ([_vp, _vp, _i32, _i32, _vp], _i32),
 }
+MFMA_CEILING_FRAG_BYTES = 24 * 1024
 NOALLOC_SCRATCH_BYTES = 4096 + 160 * 262144
 
 
@@ -366,3 +368,15 @@ def qlin_stream_copy(src, dst, stream=None):
     _check("qlin_stream_copy", lib().qlin_stream_copy(_ptr(src), _ptr(dst), nbytes,
                                                       _stream(stream)))
     return dst
+
+
+def qlin_mfma_ceiling(frags, out, workgroups, iters, stream=None):
+    """The library's matrix-core ceiling kernel: `workgroups` workgroups repeat
+    the products' MFMA sequence `iters` times on the int8 fragments in frags
+    (MFMA_CEILING_FRAG_BYTES); out (int32, workgroups * 512 * 4) gets each
+    lane's sums."""
+    _need(frags, "frags", torch.int8, (MFMA_CEILING_FRAG_BYTES,))
+    _need(out, "out", torch.int32, (int(workgroups) * 512 * 4,))
+    _check("qlin_mfma_ceiling", lib().qlin_mfma_ceiling(_ptr(frags), _ptr(out), int(workgroups),
+                                                        int(iters), _stream(stream)))
+    return out

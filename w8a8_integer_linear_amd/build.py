@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libqlin.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "quant.hip", "gemm.hip", "sgd.hip", "stream.hip"]
+SOURCES = ["api.hip", "quant.hip", "gemm.hip", "sgd.hip", "stream.hip", "mfma_ceiling.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

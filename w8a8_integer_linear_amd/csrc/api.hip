@@ -453,6 +453,21 @@ int qlin_stream_copy(const void *src, void *dst, int64_t nbytes, void *stream)
     return finish();
 }
 
+int qlin_mfma_ceiling(const int8_t *frags, int32_t *out, int workgroups, int iters,
+                      void *stream)
+{
+    static_assert(QLIN_MFMA_CEILING_FRAG_BYTES == qlin::kMfmaCeilingFrags * 1024,
+                  "fragment buffer size");
+    if (workgroups < 1 || workgroups > 65535 || iters < 1 || iters > (1 << 20))
+        return QLIN_EINVAL;
+    if (!array_ok(frags, true) || !array_ok(out, true))
+        return QLIN_EINVAL;
+    if (overlap(frags, QLIN_MFMA_CEILING_FRAG_BYTES, out, (int64_t)workgroups * 512 * 16))
+        return QLIN_EINVAL;
+    qlin::launch_mfma_ceiling(frags, out, workgroups, iters, as_stream(stream));
+    return finish();
+}
+
 int qlin_sgd_requant(int8_t *qw, float *sw, const float *dw, int64_t N, int64_t K, float lr,
                      uint64_t seed, uint64_t step, float *bias, const float *db, void *stream)
 {

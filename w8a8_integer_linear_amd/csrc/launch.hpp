@@ -79,6 +79,14 @@ void launch_product_long(const ProductArgs &p, int64_t *ws, hipStream_t st);
 // buffers: the reference for the memory-bound kernels' bandwidth.
 void launch_stream_copy(const void *src, void *dst, int64_t nbytes, hipStream_t st);
 
+// Matrix-core ceiling: `workgroups` workgroups of 8 waves repeat the
+// products' MFMA sequence `iters` times on kMfmaCeilingFrags fragments of
+// 1 KiB from frags; out gets each lane's sum of its 32 accumulator blocks
+// (workgroups x 512 x 4 int32).
+constexpr int kMfmaCeilingFrags = 24;
+void launch_mfma_ceiling(const int8_t *frags, int32_t *out, int workgroups, int iters,
+                         hipStream_t st);
+
 void launch_sgd_requant(int8_t *qw, float *sw, const float *dw, int64_t N, int64_t K, float lr,
                         uint64_t seed, uint64_t step, float *bias, const float *db,
                         hipStream_t st);

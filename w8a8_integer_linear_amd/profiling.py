@@ -14,6 +14,8 @@ Reads  OUT_DIR/kt/*kernel_stats.csv      (rocprofv3 --kernel-trace --stats)
                                     SQ_BUSY_CYCLES SQ_WAVES), if present
        OUT_DIR/power.txt (amd-smi metric -p -c samples taken while bench.py
                           ran its step loop), if present
+       OUT_DIR/power_ceiling.txt (the same while bench.py ran the matrix-core
+                          ceiling kernel), if present
 Writes profiles/kernels_headline_step.txt (per-kernel durations),
        profiles/pmc_traffic.json + profiles/pmc_traffic.txt (HBM bytes per
        launch, scaled by the reading of the calibration copy of 512 MiB) and
@@ -22,8 +24,8 @@ Writes profiles/kernels_headline_step.txt (per-kernel durations),
        fraction of those cycles the SIMDs' matrix pipes were busy) and
        profiles/lds_bank_conflicts.txt (from OUT_DIR/lds, if present),
        profiles/valu_issue.txt (per kernel: the time its vector instructions
-       alone take to issue, against its duration) and
-       profiles/power_headline_step.txt.
+       alone take to issue, against its duration),
+       profiles/power_headline_step.txt and profiles/power_mfma_ceiling.txt.
 """
 import csv
 import glob
@@ -190,6 +192,13 @@ def main(out_dir, digest=None):
         valu_summary(out_dir)
     if os.path.exists(os.path.join(out_dir, "power.txt")):
         power_summary(out_dir)
+    if os.path.exists(os.path.join(out_dir, "power_ceiling.txt")):
+        power_summary(out_dir, "power_ceiling.txt", "power_mfma_ceiling.txt",
+                      "# Socket power and graphics clocks while the matrix-core ceiling kernel "
+                      "runs back to back\n# (the products' MFMA sequence on random fragments, "
+                      "no memory traffic).\n"
+                      "#   python bench.py --mfma-ceiling-seconds 6 &  sleep 3;\n"
+                      "#   10 x (amd-smi metric -p -c; sleep 0.2)\n")
 
 
 def valu_summary(out_dir):
@@ -231,26 +240,31 @@ def valu_summary(out_dir):
     print(open(os.path.join(PROFILES, "valu_issue.txt")).read())
 
 
-def power_summary(out_dir):
-    """profiles/power_headline_step.txt from amd-smi samples taken while
-    bench.py ran its timed steps."""
+STEP_POWER_HEADER = ("# Socket power and graphics clocks while the headline step runs back to back.\n"
+                     "#   python bench.py --steps 3000 --cpu-tokens 0 --step-kernels-only &  "
+                     "sleep 4;\n"
+                     "#   10 x (amd-smi metric -p -c; sleep 0.2)\n")
+
+
+def power_summary(out_dir, src="power.txt", dst="power_headline_step.txt",
+                  header=STEP_POWER_HEADER):
+    """profiles/<dst> from the amd-smi samples in OUT/<src> (by default those
+    taken while bench.py ran its timed steps)."""
     import re
-    text = open(os.path.join(out_dir, "power.txt")).read()
+    text = open(os.path.join(out_dir, src)).read()
     rows = []
     for block in text.split("--- sample")[1:]:
         p = re.search(r"SOCKET_POWER:\s*(\d+)", block)
         clocks = [int(c) for c in re.findall(r"GFX_\d+:\s+CLK:\s*(\d+)", block)]
         if p and clocks:
             rows.append((int(p.group(1)), min(clocks), max(clocks)))
-    with open(os.path.join(PROFILES, "power_headline_step.txt"), "w") as f:
-        f.write("# Socket power and graphics clocks while the headline step runs back to back.\n")
-        f.write("#   python bench.py --steps 3000 --cpu-tokens 0 --step-kernels-only &  sleep 4;\n")
-        f.write("#   10 x (amd-smi metric -p -c; sleep 0.2)\n")
+    with open(os.path.join(PROFILES, dst), "w") as f:
+        f.write(header)
         f.write("# The MI355X board power limit is 1400 W.\n")
         f.write(f"# {'sample':>6} {'socket_W':>9} {'gfx_clk_min_MHz':>16} {'gfx_clk_max_MHz':>16}\n")
         for i, (pw, lo, hi) in enumerate(rows):
             f.write(f"  {i + 1:>6} {pw:>9} {lo:>16} {hi:>16}\n")
-    print(open(os.path.join(PROFILES, "power_headline_step.txt")).read())
+    print(open(os.path.join(PROFILES, dst)).read())
 
 
 def lds_summary(out_dir):
