@@ -197,7 +197,7 @@ def main(out_dir, digest=None):
                       "# Socket power and graphics clocks while the matrix-core ceiling kernel "
                       "runs back to back\n# (the products' MFMA sequence on random fragments, "
                       "no memory traffic).\n"
-                      "#   python bench.py --mfma-ceiling-seconds 6 &  sleep 3;\n"
+                      "#   python bench.py --mfma-ceiling-seconds 6 &  sleep 4;\n"
                       "#   10 x (amd-smi metric -p -c; sleep 0.2)\n")
 
 
