@@ -36,7 +36,7 @@
  *    and must reach no further than 2,147,483,632 bytes from it.  The product
  *    calls (qlin_fwd, qlin_bwd_dx, qlin_bwd_dw, qlin_product_ws and
  *    qlin_gemm_s32) return QLIN_EUNSUPPORTED, before launching anything, for
- *    the shapes whose offsets would go past that:
+ *    the shapes whose offsets could go past that, by these bounds:
  *      an operand strided along the contraction (dX: qw, whose rows hold K
  *      bytes; dW: qg2 and qx, rows of N and K bytes) needs
  *      (min(T, 128) - 1) * row_bytes + 256 <= 2,147,483,632, with T the

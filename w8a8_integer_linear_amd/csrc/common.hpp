@@ -237,9 +237,9 @@ __device__ __forceinline__ float recip_refined(float s)
 // is within 2^-24 (1 + 2^-22) of 1 / s, relatively).  Fast path: t =
 // fl(g * inv) is then within 2^-15 of fl(g / s) for |g| <= 127.01 s, so both
 // round to the same integer unless t lies within 2^-14 of a half-integer; if
-// any of the eight does, all eight take the exact quotient.  Rounding to an integer is done by
-// adding 1.5 * 2^23 (round to nearest even in the addition), which also leaves
-// the code as the low byte of the sum's bits.  The quotient is at most
+// any of the eight does, all eight take the exact quotient.  Rounding to an
+// integer is done by adding 1.5 * 2^23 (round to nearest even in the
+// addition), which also leaves the code as the low byte of the sum's bits.  The quotient is at most
 // 127 (1 + 2^-22) < 127.5 in magnitude, so no clamp is needed.
 __device__ __forceinline__ i32x2 quant8(const float g[8], float s, float inv)
 {

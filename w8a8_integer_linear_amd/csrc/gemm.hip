@@ -76,12 +76,14 @@ struct GemmParams {
 
 // ------------------------------------------------------------------ staging
 
-// Buffer resource over an operand from a base at the tile's first row (row
-// operand) or the stage's first contraction row (km operand): every lane
-// offset used below is either a byte offset whose 16 bytes end at or below
-// kOob, which product_addressable checks for each shape before a launch, or
-// kOob itself, which the buffer range check turns into a zero fill of the
-// lane's 16 LDS bytes.
+// Buffer resource over an operand from a base at the stage's start (row
+// operand: the tile's first row at the stage's first contraction byte; km
+// operand: the stage's first contraction row at the tile's first column), so
+// that each lane's offsets are the same in every stage: every lane offset
+// used below is either a byte offset whose 16 bytes end at or below kOob,
+// which product_addressable checks for each shape before a launch, or kOob
+// itself, which the buffer range check turns into a zero fill of the lane's
+// 16 LDS bytes.
 constexpr uint32_t kOob = 0x7FFFFFF0u;
 constexpr int kRsrcWord3 = 0x00020000;   // raw 32-bit buffer format
 // Cache policy of buffer accesses that must be coherent across the XCDs'
@@ -124,34 +126,55 @@ struct Operand {
             return (row >> 1) & 7;
     }
 
-    // Enqueue loads P0 .. P1 - 1 of this thread's share of the stage whose
-    // contraction starts at k0, into 'dst'.
-    template <int P0 = 0, int P1 = kLoads>
-    __device__ static __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, int64_t ld, int i0,
-                                                 int lim, int k0, int T, bool live, int8_t *dst)
+    // Load p of this lane: its output row or column within the tile and its
+    // contraction index within the stage.
+    __device__ static __forceinline__ void lane_slot(int p, int w, int &gi, int &gk)
     {
-        const int lane = __lane_id();
-        const int w = threadIdx.x / kWave;
-#pragma unroll
-        for (int p = P0; p < P1; p++) {
-            const int slot = (p * (NT / kWave) + w) * kWave + lane;   // 16-byte LDS slot
-            const int row = slot / kRowChunks;
-            const int c = (slot % kRowChunks) ^ swz(row);
-            int gi, gk;
-            int64_t off;
-            if constexpr (KM) {
-                gk = k0 + row;
-                gi = i0 + 16 * c;
-                off = (int64_t)gk * ld + gi;
-            } else {
-                gi = i0 + row;
-                gk = k0 + 16 * c;
-                off = (int64_t)gi * ld + gk;
-            }
-            const uint32_t voff = (live && gi < lim && gk < T) ? (uint32_t)off : kOob;
+        const int slot = (p * (NT / kWave) + w) * kWave + __lane_id();   // 16-byte LDS slot
+        const int row = slot / kRowChunks;
+        const int c = (slot % kRowChunks) ^ swz(row);
+        gi = KM ? 16 * c : row;
+        gk = KM ? row : 16 * c;
+    }
+
+    // Byte offset of load p from a stage's base (the stage's first
+    // contraction row, or byte, of the tile), the same in every stage; kOob
+    // when the load's row or column lies past lim.
+    __device__ static __forceinline__ uint32_t lane_offset(int p, int w, int64_t ld, int lim)
+    {
+        int gi, gk;
+        lane_slot(p, w, gi, gk);
+        const int64_t off = KM ? (int64_t)gk * ld + gi : (int64_t)gi * ld + gk;
+        return gi < lim ? (uint32_t)off : kOob;
+    }
+
+    // Enqueue loads P0 .. P1 - 1 of this thread's share of a stage through
+    // the resource rs based at the stage, into 'dst'.  voff holds the lane
+    // offsets (lane_offset); w is the wave index, uniform.  A full stage uses
+    // them as they are; otherwise loads whose contraction index reaches trel,
+    // the contraction left from the stage's start, or every load of a stage
+    // past the unit's end (!live), read zeros.
+    template <int P0 = 0, int P1 = kLoads>
+    __device__ static __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs,
+                                                 const uint32_t (&voff)[kLoads], int trel,
+                                                 bool live, bool full, int w, int8_t *dst)
+    {
+        auto load = [&](int p, uint32_t off) {
             lds_i8 *wave_dst = (lds_i8 *)dst + (p * (NT / kWave) + w) * (kWave * 16);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)wave_dst,
-                                                     16, voff, 0, 0, 0);
+                                                     16, off, 0, 0, 0);
+        };
+        if (full) {
+#pragma unroll
+            for (int p = P0; p < P1; p++)
+                load(p, voff[p]);
+        } else {
+#pragma unroll
+            for (int p = P0; p < P1; p++) {
+                int gi, gk;
+                lane_slot(p, w, gi, gk);
+                load(p, live && gk < trel ? voff[p] : kOob);
+            }
         }
     }
 
@@ -490,23 +513,25 @@ __device__ __forceinline__ void store_pass(const GemmParams &p, const lds_i8 *st
 template <typename OpA, typename OpB, bool AKM, bool BKM, int kBK, int G0 = 0,
           int G1 = OpA::kLoads + OpB::kLoads>
 __device__ __forceinline__ void issue_stage(const GemmParams &p, const int8_t *abase,
-                                            const int8_t *bbase, int alim, int blim, int kb,
+                                            const int8_t *bbase,
+                                            const uint32_t (&voffA)[OpA::kLoads],
+                                            const uint32_t (&voffB)[OpB::kLoads], int w, int kb,
                                             int KT, int s, int8_t *dst)
 {
     constexpr int nA = OpA::kLoads;
     const bool live = s < KT;
     const int k0 = live ? (kb + s) * kBK : 0;
+    const int trel = p.T - k0;
+    const bool full = live && trel >= kBK;
     if constexpr (G0 < nA) {
-        const int8_t *ak = AKM ? abase + (int64_t)k0 * p.lda : abase;
-        OpA::template issue<G0, (G1 < nA ? G1 : nA)>(make_rsrc(ak), p.lda, 0, alim,
-                                                     AKM ? 0 : k0, AKM ? p.T - k0 : p.T, live,
+        const int8_t *ak = AKM ? abase + (int64_t)k0 * p.lda : abase + k0;
+        OpA::template issue<G0, (G1 < nA ? G1 : nA)>(make_rsrc(ak), voffA, trel, live, full, w,
                                                      dst);
     }
     if constexpr (G1 > nA) {
-        const int8_t *bk = BKM ? bbase + (int64_t)k0 * p.ldb : bbase;
-        OpB::template issue<(G0 > nA ? G0 - nA : 0), G1 - nA>(
-            make_rsrc(bk), p.ldb, 0, blim, BKM ? 0 : k0, BKM ? p.T - k0 : p.T, live,
-            dst + OpA::kBytes);
+        const int8_t *bk = BKM ? bbase + (int64_t)k0 * p.ldb : bbase + k0;
+        OpB::template issue<(G0 > nA ? G0 - nA : 0), G1 - nA>(make_rsrc(bk), voffB, trel, live,
+                                                              full, w, dst + OpA::kBytes);
     }
 }
 
@@ -646,11 +671,20 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
     const int8_t *abase = AKM ? p.a + i0 : p.a + (int64_t)i0 * p.lda;
     const int8_t *bbase = BKM ? p.b + j0 : p.b + (int64_t)j0 * p.ldb;
     const int alim = p.R - i0, blim = p.S - j0;
+    // The lanes' load offsets within a stage, the same for every stage.
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    uint32_t voffA[OpA::kLoads], voffB[OpB::kLoads];
+#pragma unroll
+    for (int q = 0; q < OpA::kLoads; q++)
+        voffA[q] = OpA::lane_offset(q, wu, p.lda, alim);
+#pragma unroll
+    for (int q = 0; q < OpB::kLoads; q++)
+        voffB[q] = OpB::lane_offset(q, wu, p.ldb, blim);
     // Part G of stage s's buffer-to-LDS loads, into buffer s % 2.
     auto issue = [&](int s, auto G) {
         constexpr int g = decltype(G)::value, per = kLoads / kSpread;
         issue_stage<OpA, OpB, AKM, BKM, kBK, g * per, (g + 1) * per>(
-            p, abase, bbase, alim, blim, kb, KT, s, smem + (s & 1) * kStage);
+            p, abase, bbase, voffA, voffB, wu, kb, KT, s, smem + (s & 1) * kStage);
     };
 
     // Lane offsets of this wave's fragments inside a stage: per step for a
