@@ -215,6 +215,7 @@ struct Operand {
     template <int OFF>
     __device__ static __forceinline__ void frag(uint32_t addr, Raw &f)
     {
+        static_assert(OFF >= 0 && OFF + (KM ? 8 * ROWS : 0) < 65536, "LDS read immediate");
         if constexpr (KM) {
             asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(f.lo) : "v"(addr), "n"(OFF));
             asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2"
@@ -516,7 +517,7 @@ __device__ __forceinline__ void issue_stage(const GemmParams &p, const int8_t *a
                                             const int8_t *bbase,
                                             const uint32_t (&voffA)[OpA::kLoads],
                                             const uint32_t (&voffB)[OpB::kLoads], int w, int kb,
-                                            int KT, int s, int8_t *dst)
+                                            int KT, int s, int8_t *dstA, int8_t *dstB)
 {
     constexpr int nA = OpA::kLoads;
     const bool live = s < KT;
@@ -526,12 +527,12 @@ __device__ __forceinline__ void issue_stage(const GemmParams &p, const int8_t *a
     if constexpr (G0 < nA) {
         const int8_t *ak = AKM ? abase + (int64_t)k0 * p.lda : abase + k0;
         OpA::template issue<G0, (G1 < nA ? G1 : nA)>(make_rsrc(ak), voffA, trel, live, full, w,
-                                                     dst);
+                                                     dstA);
     }
     if constexpr (G1 > nA) {
         const int8_t *bk = BKM ? bbase + (int64_t)k0 * p.ldb : bbase + k0;
         OpB::template issue<(G0 > nA ? G0 - nA : 0), G1 - nA>(make_rsrc(bk), voffB, trel, live,
-                                                              full, w, dst + OpA::kBytes);
+                                                              full, w, dstB);
     }
 }
 
@@ -680,11 +681,15 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
 #pragma unroll
     for (int q = 0; q < OpB::kLoads; q++)
         voffB[q] = OpB::lane_offset(q, wu, p.ldb, blim);
-    // Part G of stage s's buffer-to-LDS loads, into buffer s % 2.
+    // LDS holds the operands' stages operand by operand: A's two stages, then
+    // B's, so that a stage's offset fits the LDS reads' immediate and the
+    // unrolled loop below addresses either stage with constants.
+    // Part G of stage s's buffer-to-LDS loads, into buffers s % 2.
     auto issue = [&](int s, auto G) {
         constexpr int g = decltype(G)::value, per = kLoads / kSpread;
         issue_stage<OpA, OpB, AKM, BKM, kBK, g * per, (g + 1) * per>(
-            p, abase, bbase, voffA, voffB, wu, kb, KT, s, smem + (s & 1) * kStage);
+            p, abase, bbase, voffA, voffB, wu, kb, KT, s, smem + (s & 1) * OpA::kBytes,
+            smem + 2 * OpA::kBytes + (s & 1) * OpB::kBytes);
     };
 
     // Lane offsets of this wave's fragments inside a stage: per step for a
@@ -697,7 +702,7 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
         offA[x] = AKM ? OpA::off(wi * RW + 16 * x, 0) : OpA::off(wi * RW, x);
 #pragma unroll
     for (int x = 0; x < (BKM ? FN : NK); x++)
-        offB[x] = OpA::kBytes + (BKM ? OpB::off(wj * CW + 16 * x, 0) : OpB::off(wj * CW, x));
+        offB[x] = 2 * OpA::kBytes + (BKM ? OpB::off(wj * CW + 16 * x, 0) : OpB::off(wj * CW, x));
 
     i32x4 acc[FM][FN];
 #pragma unroll
@@ -708,20 +713,22 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
 
     typename OpA::Raw fa[8];          // row-block fragment t in fa[t % 8]
     typename OpB::Raw fb[NK][FN];     // column-block fragments of each step
-    // Fragment t = FM kk + f (row block f, step kk) of the stage at sb.
-    auto read_a = [&](uint32_t sb, auto T) {
+    // Fragment t = FM kk + f (row block f, step kk) of the stage of parity P.
+    auto read_a = [&](auto P, auto T) {
         constexpr int t = decltype(T)::value, kk = t / FM, f = t % FM;
+        constexpr int st = decltype(P)::value * OpA::kBytes;
         if constexpr (AKM)
-            OpA::template frag<kk * OpA::kStep>(sb + offA[f], fa[t % 8]);
+            OpA::template frag<st + kk * OpA::kStep>(lds0 + offA[f], fa[t % 8]);
         else
-            OpA::template frag<f * OpA::kBlock>(sb + offA[kk], fa[t % 8]);
+            OpA::template frag<st + f * OpA::kBlock>(lds0 + offA[kk], fa[t % 8]);
     };
-    auto read_b = [&](uint32_t sb, auto KK, auto Bi) {
+    auto read_b = [&](auto P, auto KK, auto Bi) {
         constexpr int kk = decltype(KK)::value, b = decltype(Bi)::value;
+        constexpr int st = decltype(P)::value * OpB::kBytes;
         if constexpr (BKM)
-            OpB::template frag<kk * OpB::kStep>(sb + offB[b], fb[kk][b]);
+            OpB::template frag<st + kk * OpB::kStep>(lds0 + offB[b], fb[kk][b]);
         else
-            OpB::template frag<b * OpB::kBlock>(sb + offB[kk], fb[kk][b]);
+            OpB::template frag<st + b * OpB::kBlock>(lds0 + offB[kk], fb[kk][b]);
     };
     auto mfma = [&](auto T) {
         constexpr int t = decltype(T)::value, kk = t / FM, f = t % FM;
@@ -733,9 +740,9 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
     };
     using Zero = std::integral_constant<int, 0>;
     using One = std::integral_constant<int, 1>;
-    auto head = [&](uint32_t sb) {
-        static_for<FN>([&](auto Bi) { read_b(sb, Zero{}, Bi); });
-        static_for<kAhead>([&](auto T) { read_a(sb, T); });
+    auto head = [&](auto P) {
+        static_for<FN>([&](auto Bi) { read_b(P, Zero{}, Bi); });
+        static_for<kAhead>([&](auto T) { read_a(P, T); });
     };
 
     // Per stage: fragment t's MFMAs follow its wait; before them the reads of
@@ -745,12 +752,9 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
     // head reads are issued and the last kAhead fragments' MFMAs cover their
     // latency.  The next stage's buffer-to-LDS loads are issued among the
     // MFMAs of the first kSpread fragments.
-    static_for<kSpread>([&](auto G) { issue(0, G); });
-    wait_vmcnt<0>();
-    barrier_no_fence();
-    head(lds0);
-    for (int kt = 0; kt < KT; kt++) {
-        const uint32_t sb = lds0 + (kt & 1) * kStage;
+    // Stage kt, of parity P = kt % 2 (the loop below is unrolled by two).
+    auto stage = [&](int kt, auto P) {
+        constexpr int par = decltype(P)::value;
         static_for<kSteps - kAhead>([&](auto T) {
             constexpr int t = decltype(T)::value;
             wait_lgkmcnt<reads_after<kAhead, kBEvery, FM, FN, cA, cB, kSteps>(t)>();
@@ -761,8 +765,8 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
                     OpB::settle(fb[t / FM][b]);
             }
             if constexpr (b_at<kBEvery, FN>(t) >= 0)
-                read_b(sb, One{}, std::integral_constant<int, b_at<kBEvery, FN>(t)>{});
-            read_a(sb, std::integral_constant<int, t + kAhead>{});
+                read_b(P, One{}, std::integral_constant<int, b_at<kBEvery, FN>(t)>{});
+            read_a(P, std::integral_constant<int, t + kAhead>{});
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (t < kSpread) {
                 issue(kt + 1, T);
@@ -784,12 +788,21 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
             [&](auto T) { OpA::settle(fa[(kSteps - kAhead + decltype(T)::value) % 8]); });
         barrier_no_fence();
         if (kt + 1 < KT)
-            head(lds0 + ((kt + 1) & 1) * kStage);
+            head(std::integral_constant<int, 1 - par>{});
         __builtin_amdgcn_sched_barrier(0);
         static_for<kAhead>([&](auto T) {
             mfma(std::integral_constant<int, kSteps - kAhead + decltype(T)::value>{});
         });
         __builtin_amdgcn_sched_barrier(0);
+    };
+    static_for<kSpread>([&](auto G) { issue(0, G); });
+    wait_vmcnt<0>();
+    barrier_no_fence();
+    head(Zero{});
+    for (int kt = 0; kt < KT; kt += 2) {
+        stage(kt, Zero{});
+        if (kt + 1 < KT)
+            stage(kt + 1, One{});
     }
     wait_vmcnt<0>();
 
