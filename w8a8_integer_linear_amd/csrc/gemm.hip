@@ -90,10 +90,25 @@ constexpr int kRsrcWord3 = 0x00020000;   // raw 32-bit buffer format
 // L2s (sc1, the device-scope bit).
 constexpr int kCoherent = 16;
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const int8_t *base)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const int8_t *base,
+                                                          uint32_t records = kOob)
 {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(base), (short)0, (int)kOob,
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(base), (short)0, (int)records,
                                              kRsrcWord3);
+}
+
+// Bytes a km operand's stage resource covers: all of a full stage, the first
+// trel contraction rows of a partial one (whose later rows then read zeros:
+// a lane's offset is its row times ld plus a column offset below ld, both
+// multiples of 16), nothing of a stage past the unit's end.
+__device__ __forceinline__ uint32_t km_records(bool live, bool full, int trel, int64_t ld)
+{
+    if (!live)
+        return 0;
+    if (full)
+        return kOob;
+    const int64_t n = (int64_t)trel * ld;
+    return n < (int64_t)kOob ? (uint32_t)n : kOob;
 }
 
 typedef __attribute__((address_space(3))) int8_t lds_i8;
@@ -164,7 +179,8 @@ struct Operand {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)wave_dst,
                                                      16, off, 0, 0, 0);
         };
-        if (full) {
+        if (KM || full) {
+            // (A km operand's resource already bounds a partial stage.)
 #pragma unroll
             for (int p = P0; p < P1; p++)
                 load(p, voff[p]);
@@ -526,13 +542,15 @@ __device__ __forceinline__ void issue_stage(const GemmParams &p, const int8_t *a
     const bool full = live && trel >= kBK;
     if constexpr (G0 < nA) {
         const int8_t *ak = AKM ? abase + (int64_t)k0 * p.lda : abase + k0;
-        OpA::template issue<G0, (G1 < nA ? G1 : nA)>(make_rsrc(ak), voffA, trel, live, full, w,
-                                                     dstA);
+        const uint32_t ra = AKM ? km_records(live, full, trel, p.lda) : kOob;
+        OpA::template issue<G0, (G1 < nA ? G1 : nA)>(make_rsrc(ak, ra), voffA, trel, live, full,
+                                                     w, dstA);
     }
     if constexpr (G1 > nA) {
         const int8_t *bk = BKM ? bbase + (int64_t)k0 * p.ldb : bbase + k0;
-        OpB::template issue<(G0 > nA ? G0 - nA : 0), G1 - nA>(make_rsrc(bk), voffB, trel, live,
-                                                              full, w, dstB);
+        const uint32_t rb = BKM ? km_records(live, full, trel, p.ldb) : kOob;
+        OpB::template issue<(G0 > nA ? G0 - nA : 0), G1 - nA>(make_rsrc(bk, rb), voffB, trel,
+                                                              live, full, w, dstB);
     }
 }
 
