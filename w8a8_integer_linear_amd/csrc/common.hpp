@@ -8,6 +8,9 @@ namespace qlin {
 
 constexpr int kWave = 64;
 
+// Word 3 of a buffer resource for raw (unformatted) 32-bit accesses.
+constexpr int kRsrcWord3 = 0x00020000;
+
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));

@@ -85,7 +85,6 @@ struct GemmParams {
 // itself, which the buffer range check turns into a zero fill of the lane's
 // 16 LDS bytes.
 constexpr uint32_t kOob = 0x7FFFFFF0u;
-constexpr int kRsrcWord3 = 0x00020000;   // raw 32-bit buffer format
 // Cache policy of buffer accesses that must be coherent across the XCDs'
 // L2s (sc1, the device-scope bit).
 constexpr int kCoherent = 16;

@@ -388,6 +388,8 @@ constexpr int kStatCols = 512;
 constexpr int kStatBatch = 8;    // rows a lane loads before using any of them
 constexpr int kStatWaves = 4096; // waves of pass 1 (row groups x column windows)
 constexpr int kCodeRows = 16;    // rows per thread in pass 2
+// Offset of a dropped store: past any resource of pass 1 (rows * 4 bytes).
+constexpr int kDropOffset = 0x7FFFFFF0;
 
 // Maximum over the wave of each of kStatBatch values, left in lane 63: per
 // step, one v_max_f32 whose first source is read through DPP.  The quad
@@ -457,39 +459,78 @@ __global__ __launch_bounds__(256) void grad_stats_kernel(const void *__restrict_
         mx[e] = 0.0f;
         sm[e] = 0.0f;
     }
-    float *rp = rowpart + win * rows;
+    // Row maxima go out through a buffer resource over this window's rows:
+    // lane u < 8 stores row rb + u, and rows past the end (and lanes 8..63)
+    // take an offset past the resource, whose stores the buffer unit drops.
+    // So a batch issues the same memory operations on every path, and the
+    // wait before a batch's arithmetic covers that batch's loads only.
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        rowpart + win * rows, (short)0, (int)(rows * 4), kRsrcWord3);
     const int64_t step = (int64_t)gridDim.y * kStatBatch;
-    for (int64_t rb = (int64_t)blockIdx.y * kStatBatch; rb < rows; rb += step) {
-        Raw8<BF16> raw[kStatBatch];
-        float px[kStatBatch];
+    // Rows past the end read the last row.  A batch's eight row scales come
+    // in one vector load (lane l holds row rb + l % 8's).
+    Raw8<BF16> raw[2][kStatBatch];
+    float pxv[2];
+    auto fetch = [&](auto B, int64_t rb) {
+        const int64_t rl = rb + (lc & 7);
+        pxv[B()] = sx[rl < rows ? rl : rows - 1];
 #pragma unroll
         for (int u = 0; u < kStatBatch; u++) {
             const int64_t r = rb + u < rows ? rb + u : rows - 1;
-            raw[u] = load_raw8<BF16>(x, r * cols + cl);
-            px[u] = sx[r];
+            raw[B()][u] = load_raw8<BF16>(x, r * cols + cl);
         }
+    };
+    auto reduce = [&](auto B, int64_t rb) {
         float rm[kStatBatch];
 #pragma unroll
         for (int u = 0; u < kStatBatch; u++) {
             float v[8];
-            unpack8<BF16>(raw[u], v);
+            unpack8<BF16>(raw[B()][u], v);
+            const float px = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pxv[B()]), u));
             float m = 0.0f;
             if (rb + u < rows) {
 #pragma unroll
                 for (int e = 0; e < 8; e++) {
                     sm[e] = sm[e] + v[e];
-                    mx[e] = fmaxf(mx[e], __builtin_fabsf(v[e] * px[u]));
+                    mx[e] = fmaxf(mx[e], __builtin_fabsf(v[e] * px));
                     m = fmaxf(m, __builtin_fabsf(v[e] * w[e]));
                 }
             }
             rm[u] = m;
         }
         wave_max8_to_last(rm);
-        if (lc == kWave - 1) {
+        float rv = 0.0f;
 #pragma unroll
-            for (int u = 0; u < kStatBatch; u++)
-                if (rb + u < rows)
-                    rp[rb + u] = rm[u];
+        for (int u = 0; u < kStatBatch; u++) {
+            const float s = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rm[u]), kWave - 1));
+            rv = lc == u ? s : rv;
+        }
+        const int64_t r = rb + lc;
+        const int off = lc < kStatBatch && r < rows ? (int)(r * 4) : kDropOffset;
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, rv), rp, off, 0, 0);
+    };
+    using Zero = std::integral_constant<int, 0>;
+    using One = std::integral_constant<int, 1>;
+    int64_t rb = (int64_t)blockIdx.y * kStatBatch;
+    if constexpr (BF16) {
+        // Two batches in registers: the next batch's loads are issued before
+        // the current one is reduced, so the reads do not wait on the
+        // arithmetic.  (fp32 rows would take 64 more registers per lane.)
+        fetch(Zero{}, rb);
+        for (; rb < rows; rb += 2 * step) {
+            fetch(One{}, rb + step);
+            reduce(Zero{}, rb);
+            if (rb + step >= rows)
+                break;
+            fetch(Zero{}, rb + 2 * step);
+            reduce(One{}, rb + step);
+        }
+    } else {
+        for (; rb < rows; rb += step) {
+            fetch(Zero{}, rb);
+            reduce(Zero{}, rb);
         }
     }
     if (cok) {
