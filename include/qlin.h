@@ -418,8 +418,8 @@ int qlin_stream_copy(const void *src, void *dst, int64_t nbytes, void *stream);
  * reads 24 fragments of 1 KiB (two 64-byte contraction steps of 8 row blocks
  * and 4 column blocks, lane l's 16 bytes at 16 l of a fragment, wave w
  * starting at fragment w) once from frags and then repeats, `iters` times,
- * the products' step-major sequence of 64 v_mfma_i32_16x16x64_i8 into 8 x 4
- * blocks of 16 x 16 int32 sums.  It computes nothing of the layer: its rate
+ * the products' sequence of 64 v_mfma_i32_16x16x64_i8 (each block's two
+ * steps back to back) into 8 x 4 blocks of 16 x 16 int32 sums.  It computes nothing of the layer: its rate
  * on random fragments, with one workgroup per compute unit, is the int8
  * matrix throughput the device sustains within its power limit, the practical
  * ceiling against which the products are reported beside the nameplate peak.

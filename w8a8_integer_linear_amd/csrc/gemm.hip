@@ -99,15 +99,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const int8_t *base,
 // Bytes a km operand's stage resource covers: all of a full stage, the first
 // trel contraction rows of a partial one (whose later rows then read zeros:
 // a lane's offset is its row times ld plus a column offset below ld, both
-// multiples of 16), nothing of a stage past the unit's end.
+// multiples of 16), nothing of a stage past the unit's end.  For every shape
+// product_addressable admits, trel * ld < 2^32 (ld <= 2^30, and
+// (min(T, 128) - 1) ld + 256 <= kOob), so 32-bit arithmetic holds it; the
+// clamp keeps kOob past the extent.
 __device__ __forceinline__ uint32_t km_records(bool live, bool full, int trel, int64_t ld)
 {
     if (!live)
         return 0;
     if (full)
         return kOob;
-    const int64_t n = (int64_t)trel * ld;
-    return n < (int64_t)kOob ? (uint32_t)n : kOob;
+    const uint32_t n = (uint32_t)trel * (uint32_t)ld;
+    return n < kOob ? n : kOob;
 }
 
 typedef __attribute__((address_space(3))) int8_t lds_i8;
@@ -518,40 +521,48 @@ __device__ __forceinline__ void store_pass(const GemmParams &p, const lds_i8 *st
     wait_lgkmcnt0();
 }
 
-// Enqueue the buffer-to-LDS loads of stage s of a work unit (contraction
-// stage kb + s) into 'dst'.  Row operands address rows from their tile start
-// (abase, bbase), km operands columns from their tile start and contraction
-// rows from the stage.  Stages past the unit's end (s >= KT) are issued as
-// all-out-of-range loads: zero fills of a buffer that is never read, so every
-// iteration waits for the same number of loads.
-// (Only loads G0 .. G1 - 1 of the stage's OpA::kLoads + OpB::kLoads per
-// lane, A's first.)
-template <typename OpA, typename OpB, bool AKM, bool BKM, int kBK, int G0 = 0,
-          int G1 = OpA::kLoads + OpB::kLoads>
-__device__ __forceinline__ void issue_stage(const GemmParams &p, const int8_t *abase,
-                                            const int8_t *bbase,
-                                            const uint32_t (&voffA)[OpA::kLoads],
-                                            const uint32_t (&voffB)[OpB::kLoads], int w, int kb,
-                                            int KT, int s, int8_t *dstA, int8_t *dstB)
-{
-    constexpr int nA = OpA::kLoads;
-    const bool live = s < KT;
-    const int k0 = live ? (kb + s) * kBK : 0;
-    const int trel = p.T - k0;
-    const bool full = live && trel >= kBK;
-    if constexpr (G0 < nA) {
+// The buffer-to-LDS loads of stage s of a work unit (contraction stage
+// kb + s): row operands address rows from their tile start (abase, bbase),
+// km operands columns from their tile start and contraction rows from the
+// stage.  Stages past the unit's end (s >= KT) are issued as all-out-of-range
+// loads: zero fills of a buffer that is never read, so every iteration waits
+// for the same number of loads.  plan() is computed once per stage; issue()
+// enqueues loads G0 .. G1 - 1 of the stage's OpA::kLoads + OpB::kLoads per
+// lane (A's first).
+template <typename OpA, typename OpB, bool AKM, bool BKM, int kBK>
+struct StageLoads {
+    __amdgpu_buffer_rsrc_t ra, rb;
+    int trel;
+    bool live, full;
+
+    __device__ static __forceinline__ StageLoads plan(const GemmParams &p, const int8_t *abase,
+                                                      const int8_t *bbase, int kb, int KT, int s)
+    {
+        StageLoads L;
+        L.live = s < KT;
+        const int k0 = L.live ? (kb + s) * kBK : 0;
+        L.trel = p.T - k0;
+        L.full = L.live && L.trel >= kBK;
         const int8_t *ak = AKM ? abase + (int64_t)k0 * p.lda : abase + k0;
-        const uint32_t ra = AKM ? km_records(live, full, trel, p.lda) : kOob;
-        OpA::template issue<G0, (G1 < nA ? G1 : nA)>(make_rsrc(ak, ra), voffA, trel, live, full,
-                                                     w, dstA);
-    }
-    if constexpr (G1 > nA) {
         const int8_t *bk = BKM ? bbase + (int64_t)k0 * p.ldb : bbase + k0;
-        const uint32_t rb = BKM ? km_records(live, full, trel, p.ldb) : kOob;
-        OpB::template issue<(G0 > nA ? G0 - nA : 0), G1 - nA>(make_rsrc(bk, rb), voffB, trel,
-                                                              live, full, w, dstB);
+        L.ra = make_rsrc(ak, AKM ? km_records(L.live, L.full, L.trel, p.lda) : kOob);
+        L.rb = make_rsrc(bk, BKM ? km_records(L.live, L.full, L.trel, p.ldb) : kOob);
+        return L;
     }
-}
+
+    template <int G0, int G1>
+    __device__ __forceinline__ void issue(const uint32_t (&voffA)[OpA::kLoads],
+                                          const uint32_t (&voffB)[OpB::kLoads], int w,
+                                          int8_t *dstA, int8_t *dstB) const
+    {
+        constexpr int nA = OpA::kLoads;
+        if constexpr (G0 < nA)
+            OpA::template issue<G0, (G1 < nA ? G1 : nA)>(ra, voffA, trel, live, full, w, dstA);
+        if constexpr (G1 > nA)
+            OpB::template issue<(G0 > nA ? G0 - nA : 0), G1 - nA>(rb, voffB, trel, live, full, w,
+                                                                  dstB);
+    }
+};
 
 // Write one 16-byte chunk of a staged pass.
 template <int CW>
@@ -584,40 +595,6 @@ __device__ __forceinline__ void wait_lgkmcnt()
     asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Order of the 16x16x64 main loop's LDS reads in a stage: the head (the FN
-// column blocks of step 0, then row-block fragments 0 .. D - 1), then for
-// each fragment s first column block s / E of step 1 (when s is a multiple
-// of E and s / E < FN) and then fragment s + D.
-template <int E, int FN>
-constexpr int b_at(int s)
-{
-    return s % E == 0 && s / E < FN ? s / E : -1;
-}
-
-
-// LDS read instructions issued after the last read that fragment t's MFMAs
-// need (fragment t itself and, at a step's first fragment, that step's
-// column blocks) and before fragment t's wait: its lgkmcnt, since LDS reads
-// complete in order.
-template <int D, int E, int FM, int FN, int cA, int cB, int kSteps>
-constexpr int reads_after(int t)
-{
-    const bool need_b = t % FM == 0;
-    const int kk = t / FM;
-    int n = 0;
-    for (int b = 0; b < FN; b++)
-        n = need_b && kk == 0 ? 0 : n + cB;
-    for (int x = 0; x < D; x++)
-        n = x == t ? 0 : n + cA;
-    for (int s = 0; s < t; s++) {
-        if (b_at<E, FN>(s) >= 0)
-            n = need_b && kk == 1 ? 0 : n + cB;
-        if (s + D < kSteps)
-            n = s + D == t ? 0 : n + cA;
-    }
-    return n;
-}
-
 // Four consecutive int64 running sums of row i from column j when this is the
 // last chunk of a contraction past the int32 bound, otherwise zeros.
 template <int MODE>
@@ -646,14 +623,15 @@ __device__ __forceinline__ float tofloat(const GemmParams &p, int32_t c, int64_t
 // The product kernel: 256 x 256 tiles, 8 waves of RW x CW = 128 x 64 outputs
 // in FM x FN = 8 x 4 blocks of 16 x 16, 128 contraction bytes per stage in
 // two LDS stages (two MFMA steps of 64 bytes each).  Per lane the 128 int32
-// sums of the wave tile fill 128 registers.  A step's column-block fragments
-// are double-buffered (the next step's load behind the current one's MFMAs),
-// while the row-block fragments stream through registers: each one's reads
-// are issued kAhead fragments ahead of its four MFMAs (one per column block).
-// Double-buffering whole steps instead, as 32x32x32 blocks allow, would need
-// 96 fragment registers and spill.  Every fragment read is issued by inline
-// asm (constant offsets in the instruction) and waited for with an lgkmcnt
-// that counts the reads issued after it.
+// sums of the wave tile fill 128 registers.  Each block's two steps run back
+// to back, so the second MFMA takes the sums the first one produced (with
+// random operands the matrix cores sustain 0.86-0.87 of their peak in that
+// order against 0.81 step by step, at the same board power).  The column
+// blocks' fragments of both steps stay in registers for the whole stage;
+// the row blocks' fragments (both steps) are read one row block ahead into
+// a ring of two.  Every fragment read is issued by inline asm (constant
+// offsets in the instruction) and waited for with an lgkmcnt that counts the
+// reads issued after it.
 //
 // The B operand is the MFMA's first operand, so block (a, b) holds C
 // transposed: lane l has output row 16 a + l % 16 and, in register e, output
@@ -666,11 +644,10 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
     constexpr int RW = BM / WM, CW = BN / WN;
     constexpr int FM = RW / 16, FN = CW / 16;
     constexpr int NK = kBK / 64;                 // MFMA steps per stage
-    constexpr int kSteps = NK * FM;              // row-block fragments per stage
-    constexpr int kAhead = 3;                    // row-block fragments read ahead
-    constexpr int kSpread = 4;                   // fragments the stage loads spread over
-    constexpr int kBEvery = 1;                   // fragments between step 1's column blocks
-    static_assert(NK == 2 && kSteps % 8 == 0 && kAhead <= 4 && FN * kBEvery <= FM,
+    // Parts the next stage's buffer-to-LDS loads are issued in: one behind
+    // each of the first two MFMA pairs of row blocks 0 .. kSpread / 2 - 1.
+    constexpr int kSpread = 8;
+    static_assert(NK == 2 && FM % 2 == 0 && FN >= 2 && kSpread <= 2 * (FM - 1),
                   "fragment schedule shape");
     using OpA = Operand<BM, AKM, NT, kBK>;
     using OpB = Operand<BN, BKM, NT, kBK>;
@@ -701,12 +678,13 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
     // LDS holds the operands' stages operand by operand: A's two stages, then
     // B's, so that a stage's offset fits the LDS reads' immediate and the
     // unrolled loop below addresses either stage with constants.
-    // Part G of stage s's buffer-to-LDS loads, into buffers s % 2.
-    auto issue = [&](int s, auto G) {
+    // Part G of stage s's buffer-to-LDS loads (planned in L), into buffers
+    // s % 2.
+    using Loads = StageLoads<OpA, OpB, AKM, BKM, kBK>;
+    auto issue = [&](const Loads &L, int s, auto G) {
         constexpr int g = decltype(G)::value, per = kLoads / kSpread;
-        issue_stage<OpA, OpB, AKM, BKM, kBK, g * per, (g + 1) * per>(
-            p, abase, bbase, voffA, voffB, wu, kb, KT, s, smem + (s & 1) * OpA::kBytes,
-            smem + 2 * OpA::kBytes + (s & 1) * OpB::kBytes);
+        L.template issue<g * per, (g + 1) * per>(voffA, voffB, wu, smem + (s & 1) * OpA::kBytes,
+                                                 smem + 2 * OpA::kBytes + (s & 1) * OpB::kBytes);
     };
 
     // Lane offsets of this wave's fragments inside a stage: per step for a
@@ -728,16 +706,20 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
         for (int b = 0; b < FN; b++)
             acc[a][b] = i32x4{0, 0, 0, 0};
 
-    typename OpA::Raw fa[8];          // row-block fragment t in fa[t % 8]
-    typename OpB::Raw fb[NK][FN];     // column-block fragments of each step
-    // Fragment t = FM kk + f (row block f, step kk) of the stage of parity P.
-    auto read_a = [&](auto P, auto T) {
-        constexpr int t = decltype(T)::value, kk = t / FM, f = t % FM;
+    // Row block f's fragments of both steps in fa[f % 2][kk]; the column
+    // blocks' fragments of both steps in fb[kk][b].
+    typename OpA::Raw fa[2][NK];
+    typename OpB::Raw fb[NK][FN];
+    auto read_a = [&](auto P, auto F) {
+        constexpr int f = decltype(F)::value, sl = f % 2;
         constexpr int st = decltype(P)::value * OpA::kBytes;
-        if constexpr (AKM)
-            OpA::template frag<st + kk * OpA::kStep>(lds0 + offA[f], fa[t % 8]);
-        else
-            OpA::template frag<st + f * OpA::kBlock>(lds0 + offA[kk], fa[t % 8]);
+        static_for<NK>([&](auto KK) {
+            constexpr int kk = decltype(KK)::value;
+            if constexpr (AKM)
+                OpA::template frag<st + kk * OpA::kStep>(lds0 + offA[f], fa[sl][kk]);
+            else
+                OpA::template frag<st + f * OpA::kBlock>(lds0 + offA[kk], fa[sl][kk]);
+        });
     };
     auto read_b = [&](auto P, auto KK, auto Bi) {
         constexpr int kk = decltype(KK)::value, b = decltype(Bi)::value;
@@ -747,72 +729,96 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
         else
             OpB::template frag<st + b * OpB::kBlock>(lds0 + offB[kk], fb[kk][b]);
     };
-    auto mfma = [&](auto T) {
-        constexpr int t = decltype(T)::value, kk = t / FM, f = t % FM;
-        const i32x4 av = OpA::value(fa[t % 8]);
+    auto read_b_pair = [&](auto P, auto Bi) {
+        static_for<NK>([&](auto KK) { read_b(P, KK, Bi); });
+    };
+    // Block (f, b)'s two steps back to back: the second MFMA takes the sums
+    // the first one produced.
+    auto mfma_pair = [&](auto F, auto Bi) {
+        constexpr int f = decltype(F)::value, b = decltype(Bi)::value, sl = f % 2;
 #pragma unroll
-        for (int b = 0; b < FN; b++)
-            acc[f][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(OpB::value(fb[kk][b]), av,
-                                                              acc[f][b], 0, 0, 0);
+        for (int kk = 0; kk < NK; kk++)
+            acc[f][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                OpB::value(fb[kk][b]), OpA::value(fa[sl][kk]), acc[f][b], 0, 0, 0);
     };
     using Zero = std::integral_constant<int, 0>;
     using One = std::integral_constant<int, 1>;
+    // Reads of a stage's head: row block 0, then the column blocks' pairs.
     auto head = [&](auto P) {
-        static_for<FN>([&](auto Bi) { read_b(P, Zero{}, Bi); });
-        static_for<kAhead>([&](auto T) { read_a(P, T); });
+        read_a(P, Zero{});
+        static_for<FN>([&](auto Bi) { read_b_pair(P, Bi); });
     };
+    constexpr int rA = NK * cA, rB = NK * cB;       // LDS reads per row block, column block
+    auto lgk = [](int n) { return n < 15 ? n : 15; };
 
-    // Per stage: fragment t's MFMAs follow its wait; before them the reads of
-    // one of step 1's column blocks (every kBEvery fragments) and of fragment
-    // t + kAhead are issued.  After fragment kSteps - kAhead - 1 every read
-    // of the stage is waited for, the stage barrier passes, the next stage's
-    // head reads are issued and the last kAhead fragments' MFMAs cover their
-    // latency.  The next stage's buffer-to-LDS loads are issued among the
-    // MFMAs of the first kSpread fragments.
-    // Stage kt, of parity P = kt % 2 (the loop below is unrolled by two).
+    // Per stage: row block f's reads are issued one row block ahead, its
+    // waits count the reads issued after them (LDS reads complete in order).
+    // Row block 0 waits for each column block's pair just before its MFMAs:
+    // those reads were issued behind the previous stage's last MFMAs.  Before
+    // the last row block every read of the stage is waited for and the stage
+    // barrier passes; the next stage's row block 0 is read, and each column
+    // block's next pair is read into the registers that the last row block's
+    // MFMA pair on that block has just used.  The next stage's buffer-to-LDS
+    // loads are issued among the MFMAs of the first kSpread / 2 row blocks.
     auto stage = [&](int kt, auto P) {
         constexpr int par = decltype(P)::value;
-        static_for<kSteps - kAhead>([&](auto T) {
-            constexpr int t = decltype(T)::value;
-            wait_lgkmcnt<reads_after<kAhead, kBEvery, FM, FN, cA, cB, kSteps>(t)>();
-            OpA::settle(fa[t % 8]);
-            if constexpr (t % FM == 0) {
+        const Loads L = Loads::plan(p, abase, bbase, kb, KT, kt + 1);
+        static_for<FM - 1>([&](auto F) {
+            constexpr int f = decltype(F)::value;
+            read_a(P, std::integral_constant<int, f + 1>{});
+            if constexpr (f > 0) {
+                wait_lgkmcnt<lgk(rA)>();
 #pragma unroll
-                for (int b = 0; b < FN; b++)
-                    OpB::settle(fb[t / FM][b]);
+                for (int kk = 0; kk < NK; kk++)
+                    OpA::settle(fa[f % 2][kk]);
             }
-            if constexpr (b_at<kBEvery, FN>(t) >= 0)
-                read_b(P, One{}, std::integral_constant<int, b_at<kBEvery, FN>(t)>{});
-            read_a(P, std::integral_constant<int, t + kAhead>{});
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (t < kSpread) {
-                issue(kt + 1, T);
-                mfma(T);
+            static_for<FN>([&](auto Bi) {
+                constexpr int b = decltype(Bi)::value;
+                if constexpr (f == 0) {
+                    wait_lgkmcnt<lgk(rA + (FN - 1 - b) * rB)>();
+                    if constexpr (b == 0) {
 #pragma unroll
-                for (int g = 0; g < FN; g++) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x020, (kLoads / kSpread + FN - 1) / FN, 0);
+                        for (int kk = 0; kk < NK; kk++)
+                            OpA::settle(fa[0][kk]);
+                    }
+#pragma unroll
+                    for (int kk = 0; kk < NK; kk++)
+                        OpB::settle(fb[kk][b]);
                 }
-            } else {
-                mfma(T);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+                if constexpr (b < 2 && 2 * f + b < kSpread) {
+                    issue(L, kt + 1, std::integral_constant<int, 2 * f + b>{});
+                    mfma_pair(F, Bi);
+                    __builtin_amdgcn_sched_group_barrier(0x008, NK, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, kLoads / kSpread, 0);
+                } else {
+                    mfma_pair(F, Bi);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
         });
         // Stage kt + 1 has landed (its loads were the only ones in flight).
         wait_vmcnt<0>();
         wait_lgkmcnt<0>();
-        static_for<kAhead>(
-            [&](auto T) { OpA::settle(fa[(kSteps - kAhead + decltype(T)::value) % 8]); });
+#pragma unroll
+        for (int kk = 0; kk < NK; kk++)
+            OpA::settle(fa[(FM - 1) % 2][kk]);
         barrier_no_fence();
-        if (kt + 1 < KT)
-            head(std::integral_constant<int, 1 - par>{});
+        // (After the last stage these read the other buffer's stale bytes,
+        // which no MFMA uses: no branch between the MFMAs.)
+        read_a(std::integral_constant<int, 1 - par>{}, Zero{});
         __builtin_amdgcn_sched_barrier(0);
-        static_for<kAhead>([&](auto T) {
-            mfma(std::integral_constant<int, kSteps - kAhead + decltype(T)::value>{});
+        static_for<FN>([&](auto Bi) {
+            mfma_pair(std::integral_constant<int, FM - 1>{}, Bi);
+            __builtin_amdgcn_sched_barrier(0);
+            read_b_pair(std::integral_constant<int, 1 - par>{}, Bi);
+            __builtin_amdgcn_sched_barrier(0);
         });
-        __builtin_amdgcn_sched_barrier(0);
     };
-    static_for<kSpread>([&](auto G) { issue(0, G); });
+    {
+        const Loads L0 = Loads::plan(p, abase, bbase, kb, KT, 0);
+        static_for<kSpread>([&](auto G) { issue(L0, 0, G); });
+    }
     wait_vmcnt<0>();
     barrier_no_fence();
     head(Zero{});

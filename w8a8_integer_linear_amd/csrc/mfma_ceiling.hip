@@ -2,9 +2,9 @@
 // memory traffic.  Every wave holds what a product wave holds in its main
 // loop (8 x 4 blocks of 16 x 16 int32 sums, the fragments of two 64-byte
 // contraction steps: 8 row blocks and 4 column blocks each) and repeats the
-// products' step-major sequence of 64 v_mfma_i32_16x16x64_i8 (step, then row
-// block, then column block), 8 waves per workgroup, one workgroup per compute
-// unit.  On random fragments its rate is the int8 matrix throughput the
+// products' sequence of 64 v_mfma_i32_16x16x64_i8 (row block, then column
+// block, then the block's two steps back to back), 8 waves per workgroup,
+// one workgroup per compute unit.  On random fragments its rate is the int8 matrix throughput the
 // device sustains within its power limit, the practical ceiling the products
 // are measured against beside the nameplate peak.
 #include "common.hpp"
@@ -39,11 +39,11 @@ __global__ __launch_bounds__(512, 1) void mfma_ceiling_kernel(const i32x4 *__res
             acc[f][b] = i32x4{0, 0, 0, 0};
     for (int it = 0; it < iters; it++) {
 #pragma unroll
-        for (int s = 0; s < 2; s++)
+        for (int f = 0; f < 8; f++)
 #pragma unroll
-            for (int f = 0; f < 8; f++)
+            for (int b = 0; b < 4; b++)
 #pragma unroll
-                for (int b = 0; b < 4; b++) {
+                for (int s = 0; s < 2; s++) {
                     // B first, as in the products: block (f, b) holds the
                     // 16 x 16 sums transposed.
                     acc[f][b] =
