@@ -70,12 +70,44 @@ KERNEL_OF = {"fwd": ["gemm_kernel<2, 4, false, false, 2, 2>"],
              "sgd_requant": ["sgd_requant_kernel<256, 3, false>"]}
 
 
-def source_digest():
-    h = hashlib.sha256()
+def code_only(src):
+    """C/C++ source text without its comments (string and character literals
+    kept) and with whitespace runs collapsed: edits to comments or layout do
+    not change the kernels."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
+def source_digest(read=None):
+    """Digest of the kernel sources (csrc/, comments and layout ignored) that
+    the committed counter summaries must have been taken on.  read(name)
+    returns a file's text (default: the working tree's)."""
     csrc = os.path.join(ROOT, "w8a8_integer_linear_amd", "csrc")
+    if read is None:
+        def read(name):
+            with open(os.path.join(csrc, name), encoding="utf-8") as fh:
+                return fh.read()
+    h = hashlib.sha256()
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        h.update(f.encode() + code_only(read(f)).encode())
     return h.hexdigest()[:16]
 
 

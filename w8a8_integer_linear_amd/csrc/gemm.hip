@@ -759,7 +759,9 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
     // the last row block every read of the stage is waited for and the stage
     // barrier passes; the next stage's row block 0 is read, and each column
     // block's next pair is read into the registers that the last row block's
-    // MFMA pair on that block has just used.  The next stage's buffer-to-LDS
+    // MFMA pair on that block has just used (an MFMA reads its A and B
+    // operands when it issues, and only its sums, C, are read later; the LDS
+    // read writes its registers when it returns).  The next stage's buffer-to-LDS
     // loads are issued among the MFMAs of the first kSpread / FN row blocks.
     auto stage = [&](int kt, auto P) {
         constexpr int par = decltype(P)::value;
