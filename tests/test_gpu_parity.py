@@ -328,6 +328,8 @@ PRODUCT_SHAPES = [
     (130, 272, 208),     # ragged tiles in every dimension
     (257, 144, 5376),    # long contraction
     (33, 4096, 64),      # many output columns
+    (128, 384, 384),     # contractions of 1 and 3 full stages (the stage loop runs in pairs)
+    (300, 400, 400),     # ragged last stages: 4 stages (fwd, dX) and 3 (dW)
 ]
 
 
