@@ -28,7 +28,8 @@
  *    kernels surface at the caller's next synchronization.
  *  - Shapes: M (tokens) >= 0 is arbitrary; M == 0 is a no-op (except that
  *    qlin_bwd_dw then writes an all-zero dW).  N (out
- *    features) and K (in features) are multiples of 16.  A contraction longer
+ *    features) and K (in features) are multiples of 16.  The products take
+ *    M, N and K up to 2^30 (QLIN_EUNSUPPORTED above).  A contraction longer
  *    than QLIN_MAX_CONTRACTION is rejected with QLIN_EUNSUPPORTED, except by
  *    qlin_product_ws, which combines int32 chunks in int64.
  *  - Operand reach: the product kernels address each int8 operand with 32-bit
@@ -293,7 +294,8 @@ int qlin_product_noalloc(int op, const int8_t *a, const float *srow, const int8_
 /* Workspace bytes qlin_product_ws needs for this shape: beyond the int32
  * bound 4096 + 8 per output element; within it 4096 + 256 KiB per balancing
  * piece (at most 256 pieces), or 0 when nothing is balanced.  Returns 0 for
- * invalid arguments. */
+ * invalid arguments and for shapes the products do not support (M, N or K
+ * above 2^30). */
 size_t qlin_product_ws_bytes(int op, int64_t M, int64_t N, int64_t K);
 
 /*

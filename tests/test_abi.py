@@ -297,3 +297,31 @@ def test_product_ws_validation(L):
     assert call(**split_fwd, ws=None) == 1
     assert call(**{**split_fwd, "ws_bytes": need - 1}) == 1
     assert call(**split_fwd, ws=F(3) + 64) == 1      # overlaps the output
+
+
+def test_huge_sizes_are_rejected_without_overflow(L):
+    """Sizes whose byte counts overflow 64 bits are rejected: the argument
+    checks saturate instead of wrapping (with wrapping, (2^62 + 16)^2 * 4
+    would read as 1024 bytes and such calls would pass).  Buffers that large
+    necessarily overlap the other arguments (fake addresses 2^40 apart), which
+    is what rejects most of them; otherwise the size limits do."""
+    _cpu_only()
+    F = lambda i: (i + 1) << 40
+    big = (1 << 62) + 16          # a multiple of 16 whose products overflow
+    assert L.qlin_quantize_grad(F(0), 1, big, 1 << 40, F(1), F(2), F(3), F(4), F(5), F(6),
+                                None, None) == 1
+    # fp32 hadamard has no alias check: rows * cols saturates past the grid limit
+    assert L.qlin_hadamard(F(0), 0, 1 << 40, big, 16, F(1), None) == 2
+    assert L.qlin_dequantize_weight(F(0), F(1), big, big, 0, F(2), None) == 1
+    assert L.qlin_wn_init(F(0), F(1), big, 16, F(2), F(3), None) == 1
+    assert L.qlin_adamw_requant(F(0), F(1), F(2), F(3), F(4), big, big, 1e-3, 0.9, 0.999,
+                                1e-8, 0.0, 0, 1, None, None, None, None, None) == 1
+    # products: dimensions past 2^30 have no workspace size and are unsupported
+    assert L.qlin_product_ws_bytes(0, 1 << 31, 1 << 40, 1 << 40) == 0
+    assert L.qlin_product_ws_bytes(0, 1 << 30, 1 << 30, 1 << 30) == 4096 + 8 * (1 << 60)
+    assert L.qlin_product_ws(0, F(0), F(1), F(2), F(3), None, 1 << 31, big, big, 0, F(4),
+                             F(5), 1 << 20, None) == 2
+    # overlapping ranges near the top of the address space, whose ends would
+    # wrap past 2^64, are still seen to overlap
+    top = (1 << 64) - (1 << 20)
+    assert L.qlin_stream_copy(top, top - (1 << 21), 1 << 30, None) == 1

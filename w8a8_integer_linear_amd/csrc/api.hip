@@ -28,14 +28,27 @@ bool opt_aligned(const void *p) { return p == nullptr || aligned16(p); }
 // An array argument: non-null and 16-byte aligned unless it holds no element.
 bool array_ok(const void *p, bool nonempty) { return nonempty ? (p && aligned16(p)) : opt_aligned(p); }
 
+// a * b (and a * b * c) for non-negative sizes, saturated at INT64_MAX: a
+// size check on the result then rejects the arguments as it would the exact
+// product, and no argument can make the arithmetic overflow.
+int64_t sat_mul(int64_t a, int64_t b)
+{
+    int64_t r;
+    return __builtin_mul_overflow(a, b, &r) ? INT64_MAX : r;
+}
+int64_t sat_mul(int64_t a, int64_t b, int64_t c) { return sat_mul(sat_mul(a, b), c); }
+
 // Whether byte ranges [a, a + na) and [b, b + nb) intersect (empty ranges and
-// null pointers never do).
+// null pointers never do).  Compared as integer addresses, ends saturated at
+// the top of the address space.
 bool overlap(const void *a, int64_t na, const void *b, int64_t nb)
 {
     if (!a || !b || na <= 0 || nb <= 0)
         return false;
-    const char *x = static_cast<const char *>(a), *y = static_cast<const char *>(b);
-    return x < y + nb && y < x + na;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    const uintptr_t xe = (uint64_t)na > UINTPTR_MAX - x ? UINTPTR_MAX : x + (uintptr_t)na;
+    const uintptr_t ye = (uint64_t)nb > UINTPTR_MAX - y ? UINTPTR_MAX : y + (uintptr_t)nb;
+    return x < ye && y < xe;
 }
 
 // Longest contraction qlin_product_ws accepts (chunked into int32-exact pieces).
@@ -120,16 +133,14 @@ int qlin_quantize_grad(const void *dy, int dtype, int64_t rows, int64_t cols, co
     // q2 is written (as scratch, then codes) while everything else is read or
     // written, so it overlaps nothing; s2 and col_sum are accumulators.
     const int64_t eb = dtype == QLIN_BF16 ? 2 : 4;
-    if (any && (overlap(q2, rows * cols, dy, rows * cols * eb) ||
-                overlap(q2, rows * cols, q1, rows * cols) || overlap(q2, rows * cols, s1, rows * 4) ||
-                overlap(q2, rows * cols, sx, rows * 4) || overlap(q2, rows * cols, sw, cols * 4) ||
-                overlap(q2, rows * cols, s2, cols * 4) ||
-                overlap(q2, rows * cols, col_sum, col_sum ? cols * 4 : 0) ||
-                overlap(q1, rows * cols, dy, rows * cols * eb)))
+    const int64_t nq = sat_mul(rows, cols), ndy = sat_mul(rows, cols, eb);
+    const int64_t nr = sat_mul(rows, 4), nc = sat_mul(cols, 4), ncs = col_sum ? nc : 0;
+    if (any && (overlap(q2, nq, dy, ndy) || overlap(q2, nq, q1, nq) || overlap(q2, nq, s1, nr) ||
+                overlap(q2, nq, sx, nr) || overlap(q2, nq, sw, nc) || overlap(q2, nq, s2, nc) ||
+                overlap(q2, nq, col_sum, ncs) || overlap(q1, nq, dy, ndy)))
         return QLIN_EINVAL;
-    if (overlap(s2, cols * 4, col_sum, col_sum ? cols * 4 : 0) ||
-        (any && (overlap(s2, cols * 4, dy, rows * cols * eb) ||
-                 overlap(col_sum, col_sum ? cols * 4 : 0, dy, rows * cols * eb))))
+    if (overlap(s2, nc, col_sum, ncs) ||
+        (any && (overlap(s2, nc, dy, ndy) || overlap(col_sum, ncs, dy, ndy))))
         return QLIN_EINVAL;
     if (cols > QLIN_MAX_ROW || rows > 65535LL * 16)
         return QLIN_EUNSUPPORTED;
@@ -147,9 +158,10 @@ int qlin_dequantize_weight(const int8_t *qw, const float *sw, int64_t N, int64_t
         return QLIN_EINVAL;
     if (had_block != 0 && !hadamard_block_ok(K, had_block))
         return QLIN_EINVAL;
-    if (N > 0 && (overlap(w, N * K * 4, qw, N * K) || overlap(w, N * K * 4, sw, N * 4)))
+    if (N > 0 && (overlap(w, sat_mul(N, K, 4), qw, sat_mul(N, K)) ||
+                  overlap(w, sat_mul(N, K, 4), sw, sat_mul(N, 4))))
         return QLIN_EINVAL;
-    if ((N * K) / 8 / 256 >= ((int64_t)1 << 31))
+    if (sat_mul(N, K) / 8 / 256 >= ((int64_t)1 << 31))
         return QLIN_EUNSUPPORTED;
     if (N == 0)
         return QLIN_OK;
@@ -166,14 +178,11 @@ int qlin_hadamard(const void *x, int dtype, int64_t rows, int64_t cols, int bloc
         return QLIN_EINVAL;
     if (!array_ok(x, rows > 0) || !array_ok(y, rows > 0))
         return QLIN_EINVAL;
-    if (dtype == QLIN_BF16 && rows > 0) {
-        // y may alias x only for an in-place fp32 call.
-        const char *xb = static_cast<const char *>(x), *yb = reinterpret_cast<const char *>(y);
-        const int64_t n = rows * cols;
-        if (yb < xb + 2 * n && xb < yb + 4 * n)
-            return QLIN_EINVAL;
-    }
-    if (rows > (int64_t)1 << 40 || (rows * cols) / 8 / 256 >= ((int64_t)1 << 31))
+    // y may alias x only for an in-place fp32 call.
+    if (dtype == QLIN_BF16 && rows > 0 &&
+        overlap(x, sat_mul(rows, cols, 2), y, sat_mul(rows, cols, 4)))
+        return QLIN_EINVAL;
+    if (rows > (int64_t)1 << 40 || sat_mul(rows, cols) / 8 / 256 >= ((int64_t)1 << 31))
         return QLIN_EUNSUPPORTED;
     if (rows == 0)
         return QLIN_OK;
@@ -263,11 +272,13 @@ size_t qlin_product_ws_bytes(int op, int64_t M, int64_t N, int64_t K)
 {
     if (op < QLIN_OP_FWD || op > QLIN_OP_DW || M < 0 || N < 0 || K < 0)
         return 0;
+    if (M > kMaxRows || N > kMaxRows || K > kMaxRows)
+        return 0;       // a shape the products do not support
     const int64_t contraction = op == QLIN_OP_FWD ? K : (op == QLIN_OP_DX ? N : M);
     if (contraction <= QLIN_MAX_CONTRACTION)
         return qlin::split_ws_bytes(qlin::split_plan(op, M, N, K));
     const int64_t rows = op == QLIN_OP_DW ? N : M, cols = op == QLIN_OP_FWD ? N : K;
-    return qlin::kSplitCountBytes + (size_t)(8 * rows * cols);
+    return qlin::kSplitCountBytes + 8 * (size_t)rows * (size_t)cols;     // < 2^63 + 4096
 }
 
 // Validation shared by qlin_product_ws and qlin_product_noalloc once a
@@ -347,10 +358,11 @@ int qlin_product_ws(int op, const int8_t *a, const float *srow, const int8_t *b,
     if (st != QLIN_OK)
         return st < 0 ? QLIN_OK : st;
     const int64_t rows = op == QLIN_OP_DW ? N : M, cols = op == QLIN_OP_FWD ? N : K;
-    const int64_t la = op == QLIN_OP_FWD ? M * K : M * N, lb = op == QLIN_OP_DW ? M * K : N * K;
-    const int64_t nb = (int64_t)need;
+    const int64_t la = op == QLIN_OP_FWD ? sat_mul(M, K) : sat_mul(M, N);
+    const int64_t lb = op == QLIN_OP_DW ? sat_mul(M, K) : sat_mul(N, K);
+    const int64_t nb = need > (size_t)INT64_MAX ? INT64_MAX : (int64_t)need;
     if (!workspace || !aligned16(workspace) || ws_bytes < need ||
-        overlap(workspace, nb, out, 4 * rows * cols) || overlap(workspace, nb, a, la) ||
+        overlap(workspace, nb, out, sat_mul(rows, cols, 4)) || overlap(workspace, nb, a, la) ||
         overlap(workspace, nb, b, lb))
         return QLIN_EINVAL;
     return launch_ws_product(op, a, srow, b, scol, bias, M, N, K, had_block, out, workspace,
@@ -495,8 +507,8 @@ int qlin_wn_init(const int8_t *q, const float *s, int64_t N, int64_t K, float *g
     const bool any = N > 0;
     if (!array_ok(q, any) || (any && (!s || !g || !sw)))
         return QLIN_EINVAL;
-    if (any && (overlap(g, N * 4, sw, N * 4) || overlap(g, N * 4, s, N * 4) ||
-                overlap(sw, N * 4, s, N * 4)))
+    const int64_t n4 = sat_mul(N, 4);
+    if (any && (overlap(g, n4, sw, n4) || overlap(g, n4, s, n4) || overlap(sw, n4, s, n4)))
         return QLIN_EINVAL;
     if (K > QLIN_WN_MAX_ROW || N > kMaxRows)
         return QLIN_EUNSUPPORTED;
@@ -519,8 +531,8 @@ int qlin_wn_sgd_requant(int8_t *q, float *s, float *g, float *sw, const float *d
         return QLIN_EINVAL;
     if (!isfinite(lr))
         return QLIN_EINVAL;
-    if (any && (overlap(g, N * 4, sw, N * 4) || overlap(g, N * 4, s, N * 4) ||
-                overlap(sw, N * 4, s, N * 4)))
+    const int64_t n4 = sat_mul(N, 4);
+    if (any && (overlap(g, n4, sw, n4) || overlap(g, n4, s, n4) || overlap(sw, n4, s, n4)))
         return QLIN_EINVAL;
     if (K > QLIN_WN_MAX_ROW || N > kMaxRows)
         return QLIN_EUNSUPPORTED;
@@ -549,8 +561,8 @@ int qlin_adamw_requant(int8_t *qw, float *sw, const float *dw, float *m, float *
         !(weight_decay >= 0.0f) || !(beta1 >= 0.0f && beta1 < 1.0f) ||
         !(beta2 >= 0.0f && beta2 < 1.0f))
         return QLIN_EINVAL;
-    if (any && (overlap(m, N * K * 4, v, N * K * 4) || overlap(m, N * K * 4, dw, N * K * 4) ||
-                overlap(v, N * K * 4, dw, N * K * 4)))
+    const int64_t nf = sat_mul(N, K, 4);
+    if (any && (overlap(m, nf, v, nf) || overlap(m, nf, dw, nf) || overlap(v, nf, dw, nf)))
         return QLIN_EINVAL;
     if (K > QLIN_MAX_ROW || N > kMaxRows)
         return QLIN_EUNSUPPORTED;
