@@ -29,7 +29,8 @@
  *  - Shapes: M (tokens) >= 0 is arbitrary; M == 0 is a no-op (except that
  *    qlin_bwd_dw then writes an all-zero dW).  N (out
  *    features) and K (in features) are multiples of 16.  The products take
- *    M, N and K up to 2^30 (QLIN_EUNSUPPORTED above).  A contraction longer
+ *    M, N and K up to 2^30 and outputs of fewer than 2^31 tiles of 256 x 256
+ *    (QLIN_EUNSUPPORTED otherwise).  A contraction longer
  *    than QLIN_MAX_CONTRACTION is rejected with QLIN_EUNSUPPORTED, except by
  *    qlin_product_ws, which combines int32 chunks in int64.
  *  - Operand reach: the product kernels address each int8 operand with 32-bit

@@ -321,6 +321,9 @@ def test_huge_sizes_are_rejected_without_overflow(L):
     assert L.qlin_product_ws_bytes(0, 1 << 30, 1 << 30, 1 << 30) == 4096 + 8 * (1 << 60)
     assert L.qlin_product_ws(0, F(0), F(1), F(2), F(3), None, 1 << 31, big, big, 0, F(4),
                              F(5), 1 << 20, None) == 2
+    # raw products with 2^22 x 2^22 output tiles (each dimension allowed)
+    assert L.qlin_gemm_s32(0, F(0), F(1), 1 << 30, 1 << 30, 16, F(2), None) == 2
+    assert L.qlin_gemm_s32(0, F(0), F(1), 1 << 24, 1 << 23, 16, F(2), None) == 2   # 2^31 tiles
     # overlapping ranges near the top of the address space, whose ends would
     # wrap past 2^64, are still seen to overlap
     top = (1 << 64) - (1 << 20)

@@ -208,6 +208,10 @@ static int check_product(int op, const void *a, const void *b, void *out, int64_
     const int64_t contraction = op == QLIN_OP_FWD ? K : (op == QLIN_OP_DX ? N : M);
     if (contraction > max_contraction || M > kMaxRows || N > kMaxRows || K > kMaxRows)
         return QLIN_EUNSUPPORTED;
+    // The output's 256 x 256 tiles are counted (and indexed) as int.
+    const int64_t rows = op == QLIN_OP_DW ? N : M, cols = op == QLIN_OP_FWD ? N : K;
+    if (((rows + 255) / 256) * ((cols + 255) / 256) >= ((int64_t)1 << 31))
+        return QLIN_EUNSUPPORTED;
     if (!qlin::product_addressable(op, M, N, K))
         return QLIN_EUNSUPPORTED;
     return QLIN_OK;

@@ -654,7 +654,7 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
     using OpB = Operand<BN, BKM, NT, kBK>;
     constexpr int kStage = OpA::kBytes + OpB::kBytes;
     constexpr int kLoads = OpA::kLoads + OpB::kLoads;
-    static_assert(kLoads % kSpread == 0, "stage loads per fragment");
+    static_assert(kLoads % kSpread == 0, "stage loads per part");
     constexpr int cA = OpA::kReads, cB = OpB::kReads;
     __shared__ __attribute__((aligned(1024))) int8_t smem[2 * kStage];
 
