@@ -528,6 +528,46 @@ def test_products_random_shapes(T, Q, orc, i, M, N, K, had, with_bias):
         assert_bitwise(host(got), ref, what)
 
 
+def test_products_random_sweep(T, Q, orc):
+    """A wider seeded sweep in one test: 120 random shapes up to 3000 tokens
+    and 2032 features, the three products through qlin_product_ws and the
+    plain entry points, bit for bit against the oracle."""
+    rng0 = np.random.default_rng(777001)
+    for i in range(120):
+        M = int(rng0.integers(1, 3000))
+        N, K = 16 * int(rng0.integers(1, 128)), 16 * int(rng0.integers(1, 128))
+        had = [0, 128, 64, 16][i % 4]
+        if had and K % had:
+            K = had * (K // had + 1)
+        rng = np.random.default_rng(5000 + i)
+        qx, qw, qg = _codes(rng, (M, K)), _codes(rng, (N, K)), _codes(rng, (M, N))
+        sx = rng.uniform(1e-3, 1e-1, M).astype(np.float32)
+        sw = rng.uniform(1e-4, 1e-2, N).astype(np.float32)
+        sg1 = rng.uniform(1e-6, 1e-4, M).astype(np.float32)
+        sg2 = rng.uniform(1e-6, 1e-4, N).astype(np.float32)
+        b = rng.standard_normal(N).astype(np.float32) if i % 2 else None
+        announce("random sweep", i, M, N, K, had)
+        y_ref = orc.fwd(qx, sx, qw, sw, b)
+        dx_ref = orc.bwd_dx(qg, sg1, qw)
+        if had:
+            dx_ref = orc.hadamard(dx_ref, had)
+        dw_ref = orc.bwd_dw(qg, sg2, qx)
+        bias = None if b is None else dev(b)
+        got = [
+            (Q.qlin_product_ws(Q.QLIN_OP_FWD, dev(qx), dev(sx), dev(qw), M, N, K, scol=dev(sw),
+                               bias=bias), y_ref, "y"),
+            (Q.qlin_product_ws(Q.QLIN_OP_DX, dev(qg), dev(sg1), dev(qw), M, N, K, had_block=had),
+             dx_ref, "dx"),
+            (Q.qlin_product_ws(Q.QLIN_OP_DW, dev(qg), dev(sg2), dev(qx), M, N, K), dw_ref, "dw"),
+            (Q.qlin_fwd(dev(qx), dev(sx), dev(qw), dev(sw), bias), y_ref, "y plain"),
+            (Q.qlin_bwd_dx(dev(qg), dev(sg1), dev(qw), had_block=had), dx_ref, "dx plain"),
+            (Q.qlin_bwd_dw(dev(qg), dev(sg2), dev(qx)), dw_ref, "dw plain"),
+        ]
+        T.cuda.synchronize()
+        for out, ref, what in got:
+            assert_bitwise(host(out), ref, f"{what} (case {i}: {M} x {N} x {K}, block {had})")
+
+
 @pytest.mark.parametrize("M,N,K,had", [(64, 128, 256, 128), (130, 272, 384, 128), (17, 48, 512, 64),
                                        (33, 64, 256, 2), (40, 32, 64, 16), (5, 16, 1024, 256),
                                        (3, 16, 512, 512), (257, 144, 5376, 128)])
