@@ -210,6 +210,34 @@ def test_quantize_grad_random(T, Q, orc, i, rows, cols, bf16):
     assert np.all(np.abs(host(db).astype(np.float64) - dbr) <= bound)
 
 
+def test_quantize_grad_random_sweep(T, Q, orc):
+    """A wider seeded sweep of both dY quantizations in one test: 48 random
+    shapes (16..4000 rows, up to 8192 columns, both dtypes, magnitudes over
+    five decades), codes and scales bit for bit, db within its bound."""
+    rng0 = np.random.default_rng(7404)
+    for i in range(48):
+        rows = int(rng0.integers(16, 4000))
+        cols = 16 * int(rng0.integers(1, 513))
+        bf16 = bool(i % 2)
+        rng = np.random.default_rng(2300 + i)
+        x = _x(rng, rows, cols, bf16, scale=10.0 ** rng.uniform(-4, 1))
+        sw = rng.uniform(1e-3, 1e-2, cols).astype(np.float32)
+        sx = rng.uniform(1e-3, 1e-1, rows).astype(np.float32)
+        announce("quantize_grad sweep", i, rows, cols, bf16)
+        q1, s1, q2, s2, db = Q.qlin_quantize_grad(dev(x), dev(sw), dev(sx), want_sum=True)
+        T.cuda.synchronize()
+        what = f"(case {i}: {rows} x {cols}, bf16 {bf16})"
+        q1r, s1r = orc.quantize_rows(x, prescale=sw)
+        assert_bitwise(host(s1), s1r, "row scales " + what)
+        assert_bitwise(host(q1), q1r, "row codes " + what)
+        q2r, s2r, dbr = orc.quantize_cols(x, prescale=sx, want_sum=True)
+        assert_bitwise(host(s2), s2r, "column scales " + what)
+        assert_bitwise(host(q2), q2r, "column codes " + what)
+        xf = workloads.bf16_bits_to_f32(x) if bf16 else x
+        bound = 1e-5 * np.abs(xf.astype(np.float64)).sum(axis=0) + 1e-30
+        assert np.all(np.abs(host(db).astype(np.float64) - dbr) <= bound), "db " + what
+
+
 def _fragment_matrix(frag):
     """A 1 KiB MFMA fragment (lane l's 16 bytes at 16 l) as the 16 x 64 block
     it carries: lane 16 g + r holds row r, contraction bytes 16 g .. 16 g + 15."""
