@@ -644,11 +644,18 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
     constexpr int RW = BM / WM, CW = BN / WN;
     constexpr int FM = RW / 16, FN = CW / 16;
     constexpr int NK = kBK / 64;                 // MFMA steps per stage
-    // Parts the next stage's buffer-to-LDS loads are issued in: one behind
-    // each MFMA pair of row blocks 0 .. kSpread / FN - 1 (spread over the
-    // first four row blocks' first two pairs instead: 0.6-0.7% slower steps).
+    // Parts a stage's buffer-to-LDS loads are issued in.  With kLead = 1 a
+    // stage issues the next stage's loads, one part behind each MFMA pair of
+    // row blocks 0 .. kSpread / FN - 1 (spread over the first four row
+    // blocks' first two pairs instead: 0.6-0.7% slower steps).  With kLead =
+    // 2 it issues the loads of the stage after next, behind the last row
+    // block's pairs, into its own buffers, whose reads have all passed the
+    // stage barrier by then: a whole stage for the loads to land.  That pays
+    // where both operands are contraction-strided (dW: 4-5% faster) and costs
+    // 1-2% elsewhere.
     constexpr int kSpread = 8;
-    static_assert(NK == 2 && FM % 2 == 0 && kSpread <= FN * (FM - 1),
+    constexpr int kLead = AKM && BKM ? 2 : 1;
+    static_assert(NK == 2 && FM % 2 == 0 && kSpread <= FN * (FM - 1) && kSpread % FN == 0,
                   "fragment schedule shape");
     using OpA = Operand<BM, AKM, NT, kBK>;
     using OpB = Operand<BN, BKM, NT, kBK>;
@@ -761,11 +768,11 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
     // block's next pair is read into the registers that the last row block's
     // MFMA pair on that block has just used (an MFMA reads its A and B
     // operands when it issues, and only its sums, C, are read later; the LDS
-    // read writes its registers when it returns).  The next stage's buffer-to-LDS
-    // loads are issued among the MFMAs of the first kSpread / FN row blocks.
+    // read writes its registers when it returns).  Buffer-to-LDS loads go
+    // out as kLead says.
     auto stage = [&](int kt, auto P) {
         constexpr int par = decltype(P)::value;
-        const Loads L = Loads::plan(p, abase, bbase, kb, KT, kt + 1);
+        const Loads L = Loads::plan(p, abase, bbase, kb, KT, kt + kLead);
         static_for<FM - 1>([&](auto F) {
             constexpr int f = decltype(F)::value;
             read_a(P, std::integral_constant<int, f + 1>{});
@@ -789,7 +796,7 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
                     for (int kk = 0; kk < NK; kk++)
                         OpB::settle(fb[kk][b]);
                 }
-                if constexpr (FN * f + b < kSpread) {
+                if constexpr (kLead == 1 && FN * f + b < kSpread) {
                     issue(L, kt + 1, std::integral_constant<int, FN * f + b>{});
                     mfma_pair(F, Bi);
                     __builtin_amdgcn_sched_group_barrier(0x008, NK, 0);
@@ -812,17 +819,28 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
         read_a(std::integral_constant<int, 1 - par>{}, Zero{});
         __builtin_amdgcn_sched_barrier(0);
         static_for<FN>([&](auto Bi) {
+            constexpr int b = decltype(Bi)::value;
             mfma_pair(std::integral_constant<int, FM - 1>{}, Bi);
             __builtin_amdgcn_sched_barrier(0);
             read_b_pair(std::integral_constant<int, 1 - par>{}, Bi);
+            if constexpr (kLead == 2) {
+                static_for<kSpread / FN>([&](auto G) {
+                    issue(L, kt + 2,
+                          std::integral_constant<int, b * (kSpread / FN) + decltype(G)::value>{});
+                });
+            }
             __builtin_amdgcn_sched_barrier(0);
         });
     };
     {
         const Loads L0 = Loads::plan(p, abase, bbase, kb, KT, 0);
         static_for<kSpread>([&](auto G) { issue(L0, 0, G); });
+        if constexpr (kLead == 2) {
+            const Loads L1 = Loads::plan(p, abase, bbase, kb, KT, 1);
+            static_for<kSpread>([&](auto G) { issue(L1, 1, G); });
+        }
     }
-    wait_vmcnt<0>();
+    wait_vmcnt<kLead == 2 ? kLoads : 0>();      // stage 0 landed
     barrier_no_fence();
     head(Zero{});
     for (int kt = 0; kt < KT; kt += 2) {
