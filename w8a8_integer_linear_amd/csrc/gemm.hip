@@ -644,24 +644,34 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
     constexpr int RW = BM / WM, CW = BN / WN;
     constexpr int FM = RW / 16, FN = CW / 16;
     constexpr int NK = kBK / 64;                 // MFMA steps per stage
-    // Parts a stage's buffer-to-LDS loads are issued in.  With kLead = 1 a
-    // stage issues the next stage's loads, one part behind each MFMA pair of
-    // row blocks 0 .. kSpread / FN - 1 (spread over the first four row
-    // blocks' first two pairs instead: 0.6-0.7% slower steps).  With kLead =
-    // 2 it issues the loads of the stage after next, behind the last row
-    // block's pairs, into its own buffers, whose reads have all passed the
-    // stage barrier by then: a whole stage for the loads to land.  That pays
-    // where both operands are contraction-strided (dW: 4-5% faster) and costs
-    // 1-2% elsewhere.
+    // Parts a stage's buffer-to-LDS loads are issued in (one load each), and
+    // how far ahead each operand's loads run.  A contiguous operand's loads
+    // (lead 1) are for the next stage, behind the MFMA pairs of row blocks
+    // 0-1 (behind the first two pairs of row blocks 0-3 instead: 0.6-0.7%
+    // slower steps).  A contraction-strided operand's loads (lead 2) are for
+    // the stage after next, behind the last row block's pairs, into the
+    // buffers whose reads have just passed the stage barrier: a whole stage
+    // to land (dW 4-5% and dX 3% faster; lead 2 for contiguous operands made
+    // the forward 2% slower).
     constexpr int kSpread = 8;
-    constexpr int kLead = AKM && BKM ? 2 : 1;
+    constexpr int kLeadA = AKM ? 2 : 1, kLeadB = BKM ? 2 : 1;
     static_assert(NK == 2 && FM % 2 == 0 && kSpread <= FN * (FM - 1) && kSpread % FN == 0,
                   "fragment schedule shape");
     using OpA = Operand<BM, AKM, NT, kBK>;
     using OpB = Operand<BN, BKM, NT, kBK>;
     constexpr int kStage = OpA::kBytes + OpB::kBytes;
     constexpr int kLoads = OpA::kLoads + OpB::kLoads;
-    static_assert(kLoads % kSpread == 0, "stage loads per part");
+    static_assert(kLoads == kSpread, "one load per part");
+    // Loads of each lead (A's first): n1 behind the pairs of row blocks 0-1
+    // for the next stage, n2 behind the last row block's pairs for the stage
+    // after next; part_of(lead, i) is the i-th of them.
+    constexpr int n1 = (kLeadA == 1 ? OpA::kLoads : 0) + (kLeadB == 1 ? OpB::kLoads : 0);
+    constexpr int n2 = kLoads - n1;
+    static_assert((n1 == 0 || (2 * FN) % n1 == 0) && n2 % FN == 0, "load placement");
+    constexpr auto part_of = [](int lead, int i) {
+        const int a = kLeadA == lead ? OpA::kLoads : 0;
+        return i < a ? i : OpA::kLoads + (i - a);
+    };
     constexpr int cA = OpA::kReads, cB = OpB::kReads;
     __shared__ __attribute__((aligned(1024))) int8_t smem[2 * kStage];
 
@@ -769,10 +779,11 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
     // MFMA pair on that block has just used (an MFMA reads its A and B
     // operands when it issues, and only its sums, C, are read later; the LDS
     // read writes its registers when it returns).  Buffer-to-LDS loads go
-    // out as kLead says.
+    // out by their operand's lead (kLeadA, kLeadB).
     auto stage = [&](int kt, auto P) {
         constexpr int par = decltype(P)::value;
-        const Loads L = Loads::plan(p, abase, bbase, kb, KT, kt + kLead);
+        const Loads L1 = Loads::plan(p, abase, bbase, kb, KT, kt + 1);
+        const Loads L2 = Loads::plan(p, abase, bbase, kb, KT, kt + 2);
         static_for<FM - 1>([&](auto F) {
             constexpr int f = decltype(F)::value;
             read_a(P, std::integral_constant<int, f + 1>{});
@@ -796,8 +807,9 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
                     for (int kk = 0; kk < NK; kk++)
                         OpB::settle(fb[kk][b]);
                 }
-                if constexpr (kLead == 1 && FN * f + b < kSpread) {
-                    issue(L, kt + 1, std::integral_constant<int, FN * f + b>{});
+                constexpr int slot = FN * f + b, every = n1 ? 2 * FN / n1 : 1;
+                if constexpr (n1 > 0 && slot < 2 * FN && slot % every == 0) {
+                    issue(L1, kt + 1, std::integral_constant<int, part_of(1, slot / every)>{});
                     mfma_pair(F, Bi);
                     __builtin_amdgcn_sched_group_barrier(0x008, NK, 0);
                     __builtin_amdgcn_sched_group_barrier(0x020, kLoads / kSpread, 0);
@@ -823,24 +835,22 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
             mfma_pair(std::integral_constant<int, FM - 1>{}, Bi);
             __builtin_amdgcn_sched_barrier(0);
             read_b_pair(std::integral_constant<int, 1 - par>{}, Bi);
-            if constexpr (kLead == 2) {
-                static_for<kSpread / FN>([&](auto G) {
-                    issue(L, kt + 2,
-                          std::integral_constant<int, b * (kSpread / FN) + decltype(G)::value>{});
-                });
-            }
+            static_for<n2 / FN>([&](auto G) {
+                issue(L2, kt + 2,
+                      std::integral_constant<int, part_of(2, b * (n2 / FN) + decltype(G)::value)>{});
+            });
             __builtin_amdgcn_sched_barrier(0);
         });
     };
     {
         const Loads L0 = Loads::plan(p, abase, bbase, kb, KT, 0);
         static_for<kSpread>([&](auto G) { issue(L0, 0, G); });
-        if constexpr (kLead == 2) {
-            const Loads L1 = Loads::plan(p, abase, bbase, kb, KT, 1);
-            static_for<kSpread>([&](auto G) { issue(L1, 1, G); });
-        }
+        const Loads L1 = Loads::plan(p, abase, bbase, kb, KT, 1);
+        static_for<n2>([&](auto G) {
+            issue(L1, 1, std::integral_constant<int, part_of(2, decltype(G)::value)>{});
+        });
     }
-    wait_vmcnt<kLead == 2 ? kLoads : 0>();      // stage 0 landed
+    wait_vmcnt<n2>();       // stage 0 landed
     barrier_no_fence();
     head(Zero{});
     for (int kt = 0; kt < KT; kt += 2) {
