@@ -155,6 +155,32 @@ def test_headline_step(orc):
     _check_step(orc, d, got, 12000, 5376, 7168, 128, 1e-3, 0, 0, 2048, np.random.default_rng(3))
 
 
+def _random_layer_cases(n=8, seed=8801):
+    """Seeded layer shapes away from the headline ones: any token count from
+    17 (the tiled products) up, widths with a ragged last tile, rotation
+    blocks 0, 16, 64 and 128, with and without bias, both input dtypes."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        had = [128, 0, 64, 16][i % 4]
+        M = int(rng.integers(17, 4000))
+        K = 128 * int(rng.integers(1, 24))
+        N = 16 * int(rng.integers(1, 200))
+        cases.append((i, M, K, N, had, bool(i % 2), bool(rng.integers(0, 2))))
+    return cases
+
+
+@pytest.mark.parametrize("i,M,K,N,had,bias,x_bf16", _random_layer_cases())
+def test_layer_step_random_shapes(orc, i, M, K, N, had, bias, x_bf16):
+    """One training step of the layer at a random shape, checked like the
+    full-size steps: all codes and scales in full, the products at outputs of
+    every tile (layer and plain calls), the updated rows bit for bit."""
+    T = torch_cuda()
+    d = workloads.linear(M, K, N, with_bias=bias, x_bf16=x_bf16, had_block=had, seed=50 + i)
+    got = _step(T, d, M, K, N, had, 1e-3, 7, i)
+    _check_step(orc, d, got, M, K, N, had, 1e-3, 7, i, 512, np.random.default_rng(60 + i))
+
+
 @pytest.mark.parametrize("which", [1, 2])
 def test_mlp_layer_step(orc, which):
     """The transformer MLP's layers at their own shapes (8192 tokens; fc1
