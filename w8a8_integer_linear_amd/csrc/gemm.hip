@@ -807,7 +807,7 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
                     for (int kk = 0; kk < NK; kk++)
                         OpB::settle(fb[kk][b]);
                 }
-                constexpr int slot = FN * f + b, every = n1 ? 2 * FN / n1 : 1;
+                constexpr int slot = FN * f + b, every = 2 * FN / (n1 ? n1 : 2 * FN);
                 if constexpr (n1 > 0 && slot < 2 * FN && slot % every == 0) {
                     issue(L1, kt + 1, std::integral_constant<int, part_of(1, slot / every)>{});
                     mfma_pair(F, Bi);
