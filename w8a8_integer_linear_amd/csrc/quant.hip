@@ -386,7 +386,11 @@ void launch_quantize_cols(const void *x, bool bf16, int64_t rows, int64_t cols,
 // width takes this path; the partials live in q2 until pass 2 overwrites it.
 constexpr int kStatCols = 512;
 constexpr int kStatBatch = 8;    // rows a lane loads before using any of them
-constexpr int kStatWaves = 4096; // waves of pass 1 (row groups x column windows)
+// Waves of pass 1 (row groups x column windows).  At 7168 columns (14
+// windows, workgroups of 4 windows) this gives 256 row groups and 1024
+// workgroups, which at 4 waves per SIMD (120 registers per lane) are all
+// resident at once (4096 waves gave 1168, and pass 1 ran 2-3% longer).
+constexpr int kStatWaves = 3584;
 constexpr int kCodeRows = 16;    // rows per thread in pass 2
 // Offset of a dropped store: past any resource of pass 1 (rows * 4 bytes).
 constexpr int kDropOffset = 0x7FFFFFF0;
