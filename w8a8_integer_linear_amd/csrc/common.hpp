@@ -235,26 +235,37 @@ __device__ __forceinline__ float recip_refined(float s)
     return __builtin_fmaf(r, __builtin_fmaf(-s, r, 1.0f), r);
 }
 
+// Fast path of an INT8 code rne(fl(g / s)) for |g| <= 127.01 s, with inv =
+// fl(1 / s) or recip_refined(s) (either is within 2^-24 (1 + 2^-22) of 1 / s,
+// relatively).  The exact product g * inv is then within 2^-17 of g / s, and
+// fl(g / s) within 2^-17 of g / s, so they are less than 2^-16 apart.
+// f = fma(g, inv, 1.5 * 2^23) rounds the exact product to the nearest
+// integer r (ties to even) in one rounding, and leaves r as the low byte of
+// f's bits; d = fma(g, inv, -r) is the exact product's distance from r within
+// 2^-25.  If |d| < 1/2 - 2^-14, fl(g / s) is less than 1/2 from r, so r is its
+// rounded value; otherwise the caller takes the exact quotient.  Returns f;
+// folds |d| into dmax.
+__device__ __forceinline__ float code_fast(float g, float inv, float &dmax)
+{
+    constexpr float kMagic = 0x1.8p23f;
+    const float f = __builtin_fmaf(g, inv, kMagic);
+    const float d = __builtin_fmaf(g, inv, -(f - kMagic));
+    dmax = fmaxf(dmax, __builtin_fabsf(d));
+    return f;
+}
+
 // Eight INT8 codes rne(fl(g / s)) packed into two dwords, for a scale s > 0
-// that is a normal number, with inv = fl(1 / s) or recip_refined(s) (either
-// is within 2^-24 (1 + 2^-22) of 1 / s, relatively).  Fast path: t =
-// fl(g * inv) is then within 2^-15 of fl(g / s) for |g| <= 127.01 s, so both
-// round to the same integer unless t lies within 2^-14 of a half-integer; if
-// any of the eight does, all eight take the exact quotient.  Rounding to an
-// integer is done by adding 1.5 * 2^23 (round to nearest even in the
-// addition), which also leaves the code as the low byte of the sum's bits.  The quotient is at most
-// 127 (1 + 2^-22) < 127.5 in magnitude, so no clamp is needed.
+// that is a normal number and inv as code_fast takes it.  If any of the eight
+// fails code_fast's check, all eight take the exact quotient.  The quotient
+// is at most 127 (1 + 2^-22) < 127.5 in magnitude, so no clamp is needed.
 __device__ __forceinline__ i32x2 quant8(const float g[8], float s, float inv)
 {
     constexpr float kMagic = 0x1.8p23f;
     float f[8];
     float dmax = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; e++) {
-        const float t = g[e] * inv;
-        f[e] = t + kMagic;
-        dmax = fmaxf(dmax, __builtin_fabsf(t - (f[e] - kMagic)));
-    }
+    for (int e = 0; e < 8; e++)
+        f[e] = code_fast(g[e], inv, dmax);
     if (!(dmax < 0.5f - 0x1p-14f)) {
 #pragma unroll
         for (int e = 0; e < 8; e++)

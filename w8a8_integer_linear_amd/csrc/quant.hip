@@ -128,9 +128,9 @@ __global__ __launch_bounds__(THREADS) void quant_rows_kernel(
         const float sc = a / 127.0f;
         if (t == 0)
             s[row] = sc;
-        const float inv = 1.0f / sc;
         const bool zero = (a == 0.0f);
         const bool subnormal = !zero && sc < 0x1p-126f;
+        const float inv = recip_refined(sc);     // used only for a normal scale
 #pragma unroll
         for (int j = 0; j < J; j++) {
             const int64_t c = lane_chunk<HAD>(t + (int64_t)j * THREADS);
@@ -600,11 +600,8 @@ __device__ __forceinline__ i32x2 quant8_each(const float g[8], const float s[8],
     float f[8];
     float dmax = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; e++) {
-        const float t = g[e] * inv[e];
-        f[e] = t + kMagic;
-        dmax = fmaxf(dmax, __builtin_fabsf(t - (f[e] - kMagic)));
-    }
+    for (int e = 0; e < 8; e++)
+        f[e] = code_fast(g[e], inv[e], dmax);
     if (!(dmax < 0.5f - 0x1p-14f)) {
 #pragma unroll
         for (int e = 0; e < 8; e++)
