@@ -1,0 +1,94 @@
+"""The product kernels' LDS fragment reads are inline asm, so the compiler
+does not know they are in flight: it takes their registers as written when
+the read issues.  The last contraction stage reads the next stage's fragments
+(never used), so unless the kernel waits for those reads and keeps their
+registers live through the wait, the code after the loop may be given those
+registers while a read is still landing in them.  This compiles gemm.hip for
+gfx950 (device code only, the library's own flags) and checks, in every
+product kernel, that no instruction between the loop's exit and the first
+lgkmcnt(0) wait writes a register that an LDS fragment read in the loop's
+last stage targets.  CPU only (hipcc cross-compiles).
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from w8a8_integer_linear_amd import build as hip_build
+
+_READ = re.compile(r"^(ds_read_b128|ds_read_b64_tr_b8)\s+v\[(\d+):(\d+)\]")
+_LOAD = ("ds_read", "ds_load", "global_load", "buffer_load", "flat_load", "scratch_load")
+_NOT_VGPR_DEST = ("v_cmp", "v_readlane", "v_readfirstlane")
+
+
+def _dest_vgprs(line):
+    """VGPRs an instruction writes (its first operand, for VALU ops and loads)."""
+    op = line.split()[0]
+    if not (op.startswith("v_") or op.startswith(_LOAD)) or op.startswith(_NOT_VGPR_DEST):
+        return set()
+    rest = line[len(op):].strip()
+    m = re.match(r"v\[(\d+):(\d+)\]", rest)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)\b", rest)
+    return {int(m.group(1))} if m else set()
+
+
+def loop_exit_hazards(body):
+    """Instructions (after the main loop, before the first lgkmcnt(0) wait)
+    that write a register targeted by an LDS fragment read of the final
+    stage.  body: the kernel's assembly lines."""
+    lines = [l.split(";")[0].strip() for l in body]
+    mfma = [k for k, l in enumerate(lines) if l.startswith("v_mfma")]
+    assert mfma, "no MFMA in the kernel"
+    k = mfma[-1]
+    while not lines[k].startswith(("s_cbranch", "s_branch")):
+        k += 1
+    targets = set()
+    for l in lines[max(0, k - 200):k]:
+        m = _READ.match(l)
+        if m:
+            targets.update(range(int(m.group(2)), int(m.group(3)) + 1))
+    assert targets, "no fragment reads before the loop's back edge"
+    bad = []
+    for l in lines[k + 1:]:
+        if not l or l.startswith(".") or l.endswith(":"):
+            continue
+        if l.startswith("s_waitcnt") and "lgkmcnt(0)" in l:
+            return bad
+        if _dest_vgprs(l) & targets:
+            bad.append(l)
+    raise AssertionError("no lgkmcnt(0) wait after the main loop")
+
+
+def _kernels(asm):
+    out = {}
+    for m in re.finditer(r"^(_Z\w*gemm_kernel\w*):", asm, re.M):
+        end = asm.index(".Lfunc_end", m.end())
+        out[m.group(1)] = asm[m.end():end].split("\n")
+    return out
+
+
+def test_destination_parser():
+    assert _dest_vgprs("v_lshl_or_b32 v128, v171, 6, s30") == {128}
+    assert _dest_vgprs("ds_read_b64_tr_b8 v[130:131], v2 offset:64") == {130, 131}
+    assert _dest_vgprs("v_cmp_gt_i32_e32 vcc, v1, v0") == set()
+    assert _dest_vgprs("global_store_dwordx4 v[2:3], v[4:7], off") == set()
+    assert _dest_vgprs("s_mov_b32 s3, 0") == set()
+
+
+def test_no_register_reuse_before_fragment_reads_land(tmp_path):
+    cc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(cc):
+        pytest.skip("hipcc not available")
+    out = tmp_path / "gemm.s"
+    cmd = [cc, *hip_build.FLAGS, "--cuda-device-only", "-S",
+           os.path.join(hip_build.CSRC, "gemm.hip"), "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    kernels = _kernels(out.read_text())
+    assert len(kernels) >= 10
+    found = {name: loop_exit_hazards(body) for name, body in kernels.items()}
+    assert not any(found.values()), {k: v[:3] for k, v in found.items() if v}

@@ -858,7 +858,25 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_kernel(GemmParams p)
         if (kt + 1 < KT)
             stage(kt + 1, One{});
     }
+    // The last stage has issued the next stage's fragment reads (never used)
+    // and zero-fill loads into the stage buffers.  Wait for the reads and keep
+    // their registers live through that wait: the compiler sees them written
+    // at issue and would otherwise hand them to the code below while a read
+    // is still in flight.  Then wait for this wave's loads, and barrier so
+    // that no wave's loads are still landing when another wave writes its
+    // staging slice (or its arrival flag) into the same buffers.
+    wait_lgkmcnt<0>();
+#pragma unroll
+    for (int kk = 0; kk < NK; kk++) {
+#pragma unroll
+        for (int s = 0; s < 2; s++)
+            OpA::settle(fa[s][kk]);
+#pragma unroll
+        for (int b = 0; b < FN; b++)
+            OpB::settle(fb[kk][b]);
+    }
     wait_vmcnt<0>();
+    barrier_no_fence();
 
     if constexpr (MODE == MODE_SPLIT) {
         // Slot b + FN a of a lane holds block (a, b).
