@@ -7,7 +7,9 @@ registers while a read is still landing in them.  This compiles gemm.hip for
 gfx950 (device code only, the library's own flags) and checks, in every
 product kernel, that no instruction between the loop's exit and the first
 lgkmcnt(0) wait writes a register that an LDS fragment read in the loop's
-last stage targets.  CPU only (hipcc cross-compiles).
+last stage targets, and more generally that no instruction touches any
+fragment read's registers before a wait that covers that read.  CPU only
+(hipcc cross-compiles).
 """
 import os
 import re
@@ -79,16 +81,76 @@ def test_destination_parser():
     assert _dest_vgprs("s_mov_b32 s3, 0") == set()
 
 
-def test_no_register_reuse_before_fragment_reads_land(tmp_path):
+@pytest.fixture(scope="module")
+def gemm_asm(tmp_path_factory):
+    """The product kernels' gfx950 assembly: {kernel symbol: lines}."""
     cc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(cc):
         pytest.skip("hipcc not available")
-    out = tmp_path / "gemm.s"
+    out = tmp_path_factory.mktemp("asm") / "gemm.s"
     cmd = [cc, *hip_build.FLAGS, "--cuda-device-only", "-S",
            os.path.join(hip_build.CSRC, "gemm.hip"), "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     kernels = _kernels(out.read_text())
     assert len(kernels) >= 10
-    found = {name: loop_exit_hazards(body) for name, body in kernels.items()}
+    return kernels
+
+
+def test_no_register_reuse_before_fragment_reads_land(gemm_asm):
+    found = {name: loop_exit_hazards(body) for name, body in gemm_asm.items()}
+    assert not any(found.values()), {k: v[:3] for k, v in found.items() if v}
+
+
+_VREG = re.compile(r"\bv\[(\d+):(\d+)\]|\bv(\d+)\b")
+
+
+def _regs(text):
+    out = set()
+    for m in _VREG.finditer(text):
+        if m.group(3) is not None:
+            out.add(int(m.group(3)))
+        else:
+            out.update(range(int(m.group(1)), int(m.group(2)) + 1))
+    return out
+
+
+def fragment_read_hazards(body):
+    """Instructions that read or write the registers of an inline-asm LDS
+    fragment read before a wait that covers it.  LDS operations complete in
+    order, so s_waitcnt lgkmcnt(n) covers a read once n or more LDS
+    operations were issued after it.  The scan follows the text order (a
+    loop's last reads continue into the code after the loop)."""
+    lines = [l.split(";")[0].strip() for l in body]
+    bad = []
+    for i, l in enumerate(lines):
+        m = _READ.match(l)
+        if not m:
+            continue
+        dst = set(range(int(m.group(2)), int(m.group(3)) + 1))
+        after = 0
+        for l2 in lines[i + 1:]:
+            if not l2 or l2.startswith(".") or l2.endswith(":"):
+                continue
+            w = re.search(r"lgkmcnt\((\d+)\)", l2)
+            if l2.startswith("s_waitcnt") and w and after >= int(w.group(1)):
+                break
+            op = l2.split()[0]
+            operands = l2[len(op):]
+            if op.startswith("ds_read") or op.startswith("ds_load"):
+                # Another LDS read: in-order returns make a shared
+                # destination harmless; its address must not be one of ours.
+                touched = _regs(operands.split(",", 1)[1]) if "," in operands else set()
+            else:
+                touched = _regs(operands)
+            if touched & dst:
+                bad.append((l, l2))
+                break
+            if op.startswith("ds_"):
+                after += 1
+    return bad
+
+
+def test_fragment_reads_are_waited_for_before_use(gemm_asm):
+    found = {name: fragment_read_hazards(body) for name, body in gemm_asm.items()}
     assert not any(found.values()), {k: v[:3] for k, v in found.items() if v}
