@@ -978,3 +978,47 @@ def test_stream_copy(T, Q, nbytes):
     T.cuda.synchronize()
     assert T.equal(dst[:nbytes], src)
     assert int(dst[nbytes:].count_nonzero()) == 0
+
+
+# ------------------------------------------------------------- repetition
+
+def test_products_repeated(T, Q, orc):
+    """Small products launched many times in a row, every output compared bit
+    for bit with the oracle.  A race between the waves of a workgroup (such as
+    the end of the main loop against the epilogue's staging in LDS) shows as
+    a few wrong outputs in some launches only; two-stage contractions with
+    ragged edges, and split last rounds on one reused workspace."""
+    reps = 100
+    for M, N, K in [(130, 272, 208), (64, 528, 320)]:
+        rng = np.random.default_rng(7 * M + N)
+        qx, qw, qg = _codes(rng, (M, K)), _codes(rng, (N, K)), _codes(rng, (M, N))
+        for op, a, b in ((Q.QLIN_OP_FWD, qx, qw), (Q.QLIN_OP_DX, qg, qw), (Q.QLIN_OP_DW, qg, qx)):
+            announce("repeated gemm_s32", op, M, N, K, reps)
+            ref = orc.gemm_s32(op, a, b, M, N, K)
+            da, db = dev(a), dev(b)
+            outs = [Q.qlin_gemm_s32(op, da, db, M, N, K) for _ in range(reps)]
+            T.cuda.synchronize()
+            for r, c in enumerate(outs):
+                assert_bitwise(host(c), ref, f"op{op} {M}x{N}x{K} launch {r}")
+    reps = 40
+    for op, M, N, K in [(0, 700, 1040, 1008), (2, 3000, 1040, 528)]:
+        rng = np.random.default_rng(op * 31 + M)
+        sa = (M, K) if op == 0 else (M, N)
+        sb = (N, K) if op == 0 else (M, K)
+        a, b = _codes(rng, sa), _codes(rng, sb)
+        R = M if op == 0 else N
+        srow = rng.uniform(1e-4, 1e-2, R).astype(np.float32)
+        scol = rng.uniform(1e-2, 1e-1, N).astype(np.float32) if op == 0 else None
+        need = Q.qlin_product_ws_bytes(op, M, N, K)
+        assert need > 0, "the case must split"
+        announce("repeated split", op, M, N, K, reps)
+        ref = orc.fwd(a, srow, b, scol) if op == 0 else orc.bwd_dw(a, srow, b)
+        ws = T.zeros(need, dtype=T.uint8, device="cuda")
+        da, db, ds = dev(a), dev(b), dev(srow)
+        dsc = None if scol is None else dev(scol)
+        outs = [Q.qlin_product_ws(op, da, ds, db, M, N, K, scol=dsc, workspace=ws)
+                for _ in range(reps)]
+        T.cuda.synchronize()
+        for r, c in enumerate(outs):
+            assert_bitwise(host(c), ref, f"split op{op} launch {r}")
+        assert np.all(host(ws[:4096]) == 0), "arrival counters left non-zero"
