@@ -383,7 +383,8 @@ __device__ __forceinline__ WorkUnit work_unit(const GemmParams &p, int kBK)
 // while the rest of the grid is still storing outputs.
 //
 // The arrival flag lives in the stage buffers ('flag_lds'), free once every
-// wave has passed the main loop's last barrier: a second LDS object would make
+// wave has passed the barrier after the main loop (by then no wave's loads
+// into those buffers are still landing): a second LDS object would make
 // the compiler wait for each stage's buffer-to-LDS loads before any LDS read.
 template <int kSlots, int kTile, int kBatch, typename Get, typename Add>
 __device__ __forceinline__ bool split_combine(const GemmParams &p, int tail, int piece,
