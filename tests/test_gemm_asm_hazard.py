@@ -8,8 +8,9 @@ gfx950 (device code only, the library's own flags) and checks, in every
 product kernel, that no instruction between the loop's exit and the first
 lgkmcnt(0) wait writes a register that an LDS fragment read in the loop's
 last stage targets, and more generally that no instruction touches any
-fragment read's registers before a wait that covers that read.  CPU only
-(hipcc cross-compiles).
+fragment read's registers before a wait that covers that read.  It also
+checks the quantizers' hand-written DPP instructions for the two wait states
+a DPP source needs after a VALU write.  CPU only (hipcc cross-compiles).
 """
 import os
 import re
@@ -154,3 +155,70 @@ def fragment_read_hazards(body):
 def test_fragment_reads_are_waited_for_before_use(gemm_asm):
     found = {name: fragment_read_hazards(body) for name, body in gemm_asm.items()}
     assert not any(found.values()), {k: v[:3] for k, v in found.items() if v}
+
+
+# ------------------------------------------------------- DPP wait states
+
+_DPP = re.compile(r"^(v_\w+_dpp)\s+(v\d+|v\[\d+:\d+\]),\s*(v\d+|v\[\d+:\d+\])")
+
+
+def dpp_hazards(body):
+    """DPP instructions whose DPP source (src0) a VALU instruction wrote less
+    than two wait states before (s_nop n counts n + 1, any other instruction
+    one).  The scan stops at a label: the quantizers' DPP asm sits in
+    straight-line blocks that start with their own s_nop."""
+    lines = [l.split(";")[0].strip() for l in body]
+    bad = []
+    for i, l in enumerate(lines):
+        m = _DPP.match(l)
+        if not m:
+            continue
+        src = _regs(m.group(3))
+        waits = 0
+        for l2 in reversed(lines[:i]):
+            if not l2 or l2.startswith("."):
+                if l2.endswith(":"):
+                    break
+                continue
+            if l2.endswith(":"):
+                break
+            op = l2.split()[0]
+            if op == "s_nop":
+                waits += int(l2.split()[1], 0) + 1
+            else:
+                if op.startswith("v_") and _dest_vgprs(l2) & src:
+                    bad.append((l2, l))
+                    break
+                waits += 1
+            if waits >= 2:
+                break
+    return bad
+
+
+def test_dpp_sources_have_their_wait_states(tmp_path):
+    cc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(cc):
+        pytest.skip("hipcc not available")
+    out = tmp_path / "quant.s"
+    cmd = [cc, *hip_build.FLAGS, "--cuda-device-only", "-S",
+           os.path.join(hip_build.CSRC, "quant.hip"), "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    asm = out.read_text()
+    kernels = {}
+    for m in re.finditer(r"^(_Z\w*kernel\w*):", asm, re.M):
+        end = asm.index(".Lfunc_end", m.end())
+        kernels[m.group(1)] = asm[m.end():end].split("\n")
+    n_dpp = sum(1 for body in kernels.values() for l in body if "_dpp " in l)
+    assert n_dpp > 100, "the quantizers' DPP butterflies are missing from the assembly"
+    found = {name: dpp_hazards(body) for name, body in kernels.items()}
+    assert not any(found.values()), {k: v[:3] for k, v in found.items() if v}
+
+
+def test_dpp_checker_flags_a_missing_wait():
+    write = "v_add_f32_e32 v41, v1, v2"
+    dpp = "v_fmac_f32_dpp v41, v41, v53 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+    assert dpp_hazards([write, dpp])
+    assert dpp_hazards([write, "v_mov_b32_e32 v7, v8", dpp])
+    assert not dpp_hazards([write, "s_nop 1", dpp])
+    assert not dpp_hazards([write, "v_mov_b32_e32 v7, v8", "v_mov_b32_e32 v9, v8", dpp])
